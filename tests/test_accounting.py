@@ -1,0 +1,64 @@
+"""Pin the cost formulas to every printed row of the pages' two tables (CPU only).
+
+Sources: "Linear Attention > Computational Complexity Analysis" Out[15] and "Linear
+Attention > Memory Efficiency" Out[19] (mbrenndoerfer.com, ch. 123); fixtures in
+tests/golden/ quote the printed rows.
+"""
+import os
+
+from oracle import accounting as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name, sep=None):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip().split(sep) for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def test_flops_table_every_row():
+    rows = _rows("flops_table.txt")
+    assert len(rows) == 8
+    d = 64
+    for n, std, lin, speed in rows:
+        n = int(n)
+        s = A.flops_standard_attention(n, d)
+        li = A.flops_linear_attention(n, d)
+        assert A.fmt_flops(s) == std, (n, s)
+        assert A.fmt_flops(li) == lin, (n, li)
+        assert "%.1fx" % (s / li) == speed, (n, s / li)
+
+
+def test_flops_exact_values():
+    # 2nd + 4nDd + 2nD + n at d = D = 64, n = 16384; the standard count 4n^2 d + 5n^2
+    assert A.flops_linear_attention(16384, 64) == 272_646_144
+    assert A.flops_standard_attention(16384, 64) == 70_061_654_016
+    # per head-token at d = 128: 2d + 4d^2 + 2d + 1
+    assert A.flops_linear_attention(1, 128) == 66_049
+    assert A.flops_linear_attention(1, 64) == 16_641
+
+
+def test_memory_table_every_row():
+    rows = _rows("memory_table.txt", "|")
+    assert len(rows) == 6
+    d = 64
+    for n, std, lin, red in rows:
+        n = int(n)
+        s = A.memory_standard_attention(n, d)
+        li = A.memory_linear_attention(n, d)
+        assert A.fmt_mem_mb(s) == std, (n, s)
+        assert A.fmt_mem_kb(li) == lin, (n, li)
+        assert "%.0fx" % (s / li) == red, (n, s / li)
+
+
+def test_state_is_16640_bytes_at_d64():
+    assert A.memory_linear_attention(16384, 64) == 16640
+    # "over 16 GB" for the standard matrix at 65,536 tokens
+    assert A.memory_standard_attention(65536, 64) > 16e9
+
+
+def test_decode_floor():
+    # 8192 heads x (state read + write of 66,048 B each way + 4 x 256 B of q/k/v/out)
+    per_step = 8192 * (2 * 66048 + 4 * 256)
+    assert per_step == 1_090_519_040
+    assert abs(A.decode_time_floor_s(per_step, 8.0e12) - 136.3e-6) < 0.1e-6
