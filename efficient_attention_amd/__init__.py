@@ -1,0 +1,21 @@
+"""Kernelized linear attention (phi = elu + 1) for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of include/linattn.h
+(liblinattn.so, built in-tree by ``python -m efficient_attention_amd.build``).  This package
+only marshals torch tensors and streams into that library; it has no other code path.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LA_DTYPE_BF16,
+    LA_DTYPE_F32,
+    LIB_PATH,
+    LinAttnError,
+    la_abi_version,
+    la_causal_workspace_bytes,
+    la_decode_step,
+    la_forward_causal,
+    la_forward_noncausal,
+    la_noncausal_workspace_bytes,
+    la_status_string,
+    load,
+)

@@ -1,0 +1,194 @@
+"""ctypes binding of liblinattn.so (include/linattn.h), taking torch tensors.
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  If the library has not been built
+this module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_DTYPE_F32 = 0
+LA_DTYPE_BF16 = 1
+LA_OK = 0
+
+# every symbol declared in include/linattn.h
+EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
+           "la_forward_noncausal", "la_causal_workspace_bytes", "la_forward_causal",
+           "la_decode_step")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, la_status_string(status), status))
+
+
+def load():
+    """Load liblinattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("liblinattn.so is not built (run `python -m efficient_attention_amd.build` "
+                               "or __graft_entry__.build()); there is no fallback path")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        lib.la_abi_version.argtypes = []
+        lib.la_abi_version.restype = I
+        lib.la_status_string.argtypes = [I]
+        lib.la_status_string.restype = ctypes.c_char_p
+        lib.la_noncausal_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+        lib.la_noncausal_workspace_bytes.restype = SZ
+        lib.la_forward_noncausal.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]
+        lib.la_forward_noncausal.restype = I
+        lib.la_causal_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+        lib.la_causal_workspace_bytes.restype = SZ
+        lib.la_forward_causal.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
+        lib.la_forward_causal.restype = I
+        lib.la_decode_step.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, P]
+        lib.la_decode_step.restype = I
+        _lib = lib
+    return _lib
+
+
+def la_abi_version() -> int:
+    return load().la_abi_version()
+
+
+def la_status_string(status: int) -> str:
+    return load().la_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return LA_DTYPE_BF16
+    raise TypeError("linear attention supports float32 and bfloat16 tensors, got %s" % t.dtype)
+
+
+def la_noncausal_workspace_bytes(B: int, H: int, n: int, d: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().la_noncausal_workspace_bytes(B, H, n, d, code))
+
+
+def la_causal_workspace_bytes(B: int, H: int, n: int, d: int, chunk: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().la_causal_workspace_bytes(B, H, n, d, chunk, code))
+
+
+# Workspaces are zero-filled once and reused: the kernels leave their counters at zero.
+# One buffer per (device, stream), so calls queued on one stream never share it concurrently.
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device: torch.device, stream_handle: int) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    key = (device.index, stream_handle)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_qkv(q, k, v, ndim):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.dim() != ndim:
+            raise ValueError("%s must have %d dimensions, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ: %s %s %s" % (q.shape, k.shape, v.shape))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v dtypes differ")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v are on different devices")
+
+
+def _out_like(q, out):
+    if out is None:
+        return torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor with the shape, dtype and device of q")
+    return out
+
+
+def la_forward_noncausal(q, k, v, out=None, ws=None, stream=None):
+    """Non-causal forward over [B, H, n, d] tensors; returns out."""
+    _check_qkv(q, k, v, 4)
+    out = _out_like(q, out)
+    B, H, n, d = q.shape
+    code = _dtype_code(q)
+    sh = _stream_handle(q.device, stream)
+    need = la_noncausal_workspace_bytes(B, H, n, d, code)
+    if ws is None:
+        ws = workspace(need, q.device, sh)
+    st = load().la_forward_noncausal(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     B, H, n, d, code, ws.data_ptr() if ws is not None else None,
+                                     ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_forward_noncausal")
+    return out
+
+
+def la_forward_causal(q, k, v, chunk: int = 128, out=None, ws=None, stream=None):
+    """Causal (j <= i) forward over [B, H, n, d] tensors; returns out."""
+    _check_qkv(q, k, v, 4)
+    out = _out_like(q, out)
+    B, H, n, d = q.shape
+    code = _dtype_code(q)
+    sh = _stream_handle(q.device, stream)
+    need = la_causal_workspace_bytes(B, H, n, d, chunk, code)
+    if ws is None:
+        ws = workspace(need, q.device, sh)
+    st = load().la_forward_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  B, H, n, d, chunk, code,
+                                  ws.data_ptr() if ws is not None else None,
+                                  ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_forward_causal")
+    return out
+
+
+def la_decode_step(q, k, v, S, z, out=None, stream=None):
+    """One decode step over [B, H, d] tensors; S [B, H, d, d] and z [B, H, d] (fp32) are
+    updated in place; returns out."""
+    _check_qkv(q, k, v, 3)
+    B, H, d = q.shape
+    for name, t, shape in (("S", S, (B, H, d, d)), ("z", z, (B, H, d))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s" % (name, shape, q.device))
+    out = _out_like(q, out)
+    sh = _stream_handle(q.device, stream)
+    st = load().la_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), S.data_ptr(), z.data_ptr(),
+                               out.data_ptr(), B, H, d, _dtype_code(q), sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_decode_step")
+    return out

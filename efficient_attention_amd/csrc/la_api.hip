@@ -1,0 +1,251 @@
+// la_api.hip -- the C ABI declared in include/linattn.h: argument validation, workspace
+// planning and kernel dispatch.  Validation happens before any launch; on an error nothing is
+// written.  The library allocates nothing and keeps no state between calls.
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "la_kernels.h"
+#include "linattn.h"
+
+namespace {
+
+constexpr int64_t kTargetStateBlocks = 2048;  // stage-1 workgroups to aim for
+constexpr int64_t kTargetCausalBlocks = 256;  // one causal workgroup per compute unit
+constexpr int64_t kMaxSegments = 16;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int elem_bytes(int dtype) { return dtype == LA_DTYPE_BF16 ? 2 : 4; }
+
+// Checks common to every entry point; fills total bytes of one [B][H][n][d] tensor.
+int check_shape(int64_t B, int64_t H, int64_t n, int64_t d, int dtype, int64_t* bh, size_t* bytes) {
+  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16) return LA_ERR_DTYPE;
+  if (B < 0 || H < 0 || n < 0 || d < 0) return LA_ERR_SHAPE;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  int64_t t = 0, e = 0;
+  if (__builtin_mul_overflow(B, H, &t)) return LA_ERR_SHAPE;
+  *bh = t;
+  if (__builtin_mul_overflow(t, n, &e) || __builtin_mul_overflow(e, d, &e) ||
+      __builtin_mul_overflow(e, (int64_t)elem_bytes(dtype), &e))
+    return LA_ERR_SHAPE;
+  *bytes = (size_t)e;
+  return LA_OK;
+}
+
+// Stage-1 plan: `groups` token ranges of `group_len` tokens, each split over `slices`
+// workgroups of `slice_len` tokens.
+struct StatePlan {
+  int64_t groups = 0, slices = 0, slice_len = 0;
+  size_t counters_off = 0, state_off = 0, partials_off = 0, bytes = 0;
+};
+
+StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
+  StatePlan p;
+  p.groups = groups;
+  const int64_t tile = la::kv_state_tile(d, dtype);
+  const int64_t tiles = cdiv(group_len, tile);
+  int64_t slices = clamp64(cdiv(kTargetStateBlocks, groups), 1, tiles);
+  p.slice_len = cdiv(tiles, slices) * tile;
+  p.slices = cdiv(group_len, p.slice_len);
+  const size_t E = (size_t)(d * d + d) * sizeof(float);
+  p.counters_off = 0;
+  p.state_off = round256((size_t)groups * sizeof(unsigned));
+  p.partials_off = p.state_off + round256((size_t)groups * E);
+  p.bytes = p.partials_off + (p.slices > 1 ? (size_t)groups * (size_t)p.slices * E : 0);
+  return p;
+}
+
+struct CausalPlan {
+  int64_t segs = 1, seg_len = 0;
+  StatePlan state;
+  size_t bytes = 0;
+};
+
+CausalPlan plan_causal(int64_t bh, int64_t n, int64_t chunk, int d, int dtype) {
+  CausalPlan c;
+  const int64_t nchunks = cdiv(n, chunk);
+  int64_t segs = clamp64(cdiv(kTargetCausalBlocks, bh), 1, kMaxSegments);
+  segs = clamp64(segs, 1, nchunks);
+  c.seg_len = cdiv(nchunks, segs) * chunk;
+  c.segs = cdiv(n, c.seg_len);
+  if (c.segs > 1) {
+    c.state = plan_state(bh * (c.segs - 1), c.seg_len, d, dtype);
+    c.bytes = c.state.bytes;
+  }
+  return c;
+}
+
+la::KvStateArgs state_args(const StatePlan& p, const void* k, const void* v, void* ws, int64_t n,
+                           int64_t group_len, int64_t groups_per_head) {
+  la::KvStateArgs a;
+  char* base = reinterpret_cast<char*>(ws);
+  a.k = k;
+  a.v = v;
+  a.counters = reinterpret_cast<unsigned*>(base + p.counters_off);
+  a.state = reinterpret_cast<float*>(base + p.state_off);
+  a.partials = reinterpret_cast<float*>(base + p.partials_off);
+  a.n = n;
+  a.group_len = group_len;
+  a.groups_per_head = groups_per_head;
+  a.groups = p.groups;
+  a.slices = p.slices;
+  a.slice_len = p.slice_len;
+  return a;
+}
+
+bool grid_ok(int64_t blocks) { return blocks > 0 && blocks <= (int64_t)INT_MAX; }
+
+}  // namespace
+
+extern "C" {
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+const char* la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "ok";
+    case LA_ERR_NULL: return "a required pointer is NULL";
+    case LA_ERR_SHAPE: return "invalid (negative or overflowing) shape";
+    case LA_ERR_DTYPE: return "unknown element type";
+    case LA_ERR_UNSUPPORTED: return "unsupported head dimension, chunk or dtype combination";
+    case LA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LA_ERR_ALIAS: return "output overlaps an input, the state or the workspace";
+    case LA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
+  if (bh == 0 || n == 0) return 0;
+  return plan_state(bh, n, (int)d, dtype).bytes;
+}
+
+int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
+                         int64_t H, int64_t n, int64_t d, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_shape(B, H, n, d, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (bh == 0 || n == 0) return LA_OK;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
+  const StatePlan p = plan_state(bh, n, (int)d, dtype);
+  if (!workspace || workspace_bytes < p.bytes) return LA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, p.bytes))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * ((n + 255) / 256))) return LA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  la::KvStateArgs ka = state_args(p, k, v, workspace, n, n, 1);
+  if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  la::NcOutArgs oa;
+  oa.q = q;
+  oa.out = out;
+  oa.state = ka.state;
+  oa.n = n;
+  oa.bh = bh;
+  if (la::launch_nc_out(oa, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  return LA_OK;
+}
+
+size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk,
+                                 int dtype) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
+  if (chunk != 64 && chunk != 128) return 0;
+  if (bh == 0 || n == 0) return 0;
+  return plan_causal(bh, n, chunk, (int)d, dtype).bytes;
+}
+
+int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
+                      int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_shape(B, H, n, d, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (chunk != 64 && chunk != 128) return LA_ERR_UNSUPPORTED;
+  if (dtype == LA_DTYPE_F32 && d * chunk > 8192) return LA_ERR_UNSUPPORTED;
+  if (bh == 0 || n == 0) return LA_OK;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
+  const CausalPlan p = plan_causal(bh, n, chunk, (int)d, dtype);
+  if (p.bytes > 0) {
+    if (!workspace || workspace_bytes < p.bytes) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  }
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, p.bytes))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(bh * p.segs)) return LA_ERR_SHAPE;
+  if (p.segs > 1 && !grid_ok(p.state.groups * p.state.slices)) return LA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  la::CausalArgs ca;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.out = out;
+  ca.seg_state = nullptr;
+  ca.n = n;
+  ca.bh = bh;
+  ca.segs = p.segs;
+  ca.seg_len = p.seg_len;
+  if (p.segs > 1) {
+    la::KvStateArgs ka = state_args(p.state, k, v, workspace, n, p.seg_len, p.segs - 1);
+    if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+    ca.seg_state = ka.state;
+  }
+  if (la::launch_causal(ca, (int)d, (int)chunk, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  return LA_OK;
+}
+
+int la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
+                   int64_t B, int64_t H, int64_t d, int dtype, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_shape(B, H, 1, d, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (bh == 0) return LA_OK;
+  if (!q || !k || !v || !S || !z || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(z) ||
+      !aligned16(out))
+    return LA_ERR_ALIGN;
+  const size_t sbytes = (size_t)bh * (size_t)(d * d) * sizeof(float);
+  const size_t zbytes = (size_t)bh * (size_t)d * sizeof(float);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, S, sbytes) ||
+      overlaps(out, bytes, z, zbytes) || overlaps(S, sbytes, z, zbytes))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(bh)) return LA_ERR_SHAPE;
+  la::DecodeArgs da;
+  da.q = q;
+  da.k = k;
+  da.v = v;
+  da.S = S;
+  da.z = z;
+  da.out = out;
+  da.bh = bh;
+  if (la::launch_decode(da, (int)d, dtype, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return LA_ERR_HIP;
+  return LA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,450 @@
+// la_causal.hip -- causal (j <= i) linear attention, chunked, on gfx950.
+//
+// Math ("Efficient Transformers: Linear Attention and Flash Attention", section "The recurrent
+// view: attention as an RNN"): out_i = phi(q_i)^T S_i / phi(q_i)^T z_i with the prefix sums
+// S_i = sum_{j<=i} phi(k_j) v_j^T and z_i = sum_{j<=i} phi(k_j).  Split the keys of a query in
+// chunk [c0, c0+C) at c0 (associativity, section "Linear attention: reordering the matmuls"):
+//   j <  c0  : the running state (S, z) carried from earlier chunks,
+//   c0 <= j <= i : the masked pairwise weights A_ij = phi(q_i).phi(k_j) inside the chunk,
+// so  num_i = sum_j A_ij v_j + phi(q_i)^T S,  den_i = sum_j A_ij + phi(q_i)^T z,  and after the
+// chunk S += phi(K_c)^T V_c, z += phi(K_c)^T 1.
+//
+// Work split.  One workgroup walks one segment of one head chunk by chunk; a head is cut into
+// `segs` segments so that short batches still fill the GPU.  The state entering segment s is
+// the sum of the leading segments' state sums, computed beforehand by the stage-1 kernel of
+// la_noncausal.hip (any partition of the keys gives the same sums).
+#include "la_common.h"
+#include "la_kernels.h"
+
+namespace la {
+
+// Initial (S, z) of a segment: sum over the leading segments, in segment order.
+__device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64_t bh, int64_t s,
+                                                      int D) {
+  return a.seg_state + (bh * (a.segs - 1) + s) * (int64_t)(D * D + D);
+}
+
+// bf16 kernel, D = head dim, C = chunk.  256 threads = 4 waves.
+//
+// LDS (bf16 unless noted):  Kn[C][D] phi(K) token-major rows (operand of phi(K) phi(Q)^T),
+// Kt[D][C] and Vt[D][C] feature-major rows (operands whose reduction index is the token),
+// St[D][D] the running state transposed, St[c][a] = S[a][c], rounded to bf16 (operand of
+// S^T phi(Q)^T), Zr[16][D] a normaliser tile: row 0 = bf16(z), row 1 = bf16(z - row 0),
+// rows 2..15 zero; zf[D] fp32 z.
+//
+// Per wave: query tiles {w, C/16-1-w} (16 rows each; the snake order balances the masked
+// triangle), the state columns c-tiles {w, w+4, ...} in fp32 MFMA accumulators, z for
+// a-tiles {w, w+4, ...}.  Outputs are computed transposed, out^T[c][i] (c = MFMA row, query
+// = MFMA column), so that
+//   * phi(Q) needs no LDS: a lane's 16-byte load of its query row is its operand;
+//   * the masked tile is computed as A^T[j][i] = phi(K) phi(Q)^T; in the MFMA result a lane
+//     holds j = 16*jt + 4g + r for its query, so two j-tiles give 8 j values per lane, which
+//     is the operand layout of the next product with the k index permuted accordingly;
+//     V is read with the same permutation, and A never goes through LDS;
+//   * the normaliser rides along as one extra 16-row output tile: z (hi, lo) rows against
+//     phi(Q) and a row of ones against A give phi(q).z + sum_j A_ij in rows 0 and 1.
+template <int D, int C>
+__global__ __launch_bounds__(256) void causal_bf16(CausalArgs a) {
+  constexpr int LDK = D + 8;
+  constexpr int LDC = C + 8;
+  constexpr int NI = C / 16;         // query (and key) tiles per chunk
+  constexpr int NIW = NI / 4;        // query tiles per wave
+  constexpr int NC = D / 16;         // value-column tiles
+  constexpr int NCW = NC / 4;        // state column tiles per wave
+  constexpr int NA = D / 16;         // feature tiles
+  constexpr int NZW = NA / 4;        // z feature tiles per wave
+  constexpr int KA = D / 32;         // k-steps over features
+  constexpr int KJ = C / 32;         // k-steps over tokens
+  constexpr int NB = (C / 8) * (D / 8);        // 8x8 blocks per tile
+  constexpr int NKV = (2 * NB + 255) / 256;    // K/V blocks per thread
+  static_assert(NIW >= 1 && NCW >= 1 && NZW >= 1, "shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Kn[C * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * LDC];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDC];
+  __shared__ __attribute__((aligned(16))) uint16_t St[D * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDK];
+  __shared__ float zf[D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
+  const int64_t t0 = seg * a.seg_len;
+  const int64_t t1 = t0 + a.seg_len < a.n ? t0 + a.seg_len : a.n;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + bh * a.n * D;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + bh * a.n * D;
+  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
+
+  // ---- initial state (fp32 accumulators for this wave's columns, z in LDS)
+  f32x4 accS[NA][NCW];
+#pragma unroll
+  for (int at = 0; at < NA; ++at)
+#pragma unroll
+    for (int p = 0; p < NCW; ++p) accS[at][p] = zero4();
+  float zinit = 0.f;
+  for (int64_t s = 0; s < seg; ++s) {
+    const float* st = seg_state_ptr(a, bh, s, D);
+#pragma unroll
+    for (int at = 0; at < NA; ++at)
+#pragma unroll
+      for (int p = 0; p < NCW; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          accS[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
+    if (tid < D) zinit += st[D * D + tid];
+  }
+  if (tid < D) zf[tid] = zinit;
+  auto write_state_bf16 = [&]() {
+#pragma unroll
+    for (int at = 0; at < NA; ++at)
+#pragma unroll
+      for (int p = 0; p < NCW; ++p) {
+        u32x2 w2;
+        w2.x = pack_bf16(accS[at][p][0], accS[at][p][1]);
+        w2.y = pack_bf16(accS[at][p][2], accS[at][p][3]);
+        *reinterpret_cast<u32x2*>(&St[((wave + 4 * p) * 16 + l16) * LDK + at * 16 + g * 4]) = w2;
+      }
+  };
+  write_state_bf16();
+  __syncthreads();
+  for (int e = tid; e < 16 * D; e += 256) {
+    const int row = e / D, c = e % D;
+    uint16_t val = 0;
+    if (row < 2) {
+      const float z = zf[c];
+      const __bf16 hi = (__bf16)z;
+      val = row == 0 ? __builtin_bit_cast(uint16_t, hi) : __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
+    }
+    Zr[row * LDK + c] = val;
+  }
+
+  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
+  u32x4 ones;
+  ones.x = ones.y = ones.z = ones.w = (l16 == 0) ? one2 : 0u;
+
+  // ---- chunk loads (issued one chunk ahead)
+  u32x4 kvr[NKV][8];
+  u32x4 qr[NIW][KA];
+  auto itile = [&](int p) { return p == 0 ? wave : NI - 1 - wave; };
+  auto load_chunk = [&](int64_t c0) {
+#pragma unroll
+    for (int x = 0; x < NKV; ++x) {
+      const int b = tid + 256 * x;
+      if (b < 2 * NB) {
+        const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
+        const uint16_t* src = b < NB ? K : V;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int64_t tok = c0 + tb * 8 + r;
+          kvr[x][r] = tok < t1 ? ld16(src + tok * D + fb * 8) : zero_u4();
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < NIW; ++p) {
+      const int64_t row = c0 + itile(p) * 16 + l16;
+#pragma unroll
+      for (int ks = 0; ks < KA; ++ks) qr[p][ks] = row < t1 ? ld16(Q + row * D + ks * 32 + g * 8) : zero_u4();
+    }
+  };
+
+  float zp[NZW];
+#pragma unroll
+  for (int i = 0; i < NZW; ++i) zp[i] = 0.f;
+
+  if (t0 < t1) load_chunk(t0);
+  for (int64_t c0 = t0; c0 < t1; c0 += C) {
+    // ---- (a) tiles into LDS: phi(K) natural + transposed, V transposed; phi(Q) in registers
+#pragma unroll
+    for (int x = 0; x < NKV; ++x) {
+      const int b = tid + 256 * x;
+      if (b < 2 * NB) {
+        const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
+        u32x4 tr[8];
+        if (b < NB) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const bool ok = c0 + tb * 8 + r < t1;
+            kvr[x][r] = ok ? phi_bf16x8(kvr[x][r]) : zero_u4();
+            st16(&Kn[(tb * 8 + r) * LDK + fb * 8], kvr[x][r]);
+          }
+          transpose8x8(kvr[x], tr);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st16(&Kt[(fb * 8 + e) * LDC + tb * 8], tr[e]);
+        } else {
+          transpose8x8(kvr[x], tr);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st16(&Vt[(fb * 8 + e) * LDC + tb * 8], tr[e]);
+        }
+      }
+    }
+    u32x4 qf[NIW][KA];
+#pragma unroll
+    for (int p = 0; p < NIW; ++p)
+#pragma unroll
+      for (int ks = 0; ks < KA; ++ks) qf[p][ks] = phi_bf16x8(qr[p][ks]);
+    __syncthreads();  // tiles, St, Zr ready
+    if (c0 + C < t1) load_chunk(c0 + C);
+
+    // ---- (iv) state update in registers: S[:, own cols] += phi(K_c)^T V_c ; z partial sums
+#pragma unroll
+    for (int ks = 0; ks < KJ; ++ks) {
+      u32x4 bv[NCW];
+#pragma unroll
+      for (int p = 0; p < NCW; ++p) bv[p] = ld16(&Vt[((wave + 4 * p) * 16 + l16) * LDC + ks * 32 + g * 8]);
+#pragma unroll
+      for (int at = 0; at < NA; ++at) {
+        const u32x4 ak = ld16(&Kt[(at * 16 + l16) * LDC + ks * 32 + g * 8]);
+        if ((at & 3) == wave) zp[at >> 2] += sum_bf16x8(ak);
+#pragma unroll
+        for (int p = 0; p < NCW; ++p) accS[at][p] = mfma_bf16(ak, bv[p], accS[at][p]);
+      }
+    }
+
+    // ---- per query tile: masked intra-chunk part + inter-chunk part, normalise, store
+#pragma unroll
+    for (int p = 0; p < NIW; ++p) {
+      const int it = itile(p);
+      f32x4 accA[NI];
+#pragma unroll
+      for (int jt = 0; jt < NI; ++jt) {
+        accA[jt] = zero4();
+        if (jt <= it) {
+#pragma unroll
+          for (int ks = 0; ks < KA; ++ks)
+            accA[jt] = mfma_bf16(ld16(&Kn[(jt * 16 + l16) * LDK + ks * 32 + g * 8]), qf[p][ks], accA[jt]);
+        }
+        if (jt == it) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (g * 4 + r > l16) accA[jt][r] = 0.f;
+        }
+      }
+      f32x4 acco[NC];
+      f32x4 accd = zero4();
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) acco[ct] = zero4();
+      // inter-chunk: S^T phi(Q)^T and [z_hi; z_lo] phi(Q)^T
+#pragma unroll
+      for (int ks = 0; ks < KA; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct)
+          acco[ct] = mfma_bf16(ld16(&St[(ct * 16 + l16) * LDK + ks * 32 + g * 8]), qf[p][ks], acco[ct]);
+        accd = mfma_bf16(ld16(&Zr[l16 * LDK + ks * 32 + g * 8]), qf[p][ks], accd);
+      }
+      // intra-chunk: V^T A^T and ones A^T over key tiles 0..it (pairs of 16)
+#pragma unroll
+      for (int m = 0; m < NI / 2; ++m) {
+        if (2 * m <= it) {
+          u32x4 af;
+          af.x = pack_bf16(accA[2 * m][0], accA[2 * m][1]);
+          af.y = pack_bf16(accA[2 * m][2], accA[2 * m][3]);
+          af.z = pack_bf16(accA[2 * m + 1][0], accA[2 * m + 1][1]);
+          af.w = pack_bf16(accA[2 * m + 1][2], accA[2 * m + 1][3]);
+#pragma unroll
+          for (int ct = 0; ct < NC; ++ct) {
+            const uint16_t* vrow = &Vt[(ct * 16 + l16) * LDC + m * 32 + g * 4];
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+            u32x4 av;
+            av.x = lo.x;
+            av.y = lo.y;
+            av.z = hi.x;
+            av.w = hi.y;
+            acco[ct] = mfma_bf16(av, af, acco[ct]);
+          }
+          accd = mfma_bf16(ones, af, accd);
+        }
+      }
+      const float den = __shfl(accd[0] + accd[1], l16);
+      const float inv = 1.0f / den;
+      const int64_t row = c0 + it * 16 + l16;
+      if (row < t1) {
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+          u32x2 o;
+          o.x = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
+          o.y = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
+          *reinterpret_cast<u32x2*>(O + row * D + ct * 16 + g * 4) = o;
+        }
+      }
+    }
+    __syncthreads();  // every wave is done reading this chunk's tiles, St and Zr
+
+    // ---- publish the new state for the next chunk
+    write_state_bf16();
+#pragma unroll
+    for (int i = 0; i < NZW; ++i) {
+      const int at = wave + 4 * i;
+      const float zs = sum_over_groups(zp[i]);
+      zp[i] = 0.f;
+      if (g == 0) {
+        const float z = zf[at * 16 + l16] + zs;
+        zf[at * 16 + l16] = z;
+        const __bf16 hi = (__bf16)z;
+        Zr[at * 16 + l16] = __builtin_bit_cast(uint16_t, hi);
+        Zr[LDK + at * 16 + l16] = __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
+      }
+    }
+  }
+}
+
+// fp32 kernel (no bf16 rounding anywhere).  The fp32 MFMA takes one k value per lane, so every
+// operand comes from natural token-major LDS rows.  Each wave owns state columns
+// {w, w+4, ...} in fp32 accumulators and produces the outputs of those columns for every
+// query of the chunk; the masked tile A^T is recomputed per wave (cheap at the sizes fp32 is
+// meant for) and, as in the bf16 kernel, fed back as an operand with permuted k.
+template <int D, int C>
+__global__ __launch_bounds__(256) void causal_f32(CausalArgs a) {
+  constexpr int LD = D + 4;
+  constexpr int NI = C / 16;
+  constexpr int NCW = D / 64;
+  constexpr int NA = D / 16;
+  __shared__ __attribute__((aligned(16))) float Qn[C * LD];
+  __shared__ __attribute__((aligned(16))) float Kn[C * LD];
+  __shared__ __attribute__((aligned(16))) float Vn[C * LD];
+  __shared__ float zf[D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
+  const int64_t t0 = seg * a.seg_len;
+  const int64_t t1 = t0 + a.seg_len < a.n ? t0 + a.seg_len : a.n;
+  const float* Q = reinterpret_cast<const float*>(a.q) + bh * a.n * D;
+  const float* K = reinterpret_cast<const float*>(a.k) + bh * a.n * D;
+  const float* V = reinterpret_cast<const float*>(a.v) + bh * a.n * D;
+  float* O = reinterpret_cast<float*>(a.out) + bh * a.n * D;
+
+  f32x4 accS[NA][NCW];
+#pragma unroll
+  for (int at = 0; at < NA; ++at)
+#pragma unroll
+    for (int p = 0; p < NCW; ++p) accS[at][p] = zero4();
+  float zinit = 0.f;
+  for (int64_t s = 0; s < seg; ++s) {
+    const float* st = seg_state_ptr(a, bh, s, D);
+#pragma unroll
+    for (int at = 0; at < NA; ++at)
+#pragma unroll
+      for (int p = 0; p < NCW; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          accS[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
+    if (tid < D) zinit += st[D * D + tid];
+  }
+  if (tid < D) zf[tid] = zinit;
+
+  for (int64_t c0 = t0; c0 < t1; c0 += C) {
+    for (int idx = tid; idx < C * (D / 4); idx += 256) {
+      const int row = idx / (D / 4), c4 = idx % (D / 4);
+      const int64_t tok = c0 + row;
+      f32x4 qq = zero4(), kk = zero4(), vv = zero4();
+      if (tok < t1) {
+        qq = *reinterpret_cast<const f32x4*>(Q + tok * D + c4 * 4);
+        kk = *reinterpret_cast<const f32x4*>(K + tok * D + c4 * 4);
+        vv = *reinterpret_cast<const f32x4*>(V + tok * D + c4 * 4);
+        qq.x = phi(qq.x); qq.y = phi(qq.y); qq.z = phi(qq.z); qq.w = phi(qq.w);
+        kk.x = phi(kk.x); kk.y = phi(kk.y); kk.z = phi(kk.z); kk.w = phi(kk.w);
+      }
+      *reinterpret_cast<f32x4*>(&Qn[row * LD + c4 * 4]) = qq;
+      *reinterpret_cast<f32x4*>(&Kn[row * LD + c4 * 4]) = kk;
+      *reinterpret_cast<f32x4*>(&Vn[row * LD + c4 * 4]) = vv;
+    }
+    __syncthreads();
+
+    for (int it = 0; it < NI; ++it) {
+      f32x4 accA[NI];
+#pragma unroll
+      for (int jt = 0; jt < NI; ++jt) {
+        accA[jt] = zero4();
+        if (jt <= it) {
+          for (int ks = 0; ks < D / 4; ++ks)
+            accA[jt] = mfma_f32(Kn[(jt * 16 + l16) * LD + ks * 4 + g], Qn[(it * 16 + l16) * LD + ks * 4 + g], accA[jt]);
+        }
+        if (jt == it) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (g * 4 + r > l16) accA[jt][r] = 0.f;
+        }
+      }
+      f32x4 acco[NCW];
+      f32x4 accd = zero4();
+#pragma unroll
+      for (int p = 0; p < NCW; ++p) acco[p] = zero4();
+      // inter-chunk: k-slot g <-> feature 16*at + 4g + r; the state accumulator is the operand
+#pragma unroll
+      for (int at = 0; at < NA; ++at)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int fa = at * 16 + g * 4 + r;
+          const float qv = Qn[(it * 16 + l16) * LD + fa];
+#pragma unroll
+          for (int p = 0; p < NCW; ++p) acco[p] = mfma_f32(accS[at][p][r], qv, acco[p]);
+          accd = mfma_f32(l16 == 0 ? zf[fa] : 0.f, qv, accd);
+        }
+      // intra-chunk: k-slot g <-> key 16*jt + 4g + r; the A^T accumulator is the operand
+#pragma unroll
+      for (int jt = 0; jt < NI; ++jt) {
+        if (jt <= it) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = jt * 16 + g * 4 + r;
+#pragma unroll
+            for (int p = 0; p < NCW; ++p)
+              acco[p] = mfma_f32(Vn[j * LD + (wave + 4 * p) * 16 + l16], accA[jt][r], acco[p]);
+            accd = mfma_f32(l16 == 0 ? 1.f : 0.f, accA[jt][r], accd);
+          }
+        }
+      }
+      const float den = __shfl(accd[0], l16);
+      const int64_t row = c0 + it * 16 + l16;
+      if (row < t1) {
+#pragma unroll
+        for (int p = 0; p < NCW; ++p) {
+          f32x4 o = {acco[p][0] / den, acco[p][1] / den, acco[p][2] / den, acco[p][3] / den};
+          *reinterpret_cast<f32x4*>(O + row * D + (wave + 4 * p) * 16 + g * 4) = o;
+        }
+      }
+    }
+    __syncthreads();  // zf and the tiles are no longer read for outputs
+
+    // state update: S[:, own cols] += phi(K)^T V, z += column sums of phi(K)
+    for (int ks = 0; ks < C / 4; ++ks) {
+#pragma unroll
+      for (int at = 0; at < NA; ++at) {
+        const float ak = Kn[(ks * 4 + g) * LD + at * 16 + l16];
+#pragma unroll
+        for (int p = 0; p < NCW; ++p)
+          accS[at][p] = mfma_f32(ak, Vn[(ks * 4 + g) * LD + (wave + 4 * p) * 16 + l16], accS[at][p]);
+      }
+    }
+    if (tid < D) {
+      float zs = 0.f;
+      for (int j = 0; j < C; ++j) zs += Kn[j * LD + tid];
+      zf[tid] += zs;
+    }
+    __syncthreads();  // before the next chunk overwrites the tiles
+  }
+}
+
+template <int D, int C>
+static hipError_t launch_causal_t(const CausalArgs& a, int dtype, hipStream_t s) {
+  const unsigned blocks = (unsigned)(a.bh * a.segs);
+  if (dtype == 1) {
+    hipLaunchKernelGGL((causal_bf16<D, C>), dim3(blocks), dim3(256), 0, s, a);
+  } else {
+    if constexpr (D * C <= 8192)
+      hipLaunchKernelGGL((causal_f32<D, C>), dim3(blocks), dim3(256), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s) {
+  if (d == 64) return chunk == 64 ? launch_causal_t<64, 64>(a, dtype, s) : launch_causal_t<64, 128>(a, dtype, s);
+  return chunk == 64 ? launch_causal_t<128, 64>(a, dtype, s) : launch_causal_t<128, 128>(a, dtype, s);
+}
+
+}  // namespace la

@@ -1,0 +1,121 @@
+// la_common.h -- device helpers shared by the gfx950 linear-attention kernels.
+//
+// Conventions used by every kernel:
+//  * wave64; a workgroup of 256 threads is 4 waves.
+//  * bf16 is carried as raw 16-bit patterns packed two per 32-bit word (low half = lower
+//    index).  Rounding fp32 -> bf16 is round-to-nearest-even (v_cvt_pk_bf16_f32).
+//  * MFMA lane layouts (checked on gfx950 hardware):
+//      v_mfma_f32_16x16x32_bf16: A lane l holds row l%16, k = 8*(l/16)+e (e < 8);
+//                                B lane l holds column l%16, the same k; the 4 results of
+//                                lane l are rows 4*(l/16)+r (r < 4) of column l%16.
+//      v_mfma_f32_16x16x4_f32:   A lane l holds row l%16, k = l/16; B column l%16, k = l/16;
+//                                results as above.
+//    A reduction index may be mapped to the 8 (or 1) k-slots of a lane in any order, as long
+//    as both operands use the same mapping; several kernels use that to feed an MFMA result
+//    straight back in as an operand without moving data between lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// phi(x) = elu(x) + 1 with alpha = 1: x + 1 above zero, exp(x) at or below zero
+// ("Efficient Transformers: Linear Attention and Flash Attention", section "Linear attention",
+// feature map elu + 1).  exp is the hardware base-2 exponential of x*log2(e); for x < -87 the
+// result may flush to zero.
+__device__ __forceinline__ float phi(float x) {
+  float e = __builtin_amdgcn_exp2f(x * kLog2e);
+  return x > 0.f ? x + 1.f : e;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// two fp32 -> packed bf16 pair (round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t phi_pair(uint32_t w) {
+  return pack_bf16(phi(bf_lo(w)), phi(bf_hi(w)));
+}
+
+__device__ __forceinline__ u32x4 phi_bf16x8(u32x4 x) {
+  u32x4 r;
+  r.x = phi_pair(x.x);
+  r.y = phi_pair(x.y);
+  r.z = phi_pair(x.z);
+  r.w = phi_pair(x.w);
+  return r;
+}
+
+// Sum of the 8 bf16 values of a packed vector, in fp32.
+__device__ __forceinline__ float sum_bf16x8(u32x4 x) {
+  return ((bf_lo(x.x) + bf_hi(x.x)) + (bf_lo(x.y) + bf_hi(x.y))) +
+         ((bf_lo(x.z) + bf_hi(x.z)) + (bf_lo(x.w) + bf_hi(x.w)));
+}
+
+// 8x8 transpose of 16-bit elements held as 8 rows of 8 (one u32x4 per row).
+// out[e] = (row0[e], row1[e], ..., row7[e]).
+__device__ __forceinline__ uint32_t pick(uint32_t w_even_row, uint32_t w_odd_row, int e) {
+  // low half of result = element e of the even row, high half = element e of the odd row
+  return (e & 1) ? __builtin_amdgcn_perm(w_odd_row, w_even_row, 0x07060302u)
+                 : __builtin_amdgcn_perm(w_odd_row, w_even_row, 0x05040100u);
+}
+
+__device__ __forceinline__ uint32_t word(const u32x4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    out[e].x = pick(word(in[0], e >> 1), word(in[1], e >> 1), e);
+    out[e].y = pick(word(in[2], e >> 1), word(in[3], e >> 1), e);
+    out[e].z = pick(word(in[4], e >> 1), word(in[5], e >> 1), e);
+    out[e].w = pick(word(in[6], e >> 1), word(in[7], e >> 1), e);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+__device__ __forceinline__ u32x4 zero_u4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+// 16-byte global load / store
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Wave-level sum over the 4 lanes that share l % 16 (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace la

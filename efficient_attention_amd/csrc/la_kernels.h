@@ -1,0 +1,63 @@
+// la_kernels.h -- argument blocks and launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// Stage-1 state sums over token ranges ("groups": one per head for the non-causal form, one
+// per head and leading segment for the causal form), split into `slices` workgroups each.
+struct KvStateArgs {
+  const void* k;
+  const void* v;
+  float* partials;      // [groups][slices][D*D + D] fp32 (unused when slices == 1)
+  float* state;         // [groups][D*D + D] fp32: KV row-major, then z
+  unsigned* counters;   // [groups], zero on entry, left zero on exit
+  int64_t n;            // tokens per head
+  int64_t group_len;    // tokens per group (the last group of a head may be shorter)
+  int64_t groups_per_head;
+  int64_t groups;       // total groups
+  int64_t slices;       // workgroups per group
+  int64_t slice_len;    // tokens per workgroup (multiple of the kernel's tile)
+};
+
+struct NcOutArgs {
+  const void* q;
+  void* out;
+  const float* state;   // [bh][D*D + D]
+  int64_t n;
+  int64_t bh;
+};
+
+struct CausalArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const float* seg_state;  // [bh][segs-1][D*D + D]: sums over each leading segment (or null)
+  int64_t n;
+  int64_t bh;
+  int64_t segs;            // segments per head
+  int64_t seg_len;         // tokens per segment (multiple of chunk)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* S;
+  float* z;
+  void* out;
+  int64_t bh;
+};
+
+hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s);
+hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s);
+hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
+
+// Tile sizes the host needs for workspace planning.
+inline int64_t kv_state_tile(int d, int dtype) { return dtype == 1 ? 16384 / d : 64; }
+
+}  // namespace la

@@ -1,0 +1,126 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) kernelized linear-attention library.
+ *
+ * The operation.  For each (batch b, head h), with phi(x) = elu(x) + 1 (alpha = 1, i.e.
+ * x + 1 for x > 0 and exp(x) otherwise) applied elementwise to queries and keys:
+ *
+ *     out_i = phi(q_i) . KV  /  phi(q_i) . z,   KV = sum_j phi(k_j) v_j^T,  z = sum_j phi(k_j)
+ *
+ * ("Efficient Transformers: Linear Attention and Flash Attention", section "Linear
+ * attention: reordering the matmuls, not shrinking them", eq. Attention_i).  The sums run
+ * over every key (non-causal) or over keys j <= i (causal: the running state of section
+ * "The recurrent view: attention as an RNN", S_t = S_{t-1} + phi(k_t) v_t^T,
+ * z_t = z_{t-1} + phi(k_t)).  The feature dimension D equals the head dimension d because
+ * phi is elementwise.  There is no 1/sqrt(d) factor and no epsilon in the denominator.
+ *
+ * Layout.  q, k, v and out are dense row-major [B][H][n][d] (d innermost); for the decode
+ * step they are [B][H][d].  The state S is [B][H][d][d] fp32 with S[a][c] = sum phi(k)_a v_c
+ * (feature row a, value column c), and z is [B][H][d] fp32.  out has the element type of q.
+ *
+ * Pointers.  Every tensor pointer is a DEVICE pointer on the HIP device that is current
+ * on the calling thread; `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Base pointers must be 16-byte aligned.  The caller owns every buffer,
+ * including the workspace; the library allocates nothing, frees nothing, keeps no pointer
+ * after returning and has no mutable global state.
+ *
+ * Errors.  Every entry point validates its arguments before launching anything and
+ * returns LA_OK or a negative LA_ERR_* code; on an error nothing is written.  Empty
+ * shapes (B*H*n == 0) are successful no-ops.  Kernels run asynchronously on `stream`:
+ * results are valid after the caller synchronises.  A launch failure returns LA_ERR_HIP.
+ * Inputs whose phi underflows to zero for every feature (entries below about -87 in fp32)
+ * give the IEEE result of 0/0, as the formula would.
+ *
+ * Supported shapes: d in {64, 128}; chunk in {64, 128}; element types fp32 and bf16
+ * (state and accumulation are always fp32).
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+
+enum {
+  LA_OK = 0,
+  LA_ERR_NULL = -1,        /* a required pointer is NULL while the shape is non-empty   */
+  LA_ERR_SHAPE = -2,       /* negative or overflowing dimension                          */
+  LA_ERR_DTYPE = -3,       /* unknown element type                                       */
+  LA_ERR_UNSUPPORTED = -4, /* d or chunk outside the supported set                      */
+  LA_ERR_ALIGN = -5,       /* a base pointer is not 16-byte aligned                      */
+  LA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes size  */
+  LA_ERR_ALIAS = -7,       /* out overlaps an input (or the state)                       */
+  LA_ERR_HIP = -8          /* a kernel launch failed                                     */
+};
+
+/* ABI version of the loaded library (LA_ABI_VERSION at build time). */
+int la_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* la_status_string(int status);
+
+/* Bytes of device workspace la_forward_noncausal needs for this shape (0 for an empty
+ * shape; (size_t)0 also for unsupported arguments, which the call itself reports). */
+size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype);
+
+/*
+ * Non-causal forward: every query attends to all n keys of its (b, h).
+ *   q, k, v : [B][H][n][d] of `dtype`, read only
+ *   out     : [B][H][n][d] of `dtype`, written; must not overlap q, k, v or workspace
+ *   workspace, workspace_bytes : device scratch of at least
+ *             la_noncausal_workspace_bytes(B, H, n, d, dtype) bytes.  Its counter area
+ *             must be zero before the FIRST call that uses it (zero-fill the whole buffer
+ *             once); every call leaves it zero again, so it can be reused without clearing.
+ *             Two calls that share a workspace must not run concurrently.
+ * Two stages ("Efficient Transformers ...", section "Linear attention": the D x d sum and the
+ * key sum are built once and shared by every query): split-n partial sums of
+ * [phi(K)^T V | phi(K)^T 1] reduced in a fixed order (deterministic), then one pass over
+ * the queries.
+ */
+int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
+                         int64_t H, int64_t n, int64_t d, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace la_forward_causal needs (may be 0). */
+size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk,
+                                 int dtype);
+
+/*
+ * Causal forward: query i attends to keys j <= i (inclusive) of its (b, h).
+ *   q, k, v, out : as for la_forward_noncausal
+ *   chunk        : 64 or 128; the tile of the chunked evaluation.  Within a chunk the masked
+ *                  pairwise weights are used directly, earlier tokens enter through the
+ *                  running state (S, z) ("The recurrent view"); the result does not depend
+ *                  on chunk beyond rounding.
+ *   workspace    : at least la_causal_workspace_bytes(...) bytes, same zero-before-first-use
+ *                  rule as the non-causal workspace (may be NULL when that size is 0).
+ */
+int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
+                      int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step for B*H independent heads, in place on the state
+ * ("The recurrent view"; the fixed-size state of Active recall A5):
+ *     S += phi(k) v^T ;  z += phi(k) ;  out = phi(q)^T S / phi(q)^T z
+ * (the new token is folded in first, then read with q).
+ *   q, k, v : [B][H][d] of `dtype`, read only
+ *   S       : [B][H][d][d] fp32, read and written in place
+ *   z       : [B][H][d] fp32, read and written in place
+ *   out     : [B][H][d] of `dtype`, written; must not overlap q, k, v, S or z
+ * The state is the whole checkpoint: copying S and z out and back resumes bit-exactly.
+ */
+int la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
+                   int64_t B, int64_t H, int64_t d, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol that
+include/linattn.h declares, and rejects bad arguments before launching anything.
+
+The validation calls pass fake (never dereferenced) addresses: every case here fails or
+returns before the library touches HIP.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+ea = pytest.importorskip("efficient_attention_amd")
+
+
+def _lib():
+    if not os.path.exists(ea.LIB_PATH):
+        pytest.fail("liblinattn.so is not built; run `python -m efficient_attention_amd.build`")
+    return ea.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def _header_constant(name):
+    m = re.search(r"\b%s\s*=\s*(-?\d+)" % name, open(HEADER).read())
+    if m is None:
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    declared = _declared_functions()
+    assert set(declared) == set(ea.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert ea.la_abi_version() == _header_constant("LA_ABI_VERSION")
+    for code in range(-8, 1):
+        s = ea.la_status_string(code)
+        assert isinstance(s, str) and s
+    assert ea.la_status_string(-1000) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert ea.la_noncausal_workspace_bytes(0, 4, 100, 64, 1) == 0
+    assert ea.la_noncausal_workspace_bytes(2, 4, 0, 64, 1) == 0
+    assert ea.la_noncausal_workspace_bytes(2, 4, 100, 96, 1) == 0       # unsupported d
+    w = ea.la_noncausal_workspace_bytes(8, 16, 16384, 64, 1)
+    # at least one fp32 [KV | z] state per head
+    assert w >= 8 * 16 * (64 * 64 + 64) * 4
+    assert ea.la_causal_workspace_bytes(1, 1, 10, 64, 96, 1) == 0       # unsupported chunk
+    # many heads: one segment per head, no workspace
+    assert ea.la_causal_workspace_bytes(64, 8, 4096, 64, 64, 1) == 0
+    # one head: the sequence is cut into segments, whose state sums need a workspace
+    assert ea.la_causal_workspace_bytes(1, 1, 4096, 64, 64, 0) > 0
+
+
+P = ctypes.c_void_p
+
+
+def _nc(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, B=1, H=1, n=8, d=64, dtype=1,
+        ws=0x100000, wsb=1 << 30):
+    return lib.la_forward_noncausal(P(q), P(k), P(v), P(out), B, H, n, d, dtype, P(ws), wsb, None)
+
+
+def _ca(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, B=1, H=1, n=8, d=64, chunk=64, dtype=1,
+        ws=0x100000, wsb=1 << 30):
+    return lib.la_forward_causal(P(q), P(k), P(v), P(out), B, H, n, d, chunk, dtype, P(ws), wsb, None)
+
+
+def _dec(lib, q=0x1000, k=0x2000, v=0x3000, S=0x10000, z=0x20000, out=0x4000, B=1, H=1, d=64, dtype=1):
+    return lib.la_decode_step(P(q), P(k), P(v), P(S), P(z), P(out), B, H, d, dtype, None)
+
+
+def test_validation_noncausal():
+    lib = _lib()
+    assert _nc(lib, dtype=7) == -3
+    assert _nc(lib, n=-1) == -2
+    assert _nc(lib, B=1 << 40, H=1 << 40) == -2
+    assert _nc(lib, d=96) == -4
+    assert _nc(lib, n=0, q=0, k=0, v=0, out=0) == 0          # empty: no-op, no pointers needed
+    assert _nc(lib, B=0) == 0
+    assert _nc(lib, q=0) == -1
+    assert _nc(lib, out=0) == -1
+    assert _nc(lib, k=0x2008) == -5                          # misaligned
+    assert _nc(lib, ws=0) == -6
+    assert _nc(lib, wsb=16) == -6
+    assert _nc(lib, out=0x1000) == -7                        # out aliases q
+    assert _nc(lib, out=0x100000 + 64) == -7                  # out inside the workspace
+
+
+def test_validation_causal():
+    lib = _lib()
+    assert _ca(lib, chunk=96) == -4
+    assert _ca(lib, chunk=128, d=128, dtype=0) == -4          # fp32 (d, chunk) = (128, 128)
+    assert _ca(lib, d=32) == -4
+    assert _ca(lib, n=0, q=0) == 0
+    assert _ca(lib, v=0) == -1
+    assert _ca(lib, out=0x4004) == -5
+    assert _ca(lib, n=4096, ws=0) == -6                      # one head -> needs a workspace
+    assert _ca(lib, out=0x2000) == -7
+
+
+def test_validation_decode():
+    lib = _lib()
+    assert _dec(lib, dtype=5) == -3
+    assert _dec(lib, d=100) == -4
+    assert _dec(lib, B=0, q=0) == 0
+    assert _dec(lib, S=0) == -1
+    assert _dec(lib, z=0x20004) == -5
+    assert _dec(lib, out=0x10000) == -7                      # out aliases S
+    assert _dec(lib, z=0x10000 + 64) == -7                   # z inside S

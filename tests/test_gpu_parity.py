@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, on seeded inputs.
+
+Sizes here span several tiles and ragged tails while the oracle still finishes in seconds.
+Error measure: normwise per head (tests/metrics.py); bars: fp32 <= 1e-4, bf16 <= 2e-2.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from metrics import TOL_BF16, TOL_F32, floored_elementwise_err, normwise_err
+from gpu_util import f64, from_dev, need_gpu, say, to_dev
+from seeded_inputs import WORKLOADS, encode, forward_inputs, random_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": TOL_F32, "bf16": TOL_BF16}
+
+
+@pytest.fixture(scope="module")
+def ea():
+    need_gpu()
+    import efficient_attention_amd
+    return efficient_attention_amd
+
+
+def run_forward(ea, form, q, k, v, dtype, chunk=64):
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    if form == "noncausal":
+        out = ea.la_forward_noncausal(tq, tk, tv)
+    else:
+        out = ea.la_forward_causal(tq, tk, tv, chunk=chunk)
+    return from_dev(out, dtype)
+
+
+def oracle_forward(form, q, k, v, dtype):
+    Q, K, V = f64(q, dtype), f64(k, dtype), f64(v, dtype)
+    if form == "noncausal":
+        return oracle.noncausal_linear(Q, K, V)
+    return oracle.causal_recurrent(Q, K, V)
+
+
+# ----------------------------------------------------------------------------- worked example
+def _embedded_worked_example(d):
+    """The pages' hand-worked 3-token example, fed through elu + 1 preimages: phi(0) = 1,
+    phi(1) = 2, phi(2) = 3, phi(-1e4) = 0, and padded to width d with phi = 0 features and
+    zero values."""
+    Qp = np.full((3, d), -1e4, dtype=np.float32)
+    Kp = np.full((3, d), -1e4, dtype=np.float32)
+    V = np.zeros((3, d), dtype=np.float32)
+    Qp[:, :2] = [[0, -1e4], [-1e4, 0], [0, 0]]
+    Kp[:, :2] = [[1, 0], [0, 2], [0, 0]]
+    V[:, :2] = [[1, 0], [0, 1], [1, 1]]
+    return Qp[None, None], Kp[None, None], V[None, None]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_worked_example_through_gpu(ea, dtype, d):
+    q, k, v = (encode(x, dtype) for x in _embedded_worked_example(d))
+    printed = np.array([[0.75, 0.5], [0.4, 0.8], [5 / 9, 2 / 3]])
+    causal_rows = np.array([[1.0, 0.0], [0.25, 0.75], [5 / 9, 2 / 3]])
+    tol = 1e-6 if dtype == "f32" else 4e-3
+    say("worked example noncausal", dtype, d)
+    g = run_forward(ea, "noncausal", q, k, v, dtype)
+    np.testing.assert_allclose(g[0, 0, :, :2], printed, atol=tol)
+    assert np.all(g[0, 0, :, 2:] == 0)
+    for chunk in (64, 128):
+        if dtype == "f32" and d * chunk > 8192:
+            continue
+        say("worked example causal", dtype, d, chunk)
+        g = run_forward(ea, "causal", q, k, v, dtype, chunk)
+        np.testing.assert_allclose(g[0, 0, :, :2], causal_rows, atol=tol)
+    say("worked example decode", dtype, d)
+    import torch
+    S = torch.zeros((1, 1, d, d), dtype=torch.float32, device="cuda")
+    z = torch.zeros((1, 1, d), dtype=torch.float32, device="cuda")
+    for t in range(3):
+        o = ea.la_decode_step(to_dev(q[:, :, t], dtype), to_dev(k[:, :, t], dtype),
+                              to_dev(v[:, :, t], dtype), S, z)
+        np.testing.assert_allclose(from_dev(o, dtype)[0, 0, :2], causal_rows[t], atol=tol)
+    Sh = S.cpu().numpy()[0, 0]
+    np.testing.assert_array_equal(Sh[:2, :2], [[3, 2], [2, 4]])   # the printed K^T V
+    np.testing.assert_array_equal(z.cpu().numpy()[0, 0, :2], [4, 5])  # the printed key sum
+
+
+# ----------------------------------------------------------------------------- small configs
+def test_c1_noncausal_fp32_vs_linear_and_quadratic(ea):
+    w = WORKLOADS["C1"]
+    q, k, v = forward_inputs(w)
+    say("C1", w)
+    g = run_forward(ea, "noncausal", q, k, v, "f32")
+    Q, K, V = f64(q, "f32"), f64(k, "f32"), f64(v, "f32")
+    ref_lin = oracle.noncausal_linear(Q, K, V)
+    ref_quad = oracle.quadratic(Q, K, V, causal=False)
+    e1, e2 = normwise_err(g, ref_lin), normwise_err(g, ref_quad)
+    print("C1 normwise err vs linear %.3e vs quadratic %.3e, floored elementwise %.3e"
+          % (e1, e2, floored_elementwise_err(g, ref_lin)))
+    assert e1 <= TOL_F32 and e2 <= TOL_F32
+
+
+def test_c2_causal_fp32_chunk64(ea):
+    w = WORKLOADS["C2"]
+    q, k, v = forward_inputs(w)
+    say("C2", w)
+    g = run_forward(ea, "causal", q, k, v, "f32", chunk=64)
+    ref = oracle_forward("causal", q, k, v, "f32")
+    e = normwise_err(g, ref)
+    print("C2 normwise err %.3e floored elementwise %.3e" % (e, floored_elementwise_err(g, ref)))
+    assert e <= TOL_F32
+
+
+# ----------------------------------------------------------------------------- shape sweep
+CASES = []
+for form in ("noncausal", "causal"):
+    for dtype in ("f32", "bf16"):
+        for d in (64, 128):
+            for n in (1, 2, 3, 63, 64, 65, 127, 128, 129, 300, 1000):
+                for chunk in ((64, 128) if form == "causal" else (0,)):
+                    if form == "causal" and dtype == "f32" and d * chunk > 8192:
+                        continue
+                    CASES.append((form, dtype, d, n, chunk))
+
+
+@pytest.mark.parametrize("form,dtype,d,n,chunk", CASES)
+def test_shape_sweep(ea, form, dtype, d, n, chunk):
+    B, H = 2, 3
+    scale = 1.0 if dtype == "f32" else 1.0 / np.sqrt(d)
+    q, k, v = random_inputs(zlib.crc32(repr((form, dtype, d, n, chunk)).encode()) % 100000, (B, H, n, d), dtype, scale)
+    say(form, dtype, "d=%d n=%d chunk=%d" % (d, n, chunk))
+    g = run_forward(ea, form, q, k, v, dtype, chunk or 64)
+    ref = oracle_forward(form, q, k, v, dtype)
+    e = normwise_err(g, ref)
+    assert e <= TOL[dtype], e
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 64, 64), ("bf16", 128, 128), ("f32", 64, 64),
+                                           ("bf16", 64, 128), ("bf16", 128, 64), ("f32", 128, 64)])
+def test_causal_many_segments_ragged(ea, dtype, d, chunk):
+    # one head: the sequence is cut into many segments whose state sums seed each other
+    B, H, n = 1, 1, 16 * chunk + 37
+    q, k, v = random_inputs(77 + d + chunk, (B, H, n, d), dtype, 1.0 / np.sqrt(d))
+    assert ea.la_causal_workspace_bytes(B, H, n, d, chunk, 1 if dtype == "bf16" else 0) > 0
+    say("causal segments", dtype, d, chunk, n)
+    g = run_forward(ea, "causal", q, k, v, dtype, chunk)
+    ref = oracle_forward("causal", q, k, v, dtype)
+    assert normwise_err(g, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_invariance(ea, dtype):
+    d, n = 64, 777
+    q, k, v = random_inputs(5, (2, 2, n, d), dtype, 1.0 / np.sqrt(d))
+    ref = oracle_forward("causal", q, k, v, dtype)
+    outs = []
+    for chunk in (64, 128):
+        say("chunk invariance", dtype, chunk)
+        g = run_forward(ea, "causal", q, k, v, dtype, chunk)
+        assert normwise_err(g, ref) <= TOL[dtype]
+        outs.append(g)
+    assert normwise_err(outs[0], outs[1]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("form", ["noncausal", "causal"])
+def test_invariants_on_gpu(ea, form):
+    # V = 1 gives out = 1; a constant value row gives that row; out_0 = v_0 for causal
+    d, n = 64, 200
+    q, k, _ = random_inputs(9, (1, 2, n, d), "f32", 1.0)
+    row = np.linspace(-2, 3, d, dtype=np.float32)
+    v = np.broadcast_to(row, q.shape).copy()
+    say("invariants", form)
+    g = run_forward(ea, form, q, k, v, "f32")
+    np.testing.assert_allclose(g, np.broadcast_to(row, g.shape), rtol=1e-5, atol=1e-5)
+    if form == "causal":
+        _, _, v2 = random_inputs(10, (1, 2, n, d), "f32", 1.0)
+        g2 = run_forward(ea, form, q, k, v2, "f32")
+        np.testing.assert_allclose(g2[:, :, 0], v2[:, :, 0], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("form", ["noncausal", "causal"])
+def test_extreme_inputs(ea, form):
+    # large magnitudes: phi spans exp(-60) .. 61, weights vary over many decades
+    d, n = 64, 300
+    q, k, v = random_inputs(11, (1, 2, n, d), "f32", 20.0)
+    q = np.clip(q, -60, 60)
+    k = np.clip(k, -60, 60)
+    say("extreme inputs", form)
+    g = run_forward(ea, form, q, k, v, "f32")
+    ref = oracle_forward(form, q, k, v, "f32")
+    assert normwise_err(g, ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("form", ["noncausal", "causal"])
+def test_deterministic(ea, form):
+    d, n = 128, 1500
+    q, k, v = random_inputs(12, (1, 3, n, d), "bf16", 1.0 / np.sqrt(d))
+    say("determinism", form)
+    a = run_forward(ea, form, q, k, v, "bf16", 128)
+    b = run_forward(ea, form, q, k, v, "bf16", 128)
+    assert np.array_equal(a, b)
+
+
+def test_errors_write_nothing(ea):
+    import torch
+    q = torch.ones((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 7.0)
+    say("error path")
+    with pytest.raises(ea.LinAttnError):
+        ea.la_forward_causal(q, q, q, chunk=96, out=out)
+    with pytest.raises(ea.LinAttnError):
+        ea.la_forward_noncausal(q, q, q, out=out, ws=torch.zeros(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+# ----------------------------------------------------------------------------- decode
+def _state_from_prior(pk, pv, dtype):
+    S, z = oracle.state_from_tokens_matmul(f64(pk, dtype), f64(pv, dtype))
+    return S.astype(np.float32), z.astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_decode_steps_vs_oracle(ea, dtype, d):
+    import torch
+    B, H, prior, steps = 3, 5, 100, 40
+    scale = 1.0 / np.sqrt(d)
+    pk, pv, _ = random_inputs(20 + d, (B, H, prior, d), dtype, scale)
+    q, k, v = random_inputs(21 + d, (B, H, steps, d), dtype, scale)
+    S0, z0 = _state_from_prior(pk, pv, dtype)
+    S = torch.from_numpy(S0).cuda()
+    z = torch.from_numpy(z0).cuda()
+    Sr, zr = S0.astype(np.float64), z0.astype(np.float64)
+    say("decode", dtype, d)
+    for t in range(steps):
+        o = ea.la_decode_step(to_dev(q[:, :, t], dtype), to_dev(k[:, :, t], dtype), to_dev(v[:, :, t], dtype), S, z)
+        ro, Sr, zr = oracle.decode_step(f64(q[:, :, t], dtype), f64(k[:, :, t], dtype), f64(v[:, :, t], dtype), Sr, zr)
+        e = normwise_err(from_dev(o, dtype), ro, head_axes_last=1)
+        assert e <= TOL[dtype], (t, e)
+    assert normwise_err(S.cpu().numpy(), Sr) <= 1e-5
+    assert normwise_err(z.cpu().numpy(), zr, head_axes_last=1) <= 1e-5
+
+
+def test_decode_from_zero_equals_causal(ea):
+    import torch
+    B, H, n, d = 2, 2, 70, 64
+    q, k, v = random_inputs(30, (B, H, n, d), "bf16", 1.0 / np.sqrt(d))
+    S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+    z = torch.zeros((B, H, d), dtype=torch.float32, device="cuda")
+    say("decode from zero vs causal")
+    outs = []
+    for t in range(n):
+        o = ea.la_decode_step(to_dev(q[:, :, t], "bf16"), to_dev(k[:, :, t], "bf16"), to_dev(v[:, :, t], "bf16"), S, z)
+        outs.append(from_dev(o, "bf16"))
+    g = np.stack(outs, axis=2)
+    ref = oracle_forward("causal", q, k, v, "bf16")
+    assert normwise_err(g, ref) <= TOL_BF16
+    gc = run_forward(ea, "causal", q, k, v, "bf16", 64)
+    assert normwise_err(g, gc) <= TOL_BF16
+
+
+def test_decode_resume_bitwise(ea):
+    import torch
+    B, H, n, d = 4, 8, 24, 128
+    q, k, v = random_inputs(31, (B, H, n, d), "bf16", 1.0 / np.sqrt(d))
+    dq, dk, dv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+
+    def steps(S, z, t0, t1):
+        res = []
+        for t in range(t0, t1):
+            res.append(ea.la_decode_step(dq[:, :, t].contiguous(), dk[:, :, t].contiguous(),
+                                         dv[:, :, t].contiguous(), S, z).clone())
+        return res
+
+    say("decode resume")
+    S1 = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+    z1 = torch.zeros((B, H, d), dtype=torch.float32, device="cuda")
+    full = steps(S1, z1, 0, n)
+    S2 = torch.zeros_like(S1)
+    z2 = torch.zeros_like(z1)
+    first = steps(S2, z2, 0, n // 2)
+    saved = (S2.cpu().numpy().tobytes(), z2.cpu().numpy().tobytes())
+    S3 = torch.from_numpy(np.frombuffer(saved[0], dtype=np.float32).reshape(B, H, d, d).copy()).cuda()
+    z3 = torch.from_numpy(np.frombuffer(saved[1], dtype=np.float32).reshape(B, H, d).copy()).cuda()
+    second = steps(S3, z3, n // 2, n)
+    for a, b in zip(full, first + second):
+        assert torch.equal(a, b)
+    assert torch.equal(S1, S3) and torch.equal(z1, z3)

@@ -316,3 +316,11 @@ def test_state_size_matches_accounting():
         assert memory_linear_attention(n, 128) == 66048
     _, kv, z = oracle.noncausal_linear(*_rand(20, 10, 64), return_state=True)
     assert (kv[0].size + z[0].size) * 4 == 16640
+
+
+def test_state_matmul_equals_loop():
+    _, k, v = _rand(21, 50, 8, bh=3)
+    S1, z1 = oracle.state_accumulate(k, v)
+    S2, z2 = oracle.state_from_tokens_matmul(k, v)
+    np.testing.assert_allclose(S2, S1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z2, z1, rtol=1e-13)
