@@ -224,3 +224,15 @@ def state_accumulate(k, v, S=None, z=None, feature_map: int = PHI_ELU1):
     z2 = np.zeros((BH, d)) if z is None else np.array(_f64(z).reshape(BH, d), copy=True)
     lib.orc_state_accumulate(_ptr(K), _ptr(V), _ptr(S2), _ptr(z2), BH, n, d, feature_map)
     return S2.reshape(shape[:-2] + (d, d)), z2.reshape(shape[:-2] + (d,))
+
+
+def state_from_tokens_matmul(k, v, feature_map: int = PHI_ELU1):
+    """(S, z) = (phi(K)^T V, sum_j phi(k_j)) per head for k, v [..., n, d], with the library
+    fp64 matrix product as the one step (used to build large decode states quickly; pinned
+    against state_accumulate)."""
+    K = _f64(k)
+    V = _f64(v)
+    fk = phi(K, feature_map)
+    S = np.matmul(np.swapaxes(fk, -1, -2), V)
+    z = fk.sum(axis=-2)
+    return S, z
