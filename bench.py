@@ -1,0 +1,275 @@
+"""Throughput of the kernelized linear-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
+
+One step = the whole hot path over one batch of each synthetic workload:
+  * non-causal forward, bf16, B=8 H=16 n=16384 d=64 (feature map, split-n KV/z sums, output);
+  * causal forward, bf16, B=4 H=32 n=65536 d=128, chunk 128, run as its two library stages
+    (leading-segment state sums, then the chunked pass) so each is timed on its own;
+  * one decode step, bf16, 256 sequences x 32 heads, d=128, on a state built from 1024 prior
+    tokens by the library's own state-sum call.
+Inputs are seeded N(0,1)/sqrt(d) (seeded_inputs), resident in HBM before timing starts.
+The JSON line reports tokens/s of the whole step, per-stage HIP-event timings with algorithmic
+GB/s against the 8 TB/s HBM peak, the roofline of the dominant kernel, and the fp64 CPU
+oracle timed on a bounded sample of the same work (single thread) as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "tokens/sec + HBM GB/s (% peak), linear-attn fwd n=16K/64K, d=64/128, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "causal_bf16_d128_c128_traffic.json")
+ROOFLINE_SOURCES = ["efficient_attention_amd/csrc/la_causal.hip", "efficient_attention_amd/csrc/la_common.h"]
+
+
+def algorithmic_bytes(B, H, n, d, eb):
+    """q, k, v read once and out written once: 4 * d * eb bytes per head-token."""
+    return 4 * B * H * n * d * eb
+
+
+def decode_bytes(BH, d, eb):
+    """per head: state read + write (2 * (d*d + d) * 4 B) plus q, k, v, out (4 * d * eb)."""
+    return BH * (2 * (d * d + d) * 4 + 4 * d * eb)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for rel in ROOFLINE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter runs,
+    or None when absent or taken on different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
+    """The fp64 oracle, as it stands, single-threaded, on a bounded sample of the step's work,
+    scaled to the whole step by head counts (heads are independent and equal-sized)."""
+    import oracle
+    from seeded_inputs import bf16_bits_to_f32
+
+    def f64(x):
+        return bf16_bits_to_f32(x).astype(np.float64)
+
+    oracle._load()
+    # non-causal: 2 heads of n = 16384
+    Q, K, V = f64(q3[0, :2]), f64(k3[0, :2]), f64(v3[0, :2])
+    t = time.perf_counter()
+    oracle.noncausal_linear(Q, K, V)
+    t_nc = (time.perf_counter() - t) / 2 * (C3.B * C3.H)
+    # causal: 1 head of n = 65536 by the recurrence
+    Q, K, V = f64(q4[0, :1]), f64(k4[0, :1]), f64(v4[0, :1])
+    t = time.perf_counter()
+    oracle.causal_recurrent(Q, K, V)
+    t_c = (time.perf_counter() - t) * (C4.B * C4.H)
+    # decode: one step for 1024 of the 8192 heads
+    dq, dk, dv, S0, z0 = dec
+    t = time.perf_counter()
+    oracle.decode_step(f64(dq[:4]), f64(dk[:4]), f64(dv[:4]), S0[:4], z0[:4])
+    t_d = (time.perf_counter() - t) * (C5.B * C5.H) / (4 * C5.H)
+    step_s = t_nc + t_c + t_d
+    tokens = C3.B * C3.n + C4.B * C4.n + C5.B
+    return {
+        "value": tokens / step_s,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("fp64 C oracle, 1 thread: non-causal 2 of 128 heads (n=16384), causal 1 of 128 "
+                   "heads (n=65536, recurrence), decode 1 step of 128 of 8192 heads; each scaled by "
+                   "its head count to one step of %d tokens; step time %.1f s" % (tokens, step_s)),
+        "host_cores": os.cpu_count(),
+        "cpu_model": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of 2 GiB (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import efficient_attention_amd as ea
+    from seeded_inputs import WORKLOADS, decode_inputs, forward_inputs
+
+    def log(*m):
+        print("[bench]", *m, file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    C3, C4, C5 = WORKLOADS["C3"], WORKLOADS["C4"], WORKLOADS["C5"]
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    log("generating C3 inputs")
+    q3, k3, v3 = forward_inputs(C3)
+    Q3, K3, V3 = to_dev(q3), to_dev(k3), to_dev(v3)
+    log("generating C4 inputs")
+    q4, k4, v4 = forward_inputs(C4)
+    Q4, K4, V4 = to_dev(q4), to_dev(k4), to_dev(v4)
+    nsteps_in = min(C5.n, args.warmup + args.steps)
+    log("generating C5 inputs (%d distinct steps)" % nsteps_in)
+    pk, pv, dq, dk, dv = decode_inputs(C5, steps=nsteps_in)
+    DQ = to_dev(dq).permute(2, 0, 1, 3).contiguous()
+    DK = to_dev(dk).permute(2, 0, 1, 3).contiguous()
+    DV = to_dev(dv).permute(2, 0, 1, 3).contiguous()
+    O3 = torch.empty_like(Q3)
+    O4 = torch.empty_like(Q4)
+    O5 = torch.empty_like(DQ[0])
+
+    # decode state from the 1024 prior tokens (the library's own state sums)
+    PK, PV = to_dev(pk), to_dev(pv)
+    sums = ea.la_state_sums(PK, PV, C5.prior, 1)
+    d5 = C5.d
+    S5 = sums[:, :, 0, : d5 * d5].reshape(C5.B, C5.H, d5, d5).contiguous()
+    Z5 = sums[:, :, 0, d5 * d5:].contiguous()
+    del PK, PV, sums
+    S5_init, Z5_init = S5.clone(), Z5.clone()
+
+    seg_len = ea.la_causal_plan(C4.B, C4.H, C4.n, C4.d, C4.chunk, torch.bfloat16)
+    nseg = -(-C4.n // seg_len)
+    sums4 = torch.empty((C4.B, C4.H, max(nseg - 1, 1), C4.d * C4.d + C4.d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ea.la_forward_noncausal(Q3, K3, V3, out=O3)
+        if ev is not None:
+            ev[1].record(stream)
+        if nseg > 1:
+            ea.la_state_sums(K4, V4, seg_len, nseg - 1, sums=sums4)
+        if ev is not None:
+            ev[2].record(stream)
+        ea.la_causal_segments(Q4, K4, V4, sums4 if nseg > 1 else None, seg_len, C4.chunk, out=O4)
+        if ev is not None:
+            ev[3].record(stream)
+        i = t % nsteps_in
+        ea.la_decode_step(DQ[i], DK[i], DV[i], S5, Z5, out=O5)
+        if ev is not None:
+            ev[4].record(stream)
+
+    log("warmup %d" % args.warmup)
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        step(args.warmup + t, evs[t])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    stages = ["noncausal", "causal_state_sums", "causal_chunked", "decode_step"]
+    stage_ms = {s: float(np.mean([evs[t][i].elapsed_time(evs[t][i + 1]) for t in range(args.steps)]))
+                for i, s in enumerate(stages)}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    b3 = algorithmic_bytes(C3.B, C3.H, C3.n, C3.d, 2)
+    b4 = algorithmic_bytes(C4.B, C4.H, C4.n, C4.d, 2)
+    b5 = decode_bytes(C5.B * C5.H, C5.d, 2)
+    tokens = C3.B * C3.n + C4.B * C4.n + C5.B
+    c4_ms = stage_ms["causal_state_sums"] + stage_ms["causal_chunked"]
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    breakdown = {
+        "noncausal_C3": {"ms": stage_ms["noncausal"], "tokens_per_s": C3.B * C3.n / (stage_ms["noncausal"] * 1e-3),
+                         "algorithmic_GBps": gbs(b3, stage_ms["noncausal"]),
+                         "pct_hbm_peak": 100 * gbs(b3, stage_ms["noncausal"]) / HBM_PEAK_GBS},
+        "causal_C4": {"ms": c4_ms, "state_sums_ms": stage_ms["causal_state_sums"],
+                      "chunked_ms": stage_ms["causal_chunked"], "segments_per_head": nseg,
+                      "tokens_per_s": C4.B * C4.n / (c4_ms * 1e-3),
+                      "algorithmic_GBps": gbs(b4, c4_ms), "pct_hbm_peak": 100 * gbs(b4, c4_ms) / HBM_PEAK_GBS},
+        "decode_C5": {"ms": stage_ms["decode_step"], "tokens_per_s": C5.B / (stage_ms["decode_step"] * 1e-3),
+                      "algorithmic_GBps": gbs(b5, stage_ms["decode_step"]),
+                      "pct_hbm_peak": 100 * gbs(b5, stage_ms["decode_step"]) / HBM_PEAK_GBS},
+    }
+    # dominant kernel: the chunked causal kernel (one launch per la_causal_segments call)
+    ach = gbs(b4, stage_ms["causal_chunked"])
+    roofline = {"kernel": "causal_bf16<128,128> (la_causal_segments, C4)", "bound": "hbm",
+                "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": measured_traffic(), "algorithmic_bytes_per_launch": b4,
+                "avg_launch_ms": stage_ms["causal_chunked"]}
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(d) bf16 Q/K/V)",
+        "config": {
+            "workload": ("non-causal bf16 B=8 H=16 n=16384 d=64 + causal bf16 B=4 H=32 n=65536 d=128 "
+                         "chunk=128 + one decode step bf16 256 seqs x 32 heads d=128 (state from 1024 "
+                         "prior tokens)"),
+            "tokens_per_step": tokens,
+            "global_batch": {"noncausal": C3.B, "causal": C4.B, "decode": C5.B},
+            "seq_len": {"noncausal": C3.n, "causal": C4.n},
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, one thread)")
+        dec = (dq[:, :, 0], dk[:, :, 0], dv[:, :, 0],
+               S5_init.cpu().numpy().astype(np.float64), Z5_init.cpu().numpy().astype(np.float64))
+        res["cpu_baseline"] = cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

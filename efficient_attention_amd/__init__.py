@@ -11,11 +11,15 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     LinAttnError,
     la_abi_version,
+    la_causal_plan,
+    la_causal_segments,
     la_causal_workspace_bytes,
     la_decode_step,
     la_forward_causal,
     la_forward_noncausal,
     la_noncausal_workspace_bytes,
+    la_state_sums,
+    la_state_sums_workspace_bytes,
     la_status_string,
     load,
 )

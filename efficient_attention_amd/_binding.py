@@ -22,7 +22,8 @@ LA_OK = 0
 # every symbol declared in include/linattn.h
 EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
            "la_forward_noncausal", "la_causal_workspace_bytes", "la_forward_causal",
-           "la_decode_step")
+           "la_causal_plan", "la_state_sums_workspace_bytes", "la_state_sums",
+           "la_causal_segments", "la_decode_step")
 
 _lib = None
 _lock = threading.Lock()
@@ -59,6 +60,14 @@ def load():
         lib.la_causal_workspace_bytes.restype = SZ
         lib.la_forward_causal.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
         lib.la_forward_causal.restype = I
+        lib.la_causal_plan.argtypes = [I64, I64, I64, I64, I64, I, ctypes.POINTER(I64)]
+        lib.la_causal_plan.restype = I
+        lib.la_state_sums_workspace_bytes.argtypes = [I64, I64, I64, I64, I, I64, I64]
+        lib.la_state_sums_workspace_bytes.restype = SZ
+        lib.la_state_sums.argtypes = [P, P, P, I64, I64, I64, I64, I, I64, I64, P, SZ, P]
+        lib.la_state_sums.restype = I
+        lib.la_causal_segments.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I, I64, P]
+        lib.la_causal_segments.restype = I
         lib.la_decode_step.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, P]
         lib.la_decode_step.restype = I
         _lib = lib
@@ -91,8 +100,8 @@ def la_causal_workspace_bytes(B: int, H: int, n: int, d: int, chunk: int, dtype)
     return int(load().la_causal_workspace_bytes(B, H, n, d, chunk, code))
 
 
-# Workspaces are zero-filled once and reused: the kernels leave their counters at zero.
-# One buffer per (device, stream), so calls queued on one stream never share it concurrently.
+# One reusable workspace per (device, stream): calls queued on one stream never use it
+# concurrently, and each call initialises the part it uses.
 _ws_cache: dict = {}
 
 
@@ -102,7 +111,7 @@ def workspace(nbytes: int, device: torch.device, stream_handle: int) -> torch.Te
     key = (device.index, stream_handle)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -191,4 +200,56 @@ def la_decode_step(q, k, v, S, z, out=None, stream=None):
                                out.data_ptr(), B, H, d, _dtype_code(q), sh)
     if st != LA_OK:
         raise LinAttnError(st, "la_decode_step")
+    return out
+
+
+def la_causal_plan(B: int, H: int, n: int, d: int, chunk: int, dtype) -> int:
+    """Segment length la_forward_causal uses for this shape."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    out = ctypes.c_int64(0)
+    st = load().la_causal_plan(B, H, n, d, chunk, code, ctypes.byref(out))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_causal_plan")
+    return int(out.value)
+
+
+def la_state_sums_workspace_bytes(B: int, H: int, n: int, d: int, dtype, seg_len: int, nseg: int) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().la_state_sums_workspace_bytes(B, H, n, d, code, seg_len, nseg))
+
+
+def la_state_sums(k, v, seg_len: int, nseg: int, sums=None, ws=None, stream=None):
+    """Per-segment [S | z] sums of [B, H, n, d] keys/values: returns fp32 [B, H, nseg, d*d + d]."""
+    _check_qkv(k, k, v, 4)
+    B, H, n, d = k.shape
+    code = _dtype_code(k)
+    if sums is None:
+        sums = torch.empty((B, H, nseg, d * d + d), dtype=torch.float32, device=k.device)
+    elif sums.dtype != torch.float32 or tuple(sums.shape) != (B, H, nseg, d * d + d) or not sums.is_contiguous():
+        raise ValueError("sums must be a contiguous float32 tensor of shape %s" % ((B, H, nseg, d * d + d),))
+    sh = _stream_handle(k.device, stream)
+    need = la_state_sums_workspace_bytes(B, H, n, d, code, seg_len, nseg)
+    if ws is None:
+        ws = workspace(need, k.device, sh)
+    st = load().la_state_sums(k.data_ptr(), v.data_ptr(), sums.data_ptr(), B, H, n, d, code, seg_len, nseg,
+                              ws.data_ptr() if ws is not None else None,
+                              ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_state_sums")
+    return sums
+
+
+def la_causal_segments(q, k, v, sums, seg_len: int, chunk: int = 128, out=None, stream=None):
+    """Chunked causal pass where segment s starts from the sum of sums[:, :, :s]."""
+    _check_qkv(q, k, v, 4)
+    out = _out_like(q, out)
+    B, H, n, d = q.shape
+    if sums is not None and (sums.dtype != torch.float32 or not sums.is_contiguous() or sums.device != q.device):
+        raise ValueError("sums must be a contiguous float32 GPU tensor")
+    sh = _stream_handle(q.device, stream)
+    st = load().la_causal_segments(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   sums.data_ptr() if sums is not None else None,
+                                   B, H, n, d, chunk, _dtype_code(q), seg_len, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_causal_segments")
     return out

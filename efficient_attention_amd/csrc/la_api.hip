@@ -44,10 +44,10 @@ int check_shape(int64_t B, int64_t H, int64_t n, int64_t d, int dtype, int64_t* 
 }
 
 // Stage-1 plan: `groups` token ranges of `group_len` tokens, each split over `slices`
-// workgroups of `slice_len` tokens.
+// workgroups of `slice_len` tokens.  Scratch layout: [counters][partials].
 struct StatePlan {
   int64_t groups = 0, slices = 0, slice_len = 0;
-  size_t counters_off = 0, state_off = 0, partials_off = 0, bytes = 0;
+  size_t counters_off = 0, partials_off = 0, scratch_bytes = 0;
 };
 
 StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
@@ -60,41 +60,33 @@ StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
   p.slices = cdiv(group_len, p.slice_len);
   const size_t E = (size_t)(d * d + d) * sizeof(float);
   p.counters_off = 0;
-  p.state_off = round256((size_t)groups * sizeof(unsigned));
-  p.partials_off = p.state_off + round256((size_t)groups * E);
-  p.bytes = p.partials_off + (p.slices > 1 ? (size_t)groups * (size_t)p.slices * E : 0);
+  p.partials_off = round256((size_t)groups * sizeof(unsigned));
+  p.scratch_bytes = p.partials_off + (p.slices > 1 ? (size_t)groups * (size_t)p.slices * E : 0);
   return p;
 }
 
-struct CausalPlan {
-  int64_t segs = 1, seg_len = 0;
-  StatePlan state;
-  size_t bytes = 0;
-};
+// Workspace of the fused forward calls: stage-1 scratch, then the group states.
+size_t state_region_off(const StatePlan& p) { return round256(p.scratch_bytes); }
+size_t forward_ws_bytes(const StatePlan& p, int d) {
+  return state_region_off(p) + (size_t)p.groups * (size_t)(d * d + d) * sizeof(float);
+}
 
-CausalPlan plan_causal(int64_t bh, int64_t n, int64_t chunk, int d, int dtype) {
-  CausalPlan c;
+int64_t causal_seg_len(int64_t bh, int64_t n, int64_t chunk) {
   const int64_t nchunks = cdiv(n, chunk);
   int64_t segs = clamp64(cdiv(kTargetCausalBlocks, bh), 1, kMaxSegments);
   segs = clamp64(segs, 1, nchunks);
-  c.seg_len = cdiv(nchunks, segs) * chunk;
-  c.segs = cdiv(n, c.seg_len);
-  if (c.segs > 1) {
-    c.state = plan_state(bh * (c.segs - 1), c.seg_len, d, dtype);
-    c.bytes = c.state.bytes;
-  }
-  return c;
+  return cdiv(nchunks, segs) * chunk;
 }
 
-la::KvStateArgs state_args(const StatePlan& p, const void* k, const void* v, void* ws, int64_t n,
-                           int64_t group_len, int64_t groups_per_head) {
+la::KvStateArgs state_args(const StatePlan& p, const void* k, const void* v, void* scratch,
+                           float* states, int64_t n, int64_t group_len, int64_t groups_per_head) {
   la::KvStateArgs a;
-  char* base = reinterpret_cast<char*>(ws);
+  char* base = reinterpret_cast<char*>(scratch);
   a.k = k;
   a.v = v;
   a.counters = reinterpret_cast<unsigned*>(base + p.counters_off);
-  a.state = reinterpret_cast<float*>(base + p.state_off);
   a.partials = reinterpret_cast<float*>(base + p.partials_off);
+  a.state = states;
   a.n = n;
   a.group_len = group_len;
   a.groups_per_head = groups_per_head;
@@ -105,6 +97,15 @@ la::KvStateArgs state_args(const StatePlan& p, const void* k, const void* v, voi
 }
 
 bool grid_ok(int64_t blocks) { return blocks > 0 && blocks <= (int64_t)INT_MAX; }
+
+int check_causal(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                 int64_t* bh, size_t* bytes) {
+  int st = check_shape(B, H, n, d, dtype, bh, bytes);
+  if (st != LA_OK) return st;
+  if (chunk != 64 && chunk != 128) return LA_ERR_UNSUPPORTED;
+  if (dtype == LA_DTYPE_F32 && d * chunk > 8192) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
 
 }  // namespace
 
@@ -132,7 +133,7 @@ size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, 
   size_t bytes = 0;
   if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
   if (bh == 0 || n == 0) return 0;
-  return plan_state(bh, n, (int)d, dtype).bytes;
+  return forward_ws_bytes(plan_state(bh, n, (int)d, dtype), (int)d);
 }
 
 int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -146,19 +147,21 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   const StatePlan p = plan_state(bh, n, (int)d, dtype);
-  if (!workspace || workspace_bytes < p.bytes) return LA_ERR_WORKSPACE;
+  const size_t need = forward_ws_bytes(p, (int)d);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LA_ERR_ALIGN;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, p.bytes))
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
     return LA_ERR_ALIAS;
   if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * ((n + 255) / 256))) return LA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  la::KvStateArgs ka = state_args(p, k, v, workspace, n, n, 1);
+  float* states = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + state_region_off(p));
+  la::KvStateArgs ka = state_args(p, k, v, workspace, states, n, n, 1);
   if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
   la::NcOutArgs oa;
   oa.q = q;
   oa.out = out;
-  oa.state = ka.state;
+  oa.state = states;
   oa.n = n;
   oa.bh = bh;
   if (la::launch_nc_out(oa, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
@@ -169,10 +172,94 @@ size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
                                  int dtype) {
   int64_t bh = 0;
   size_t bytes = 0;
-  if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
-  if (chunk != 64 && chunk != 128) return 0;
+  if (check_causal(B, H, n, d, chunk, dtype, &bh, &bytes) != LA_OK) return 0;
   if (bh == 0 || n == 0) return 0;
-  return plan_causal(bh, n, chunk, (int)d, dtype).bytes;
+  const int64_t seg_len = causal_seg_len(bh, n, chunk);
+  const int64_t segs = cdiv(n, seg_len);
+  if (segs == 1) return 0;
+  return forward_ws_bytes(plan_state(bh * (segs - 1), seg_len, (int)d, dtype), (int)d);
+}
+
+int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                   int64_t* seg_len) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_causal(B, H, n, d, chunk, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (!seg_len) return LA_ERR_NULL;
+  *seg_len = (bh == 0 || n == 0) ? chunk : causal_seg_len(bh, n, chunk);
+  return LA_OK;
+}
+
+size_t la_state_sums_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype,
+                                     int64_t seg_len, int64_t nseg) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
+  if (bh == 0 || n == 0 || seg_len < 1 || nseg < 1) return 0;
+  return plan_state(bh * nseg, seg_len, (int)d, dtype).scratch_bytes;
+}
+
+int la_state_sums(const void* k, const void* v, float* sums, int64_t B, int64_t H, int64_t n,
+                  int64_t d, int dtype, int64_t seg_len, int64_t nseg, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_shape(B, H, n, d, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (seg_len < 1 || nseg < 1) return LA_ERR_SHAPE;
+  if (bh == 0 || n == 0) return LA_OK;
+  int64_t last = 0;
+  if (__builtin_mul_overflow(nseg - 1, seg_len, &last) || last >= n) return LA_ERR_SHAPE;
+  if (!k || !v || !sums) return LA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(sums)) return LA_ERR_ALIGN;
+  const StatePlan p = plan_state(bh * nseg, seg_len, (int)d, dtype);
+  if (!workspace || workspace_bytes < p.scratch_bytes) return LA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  const size_t sbytes = (size_t)p.groups * (size_t)(d * d + d) * sizeof(float);
+  if (overlaps(sums, sbytes, k, bytes) || overlaps(sums, sbytes, v, bytes) ||
+      overlaps(sums, sbytes, workspace, p.scratch_bytes))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(p.groups * p.slices)) return LA_ERR_SHAPE;
+  la::KvStateArgs ka = state_args(p, k, v, workspace, sums, n, seg_len, nseg);
+  if (la::launch_kv_state(ka, (int)d, dtype, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return LA_ERR_HIP;
+  return LA_OK;
+}
+
+int la_causal_segments(const void* q, const void* k, const void* v, void* out,
+                       const float* sums, int64_t B, int64_t H, int64_t n, int64_t d,
+                       int64_t chunk, int dtype, int64_t seg_len, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_causal(B, H, n, d, chunk, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (seg_len < chunk || seg_len % chunk != 0) return LA_ERR_SHAPE;
+  if (bh == 0 || n == 0) return LA_OK;
+  const int64_t segs = cdiv(n, seg_len);
+  if (!q || !k || !v || !out || (segs > 1 && !sums)) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (sums && !aligned16(sums)))
+    return LA_ERR_ALIGN;
+  const size_t sbytes = (size_t)bh * (size_t)(segs - 1) * (size_t)(d * d + d) * sizeof(float);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, sums, sbytes))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(bh * segs)) return LA_ERR_SHAPE;
+  la::CausalArgs ca;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.out = out;
+  ca.seg_state = segs > 1 ? sums : nullptr;
+  ca.n = n;
+  ca.bh = bh;
+  ca.segs = segs;
+  ca.seg_len = seg_len;
+  if (la::launch_causal(ca, (int)d, (int)chunk, dtype, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return LA_ERR_HIP;
+  return LA_OK;
 }
 
 int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -180,23 +267,25 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
                       void* workspace, size_t workspace_bytes, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
-  int st = check_shape(B, H, n, d, dtype, &bh, &bytes);
+  int st = check_causal(B, H, n, d, chunk, dtype, &bh, &bytes);
   if (st != LA_OK) return st;
-  if (chunk != 64 && chunk != 128) return LA_ERR_UNSUPPORTED;
-  if (dtype == LA_DTYPE_F32 && d * chunk > 8192) return LA_ERR_UNSUPPORTED;
   if (bh == 0 || n == 0) return LA_OK;
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
-  const CausalPlan p = plan_causal(bh, n, chunk, (int)d, dtype);
-  if (p.bytes > 0) {
-    if (!workspace || workspace_bytes < p.bytes) return LA_ERR_WORKSPACE;
+  const int64_t seg_len = causal_seg_len(bh, n, chunk);
+  const int64_t segs = cdiv(n, seg_len);
+  StatePlan p;
+  size_t need = 0;
+  if (segs > 1) {
+    p = plan_state(bh * (segs - 1), seg_len, (int)d, dtype);
+    need = forward_ws_bytes(p, (int)d);
+    if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return LA_ERR_ALIGN;
   }
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, p.bytes))
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
     return LA_ERR_ALIAS;
-  if (!grid_ok(bh * p.segs)) return LA_ERR_SHAPE;
-  if (p.segs > 1 && !grid_ok(p.state.groups * p.state.slices)) return LA_ERR_SHAPE;
+  if (!grid_ok(bh * segs) || (segs > 1 && !grid_ok(p.groups * p.slices))) return LA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   la::CausalArgs ca;
   ca.q = q;
@@ -206,12 +295,13 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
   ca.seg_state = nullptr;
   ca.n = n;
   ca.bh = bh;
-  ca.segs = p.segs;
-  ca.seg_len = p.seg_len;
-  if (p.segs > 1) {
-    la::KvStateArgs ka = state_args(p.state, k, v, workspace, n, p.seg_len, p.segs - 1);
+  ca.segs = segs;
+  ca.seg_len = seg_len;
+  if (segs > 1) {
+    float* states = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + state_region_off(p));
+    la::KvStateArgs ka = state_args(p, k, v, workspace, states, n, seg_len, segs - 1);
     if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
-    ca.seg_state = ka.state;
+    ca.seg_state = states;
   }
   if (la::launch_causal(ca, (int)d, (int)chunk, dtype, s) != hipSuccess) return LA_ERR_HIP;
   return LA_OK;

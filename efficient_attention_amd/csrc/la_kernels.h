@@ -13,7 +13,7 @@ struct KvStateArgs {
   const void* v;
   float* partials;      // [groups][slices][D*D + D] fp32 (unused when slices == 1)
   float* state;         // [groups][D*D + D] fp32: KV row-major, then z
-  unsigned* counters;   // [groups], zero on entry, left zero on exit
+  unsigned* counters;   // [groups] arrival counters, cleared at the start of each call
   int64_t n;            // tokens per head
   int64_t group_len;    // tokens per group (the last group of a head may be shorter)
   int64_t groups_per_head;

@@ -71,7 +71,6 @@ __device__ void publish_state(const KvStateArgs& a, const GroupRange& gr, const 
     for (int p = 0; p < a.slices; ++p) acc += base[(int64_t)p * E + e];
     dst[e] = acc;
   }
-  if (tid == 0) a.counters[gr.g] = 0u;  // leave the counter zero for the next call
 }
 
 // bf16 stage 1.  Tile = T tokens with T*D = 16384, so each of the 256 threads owns one 8x8
@@ -380,10 +379,25 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   }
 }
 
+// Clears the per-group arrival counters before stage 1.  A workspace is reused across calls
+// of different shapes, so the bytes that serve as counters in this call may hold partial sums
+// of an earlier one; each call therefore zeroes its own counters first (a fill kernel rather
+// than a memset, so the sequence stays valid inside a captured graph).
+__global__ __launch_bounds__(256) void zero_counters(unsigned* c, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) c[i] = 0u;
+}
+
 // ----------------------------------------------------------------------------- launchers
 template <int D>
 static hipError_t launch_kv_state_t(const KvStateArgs& a, int dtype, hipStream_t s) {
   const int64_t blocks = a.groups * a.slices;
+  if (a.slices > 1) {
+    hipLaunchKernelGGL(zero_counters, dim3((unsigned)((a.groups + 255) / 256)), dim3(256), 0, s,
+                       a.counters, a.groups);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (dtype == 1)
     hipLaunchKernelGGL(kv_state_bf16<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else

@@ -74,10 +74,9 @@ size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, 
  *   q, k, v : [B][H][n][d] of `dtype`, read only
  *   out     : [B][H][n][d] of `dtype`, written; must not overlap q, k, v or workspace
  *   workspace, workspace_bytes : device scratch of at least
- *             la_noncausal_workspace_bytes(B, H, n, d, dtype) bytes.  Its counter area
- *             must be zero before the FIRST call that uses it (zero-fill the whole buffer
- *             once); every call leaves it zero again, so it can be reused without clearing.
- *             Two calls that share a workspace must not run concurrently.
+ *             la_noncausal_workspace_bytes(B, H, n, d, dtype) bytes, any contents (each call
+ *             initialises what it uses); it may be reused across calls of any shape, but two
+ *             calls that share a workspace must not run concurrently.
  * Two stages ("Efficient Transformers ...", section "Linear attention": the D x d sum and the
  * key sum are built once and shared by every query): split-n partial sums of
  * [phi(K)^T V | phi(K)^T 1] reduced in a fixed order (deterministic), then one pass over
@@ -98,12 +97,45 @@ size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
  *                  pairwise weights are used directly, earlier tokens enter through the
  *                  running state (S, z) ("The recurrent view"); the result does not depend
  *                  on chunk beyond rounding.
- *   workspace    : at least la_causal_workspace_bytes(...) bytes, same zero-before-first-use
- *                  rule as the non-causal workspace (may be NULL when that size is 0).
+ *   workspace    : at least la_causal_workspace_bytes(...) bytes, same rules as the
+ *                  non-causal workspace (may be NULL when that size is 0).
  */
 int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of la_forward_causal, callable on their own (a caller can time them apart,
+ * or supply segment states computed elsewhere, e.g. on another device that holds the earlier
+ * part of the sequence).  Each head's sequence is cut into segments of `seg_len` tokens
+ * (a positive multiple of chunk); segment s covers tokens [s*seg_len, min(n, (s+1)*seg_len)).
+ *
+ * la_causal_plan: the seg_len la_forward_causal uses for this shape (1 segment when the
+ * batch alone fills the GPU).  Returns LA_OK and writes *seg_len, or an error code.
+ *
+ * la_state_sums: for s < nseg writes sums[b][h][s] = [S | z] (fp32, d*d values of
+ * S = sum phi(k_j) v_j^T row-major, then d values of z = sum phi(k_j)) over the tokens of
+ * segment s ("The recurrent view": the state is a plain sum over tokens, so it splits over
+ * segments).  sums is [B][H][nseg][d*d + d] fp32 and must not overlap k, v or workspace.
+ * Needs la_state_sums_workspace_bytes(...) bytes of workspace (same rules as above).  Requires 1 <= nseg and (nseg-1)*seg_len < n.
+ *
+ * la_causal_segments: the chunked causal pass.  Segment s starts from the state
+ * sum_{s' < s} sums[b][h][s'] (zero for s = 0), so sums must hold ceil(n/seg_len) - 1 entries
+ * per head: [B][H][ceil(n/seg_len) - 1][d*d + d] (may be NULL when that count is 0).
+ */
+int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                   int64_t* seg_len);
+
+size_t la_state_sums_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype,
+                                     int64_t seg_len, int64_t nseg);
+
+int la_state_sums(const void* k, const void* v, float* sums, int64_t B, int64_t H, int64_t n,
+                  int64_t d, int dtype, int64_t seg_len, int64_t nseg, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+int la_causal_segments(const void* q, const void* k, const void* v, void* out,
+                       const float* sums, int64_t B, int64_t H, int64_t n, int64_t d,
+                       int64_t chunk, int dtype, int64_t seg_len, void* stream);
 
 /*
  * One recurrent decode step for B*H independent heads, in place on the state

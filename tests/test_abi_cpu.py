@@ -120,3 +120,36 @@ def test_validation_decode():
     assert _dec(lib, z=0x20004) == -5
     assert _dec(lib, out=0x10000) == -7                      # out aliases S
     assert _dec(lib, z=0x10000 + 64) == -7                   # z inside S
+
+
+def test_causal_plan_and_stage_validation():
+    lib = _lib()
+    assert ea.la_causal_plan(4, 32, 65536, 128, 128, 1) == 32768     # 2 segments per head
+    assert ea.la_causal_plan(64, 8, 4096, 64, 64, 1) == 4096         # batch fills the GPU
+    seg = ea.la_causal_plan(1, 1, 4096, 64, 64, 0)
+    assert seg % 64 == 0 and 64 <= seg < 4096
+    out = ctypes.c_int64(0)
+    assert lib.la_causal_plan(1, 1, 100, 64, 96, 1, ctypes.byref(out)) == -4
+    assert lib.la_causal_plan(1, 1, 100, 64, 64, 1, None) == -1
+    # la_state_sums
+    ss = lambda **kw: lib.la_state_sums(P(kw.get("k", 0x2000)), P(kw.get("v", 0x3000)),
+                                        P(kw.get("sums", 0x80000)), 1, 1, kw.get("n", 1000), 64, 1,
+                                        kw.get("seg_len", 100), kw.get("nseg", 3),
+                                        P(kw.get("ws", 0x900000)), kw.get("wsb", 1 << 30), None)
+    assert ss(nseg=0) == -2
+    assert ss(seg_len=0) == -2
+    assert ss(nseg=11) == -2                                  # segment 10 would start at n
+    assert ss(sums=0) == -1
+    assert ss(sums=0x80004) == -5
+    assert ss(sums=0x2000) == -7
+    assert ss(n=0, k=0) == 0
+    assert ea.la_state_sums_workspace_bytes(1, 1, 1000, 64, 1, 100, 3) > 0
+    # la_causal_segments
+    cs = lambda **kw: lib.la_causal_segments(P(kw.get("q", 0x1000)), P(0x2000), P(0x3000), P(kw.get("out", 0x4000)),
+                                             P(kw.get("sums", 0x80000)), 1, 1, kw.get("n", 1000), 64,
+                                             kw.get("chunk", 64), 1, kw.get("seg_len", 128), None)
+    assert cs(seg_len=100) == -2                              # not a multiple of chunk
+    assert cs(chunk=96) == -4
+    assert cs(sums=0) == -1                                   # several segments need sums
+    assert cs(out=0x80000) == -7                              # out overlaps sums
+    assert cs(n=0, q=0) == 0

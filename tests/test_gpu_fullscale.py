@@ -1,0 +1,126 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The oracle cannot redo a whole 16K/64K-token batch in seconds, so each test checks:
+  * whole heads (sampled) against the oracle's full computation,
+  * single rows (sampled, incl. segment and chunk boundaries and the last row) against the
+    quadratic definition at O(n d) per row,
+  * for decode, every step's output of sampled heads, and the final state of EVERY head
+    against the fp64 sum of all tokens it has seen.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import f64, from_dev, need_gpu, say, to_dev
+from metrics import TOL_BF16, normwise_err
+from seeded_inputs import WORKLOADS, decode_inputs, forward_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ea():
+    need_gpu()
+    import efficient_attention_amd
+    return efficient_attention_amd
+
+
+def _sample_rows(n, extra, rng, count=12):
+    rows = set(int(x) for x in rng.integers(0, n, size=count))
+    rows.update(r for r in extra if 0 <= r < n)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _check_forward(ea, name, form):
+    w = WORKLOADS[name]
+    say(name, "generating inputs", w)
+    q, k, v = forward_inputs(w)
+    tq, tk, tv = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype)
+    say(name, "GPU run")
+    if form == "noncausal":
+        out = ea.la_forward_noncausal(tq, tk, tv)
+    else:
+        out = ea.la_forward_causal(tq, tk, tv, chunk=w.chunk)
+    g = from_dev(out, w.dtype)
+    assert np.all(np.isfinite(g))
+    # whole heads
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    for (b, h) in heads:
+        say(name, "oracle head", b, h)
+        Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
+        ref = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
+        e = normwise_err(g[b, h], ref)
+        print("%s head (%d,%d) normwise err %.3e" % (name, b, h, e))
+        assert e <= TOL_BF16
+    # sampled rows of other heads, by the quadratic definition
+    rng = np.random.default_rng(7)
+    seg_len = ea.la_causal_plan(w.B, w.H, w.n, w.d, w.chunk or 128, tq.dtype) if form == "causal" else w.n
+    extra = [0, 1, w.n - 1, seg_len - 1, seg_len, seg_len + 1, (w.chunk or 64) - 1, w.chunk or 64]
+    for _ in range(6):
+        b, h = int(rng.integers(0, w.B)), int(rng.integers(0, w.H))
+        rows = _sample_rows(w.n, extra, rng)
+        say(name, "oracle rows", b, h, len(rows))
+        Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
+        ref = oracle.rows(Q, K, V, rows, causal=(form == "causal"))
+        e = normwise_err(g[b, h][rows][None], ref[None])
+        assert e <= TOL_BF16, (b, h, e)
+
+
+def test_c3_noncausal_bf16_full(ea):
+    _check_forward(ea, "C3", "noncausal")
+
+
+def test_c4_causal_bf16_full(ea):
+    _check_forward(ea, "C4", "causal")
+
+
+def test_c5_decode_full(ea):
+    import torch
+    w = WORKLOADS["C5"]
+    say("C5 generating inputs")
+    pk, pv, q, k, v = decode_inputs(w)
+    B, H, d, steps = w.B, w.H, w.d, w.n
+    # initial state: the 1024 prior tokens summed by the oracle in fp64, rounded to fp32; the
+    # same fp32 bytes start the GPU and the oracle
+    say("C5 initial state (oracle, fp64 matmul)")
+    S0 = np.empty((B, H, d, d), dtype=np.float32)
+    z0 = np.empty((B, H, d), dtype=np.float32)
+    for b in range(B):
+        S, z = oracle.state_from_tokens_matmul(f64(pk[b], w.dtype), f64(pv[b], w.dtype))
+        S0[b], z0[b] = S, z
+    S = torch.from_numpy(S0).cuda()
+    z = torch.from_numpy(z0).cuda()
+    dq = to_dev(q, w.dtype).permute(2, 0, 1, 3).contiguous()   # [steps, B, H, d]
+    dk = to_dev(k, w.dtype).permute(2, 0, 1, 3).contiguous()
+    dv = to_dev(v, w.dtype).permute(2, 0, 1, 3).contiguous()
+    rng = np.random.default_rng(5)
+    sample = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(14)]
+    sb = torch.tensor([s[0] for s in sample], device="cuda")
+    sh = torch.tensor([s[1] for s in sample], device="cuda")
+    outs = []
+    say("C5 GPU 512 steps")
+    for t in range(steps):
+        o = ea.la_decode_step(dq[t], dk[t], dv[t], S, z)
+        outs.append(o[sb, sh].clone())
+    g = np.stack([from_dev(x, w.dtype) for x in outs], axis=1)     # [sample, steps, d]
+    say("C5 oracle on sampled heads")
+    worst = 0.0
+    for i, (b, h) in enumerate(sample):
+        Sr, zr = S0[b, h].astype(np.float64), z0[b, h].astype(np.float64)
+        Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
+        for t in range(steps):
+            ro, Sr, zr = oracle.decode_step(Q[t], K[t], V[t], Sr, zr)
+            e = normwise_err(g[i, t][None], ro[None], head_axes_last=1)
+            worst = max(worst, e)
+            assert e <= TOL_BF16, (b, h, t, e)
+        assert normwise_err(S[b, h].cpu().numpy(), Sr) <= 1e-4
+    print("C5 worst per-step normwise err on sampled heads %.3e" % worst)
+    # final state of every head vs the fp64 sum over all 1024 + 512 tokens
+    say("C5 final state of every head")
+    Sg, zg = S.cpu().numpy(), z.cpu().numpy()
+    for b in range(B):
+        Sa, za = oracle.state_from_tokens_matmul(f64(k[b], w.dtype), f64(v[b], w.dtype))
+        Sref = S0[b].astype(np.float64) + Sa
+        zref = z0[b].astype(np.float64) + za
+        assert normwise_err(Sg[b], Sref) <= 1e-4
+        assert normwise_err(zg[b], zref, head_axes_last=1) <= 1e-5

@@ -286,3 +286,80 @@ def test_decode_resume_bitwise(ea):
     for a, b in zip(full, first + second):
         assert torch.equal(a, b)
     assert torch.equal(S1, S3) and torch.equal(z1, z3)
+
+
+# ----------------------------------------------------------------------------- causal stages
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_state_sums_vs_oracle(ea, dtype, d):
+    import torch
+    B, H, n, seg_len, nseg = 2, 3, 1000, 300, 4          # last segment ragged (100 tokens)
+    q, k, v = random_inputs(40 + d, (B, H, n, d), dtype, 1.0 / np.sqrt(d))
+    say("state sums", dtype, d)
+    sums = ea.la_state_sums(to_dev(k, dtype), to_dev(v, dtype), seg_len, nseg)
+    torch.cuda.synchronize()
+    g = sums.cpu().numpy().astype(np.float64)
+    K, V = f64(k, dtype), f64(v, dtype)
+    for s in range(nseg):
+        S, z = oracle.state_accumulate(K[:, :, s * seg_len:(s + 1) * seg_len], V[:, :, s * seg_len:(s + 1) * seg_len])
+        ref = np.concatenate([S.reshape(B, H, d * d), z], axis=-1)
+        # bf16 rounds phi(K) once before the MFMA, fp32 does not
+        assert normwise_err(g[:, :, s], ref, head_axes_last=1) <= (4e-3 if dtype == "bf16" else 1e-6)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 128), ("bf16", 64, 64), ("f32", 64, 128)])
+def test_causal_segments_from_oracle_sums(ea, dtype, d, chunk):
+    import torch
+    B, H, n = 1, 2, 5 * chunk + 11
+    seg_len = 2 * chunk                                    # 3 segments, last one ragged
+    q, k, v = random_inputs(50 + d, (B, H, n, d), dtype, 1.0 / np.sqrt(d))
+    Q, K, V = f64(q, dtype), f64(k, dtype), f64(v, dtype)
+    sums = []
+    for s in range(2):
+        S, z = oracle.state_accumulate(K[:, :, s * seg_len:(s + 1) * seg_len], V[:, :, s * seg_len:(s + 1) * seg_len])
+        sums.append(np.concatenate([S.reshape(B, H, d * d), z], axis=-1))
+    sums = torch.from_numpy(np.stack(sums, axis=2).astype(np.float32)).cuda()
+    say("causal segments from oracle sums", dtype, d, chunk)
+    out = ea.la_causal_segments(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), sums, seg_len, chunk)
+    assert normwise_err(from_dev(out, dtype), oracle.causal_recurrent(Q, K, V)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,B,H,n", [("bf16", 128, 128, 2, 4, 3000), ("bf16", 64, 64, 1, 1, 5000),
+                                                 ("f32", 64, 64, 1, 3, 2000)])
+def test_stages_compose_to_forward_causal(ea, dtype, d, chunk, B, H, n):
+    q, k, v = random_inputs(60 + d, (B, H, n, d), dtype, 1.0 / np.sqrt(d))
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    seg_len = ea.la_causal_plan(B, H, n, d, chunk, tq.dtype)
+    nseg = -(-n // seg_len)
+    assert nseg > 1
+    say("stages compose", dtype, d, chunk, B, H, n, seg_len)
+    sums = ea.la_state_sums(tk, tv, seg_len, nseg - 1)
+    a = ea.la_causal_segments(tq, tk, tv, sums, seg_len, chunk)
+    b = ea.la_forward_causal(tq, tk, tv, chunk=chunk)
+    assert np.array_equal(from_dev(a, dtype), from_dev(b, dtype))
+
+
+@pytest.mark.parametrize("fill", [0x00, 0x3F, 0xFF])
+def test_workspace_contents_do_not_matter(ea, fill):
+    # regression: a workspace reused across shapes may hold an earlier call's partial sums
+    # where this call keeps its arrival counters; every call must initialise them itself
+    import torch
+    dtype = "bf16"
+    shapes = [(1, 1, 5000, 64, 64), (2, 4, 3000, 128, 128), (4, 8, 1500, 64, 64)]
+    ref = {}
+    for (B, H, n, d, chunk) in shapes:
+        q, k, v = random_inputs(70 + n, (B, H, n, d), dtype, 1.0 / np.sqrt(d))
+        ref[(B, H, n, d, chunk)] = (q, k, v, oracle_forward("causal", q, k, v, dtype),
+                                    oracle_forward("noncausal", q, k, v, dtype))
+    big = 64 << 20
+    ws = torch.full((big,), fill, dtype=torch.uint8, device="cuda")
+    say("workspace fill", fill)
+    for (B, H, n, d, chunk), (q, k, v, rc, rn) in ref.items():
+        tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+        gc = from_dev(ea.la_forward_causal(tq, tk, tv, chunk=chunk, ws=ws), dtype)
+        gn = from_dev(ea.la_forward_noncausal(tq, tk, tv, ws=ws), dtype)
+        assert normwise_err(gc, rc) <= TOL_BF16
+        assert normwise_err(gn, rn) <= TOL_BF16
+        # and bitwise equal to a run on a fresh workspace
+        gc2 = from_dev(ea.la_forward_causal(tq, tk, tv, chunk=chunk,
+                                            ws=torch.zeros(big, dtype=torch.uint8, device="cuda")), dtype)
+        assert np.array_equal(gc, gc2)
