@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int64_t kTargetStateBlocks = 2048;  // stage-1 workgroups to aim for
+constexpr int64_t kTargetStateBlocks = 512;  // stage-1 workgroups to aim for (2 per CU)
 constexpr int64_t kTargetCausalBlocks = 256;  // one causal workgroup per compute unit
 constexpr int64_t kMaxSegments = 16;
 
@@ -153,7 +153,7 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
       overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
     return LA_ERR_ALIAS;
-  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * ((n + 255) / 256))) return LA_ERR_SHAPE;
+  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * ((n + la::kNcQueries - 1) / la::kNcQueries))) return LA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* states = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + state_region_off(p));
   la::KvStateArgs ka = state_args(p, k, v, workspace, states, n, n, 1);

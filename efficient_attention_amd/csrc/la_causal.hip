@@ -24,7 +24,7 @@ __device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64
   return a.seg_state + (bh * (a.segs - 1) + s) * (int64_t)(D * D + D);
 }
 
-// bf16 kernel, D = head dim, C = chunk.  256 threads = 4 waves.
+// bf16 kernel, D = head dim, C = chunk.  512 threads = 8 waves; waves w and w+4 share SIMD w%4.
 //
 // LDS (bf16 unless noted):  Kn[C][D] phi(K) token-major rows (operand of phi(K) phi(Q)^T),
 // Kt[D][C] and Vt[D][C] feature-major rows (operands whose reduction index is the token),
@@ -32,10 +32,13 @@ __device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64
 // S^T phi(Q)^T), Zr[16][D] a normaliser tile: row 0 = bf16(z), row 1 = bf16(z - row 0),
 // rows 2..15 zero; zf[D] fp32 z.
 //
-// Per wave: query tiles {w, C/16-1-w} (16 rows each; the snake order balances the masked
-// triangle), the state columns c-tiles {w, w+4, ...} in fp32 MFMA accumulators, z for
-// a-tiles {w, w+4, ...}.  Outputs are computed transposed, out^T[c][i] (c = MFMA row, query
-// = MFMA column), so that
+// Work per wave:
+//   * one query tile of 16 rows (C = 128: tile w for w < 4, 11 - w otherwise, so the two waves
+//     of a SIMD hold tiles s and 7 - s and share the masked triangle evenly; C = 64: four
+//     tiles for eight waves, tile w or 7 - w, each wave taking half of the value columns);
+//   * a 2-D block of the fp32 state accumulators: feature tiles NAW*(w%4).., value-column
+//     tiles NCW*(w/4)..; waves 0..3 also keep z for their feature tiles.
+// Outputs are computed transposed, out^T[c][i] (c = MFMA row, query = MFMA column), so that
 //   * phi(Q) needs no LDS: a lane's 16-byte load of its query row is its operand;
 //   * the masked tile is computed as A^T[j][i] = phi(K) phi(Q)^T; in the MFMA result a lane
 //     holds j = 16*jt + 4g + r for its query, so two j-tiles give 8 j values per lane, which
@@ -44,20 +47,21 @@ __device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64
 //   * the normaliser rides along as one extra 16-row output tile: z (hi, lo) rows against
 //     phi(Q) and a row of ones against A give phi(q).z + sum_j A_ij in rows 0 and 1.
 template <int D, int C>
-__global__ __launch_bounds__(256) void causal_bf16(CausalArgs a) {
+__global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
+  constexpr int NT = 512;
   constexpr int LDK = D + 8;
   constexpr int LDC = C + 8;
   constexpr int NI = C / 16;         // query (and key) tiles per chunk
-  constexpr int NIW = NI / 4;        // query tiles per wave
   constexpr int NC = D / 16;         // value-column tiles
-  constexpr int NCW = NC / 4;        // state column tiles per wave
   constexpr int NA = D / 16;         // feature tiles
-  constexpr int NZW = NA / 4;        // z feature tiles per wave
+  constexpr int NAW = NA / 4;        // state feature tiles per wave
+  constexpr int NCW = NC / 2;        // state value-column tiles per wave
+  constexpr int OCT = NI == 8 ? NC : NC / 2;   // output column tiles per wave
   constexpr int KA = D / 32;         // k-steps over features
   constexpr int KJ = C / 32;         // k-steps over tokens
   constexpr int NB = (C / 8) * (D / 8);        // 8x8 blocks per tile
-  constexpr int NKV = (2 * NB + 255) / 256;    // K/V blocks per thread
-  static_assert(NIW >= 1 && NCW >= 1 && NZW >= 1, "shape");
+  constexpr int NKV = (2 * NB + NT - 1) / NT;  // K/V blocks per thread
+  static_assert(NI == 8 || NI == 4, "chunk");
 
   __shared__ __attribute__((aligned(16))) uint16_t Kn[C * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Kt[D * LDC];
@@ -76,39 +80,44 @@ __global__ __launch_bounds__(256) void causal_bf16(CausalArgs a) {
   const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + bh * a.n * D;
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
 
-  // ---- initial state (fp32 accumulators for this wave's columns, z in LDS)
-  f32x4 accS[NA][NCW];
+  const int it = wave < 4 ? wave : (NI == 8 ? 11 - wave : 7 - wave);   // this wave's query tile
+  const int oc0 = (NI == 8 || wave < 4) ? 0 : NC / 2;                 // its first output column tile
+  const int sa0 = NAW * (wave & 3), sc0 = NCW * (wave >> 2);           // its state block
+  const bool zown = wave < 4;                                          // keeps z of tiles sa0..
+
+  // ---- initial state: sum of the leading segments' sums
+  f32x4 accS[NAW][NCW];
 #pragma unroll
-  for (int at = 0; at < NA; ++at)
+  for (int i = 0; i < NAW; ++i)
 #pragma unroll
-    for (int p = 0; p < NCW; ++p) accS[at][p] = zero4();
+    for (int j = 0; j < NCW; ++j) accS[i][j] = zero4();
   float zinit = 0.f;
   for (int64_t s = 0; s < seg; ++s) {
     const float* st = seg_state_ptr(a, bh, s, D);
 #pragma unroll
-    for (int at = 0; at < NA; ++at)
+    for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p)
+      for (int j = 0; j < NCW; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          accS[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
+          accS[i][j][r] += st[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16];
     if (tid < D) zinit += st[D * D + tid];
   }
   if (tid < D) zf[tid] = zinit;
   auto write_state_bf16 = [&]() {
 #pragma unroll
-    for (int at = 0; at < NA; ++at)
+    for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p) {
+      for (int j = 0; j < NCW; ++j) {
         u32x2 w2;
-        w2.x = pack_bf16(accS[at][p][0], accS[at][p][1]);
-        w2.y = pack_bf16(accS[at][p][2], accS[at][p][3]);
-        *reinterpret_cast<u32x2*>(&St[((wave + 4 * p) * 16 + l16) * LDK + at * 16 + g * 4]) = w2;
+        w2.x = pack_bf16(accS[i][j][0], accS[i][j][1]);
+        w2.y = pack_bf16(accS[i][j][2], accS[i][j][3]);
+        *reinterpret_cast<u32x2*>(&St[((sc0 + j) * 16 + l16) * LDK + (sa0 + i) * 16 + g * 4]) = w2;
       }
   };
   write_state_bf16();
   __syncthreads();
-  for (int e = tid; e < 16 * D; e += 256) {
+  for (int e = tid; e < 16 * D; e += NT) {
     const int row = e / D, c = e % D;
     uint16_t val = 0;
     if (row < 2) {
@@ -125,12 +134,11 @@ __global__ __launch_bounds__(256) void causal_bf16(CausalArgs a) {
 
   // ---- chunk loads (issued one chunk ahead)
   u32x4 kvr[NKV][8];
-  u32x4 qr[NIW][KA];
-  auto itile = [&](int p) { return p == 0 ? wave : NI - 1 - wave; };
+  u32x4 qr[KA];
   auto load_chunk = [&](int64_t c0) {
 #pragma unroll
     for (int x = 0; x < NKV; ++x) {
-      const int b = tid + 256 * x;
+      const int b = tid + NT * x;
       if (b < 2 * NB) {
         const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
         const uint16_t* src = b < NB ? K : V;
@@ -141,24 +149,21 @@ __global__ __launch_bounds__(256) void causal_bf16(CausalArgs a) {
         }
       }
     }
+    const int64_t row = c0 + it * 16 + l16;
 #pragma unroll
-    for (int p = 0; p < NIW; ++p) {
-      const int64_t row = c0 + itile(p) * 16 + l16;
-#pragma unroll
-      for (int ks = 0; ks < KA; ++ks) qr[p][ks] = row < t1 ? ld16(Q + row * D + ks * 32 + g * 8) : zero_u4();
-    }
+    for (int ks = 0; ks < KA; ++ks) qr[ks] = row < t1 ? ld16(Q + row * D + ks * 32 + g * 8) : zero_u4();
   };
 
-  float zp[NZW];
+  float zp[NAW];
 #pragma unroll
-  for (int i = 0; i < NZW; ++i) zp[i] = 0.f;
+  for (int i = 0; i < NAW; ++i) zp[i] = 0.f;
 
   if (t0 < t1) load_chunk(t0);
   for (int64_t c0 = t0; c0 < t1; c0 += C) {
     // ---- (a) tiles into LDS: phi(K) natural + transposed, V transposed; phi(Q) in registers
 #pragma unroll
     for (int x = 0; x < NKV; ++x) {
-      const int b = tid + 256 * x;
+      const int b = tid + NT * x;
       if (b < 2 * NB) {
         const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
         u32x4 tr[8];
@@ -179,112 +184,108 @@ __global__ __launch_bounds__(256) void causal_bf16(CausalArgs a) {
         }
       }
     }
-    u32x4 qf[NIW][KA];
+    u32x4 qf[KA];
 #pragma unroll
-    for (int p = 0; p < NIW; ++p)
-#pragma unroll
-      for (int ks = 0; ks < KA; ++ks) qf[p][ks] = phi_bf16x8(qr[p][ks]);
+    for (int ks = 0; ks < KA; ++ks) qf[ks] = phi_bf16x8(qr[ks]);
     __syncthreads();  // tiles, St, Zr ready
     if (c0 + C < t1) load_chunk(c0 + C);
 
-    // ---- (iv) state update in registers: S[:, own cols] += phi(K_c)^T V_c ; z partial sums
+    // ---- (iv) state update in registers: S[own block] += phi(K_c)^T V_c ; z partial sums
 #pragma unroll
     for (int ks = 0; ks < KJ; ++ks) {
       u32x4 bv[NCW];
 #pragma unroll
-      for (int p = 0; p < NCW; ++p) bv[p] = ld16(&Vt[((wave + 4 * p) * 16 + l16) * LDC + ks * 32 + g * 8]);
+      for (int j = 0; j < NCW; ++j) bv[j] = ld16(&Vt[((sc0 + j) * 16 + l16) * LDC + ks * 32 + g * 8]);
 #pragma unroll
-      for (int at = 0; at < NA; ++at) {
-        const u32x4 ak = ld16(&Kt[(at * 16 + l16) * LDC + ks * 32 + g * 8]);
-        if ((at & 3) == wave) zp[at >> 2] += sum_bf16x8(ak);
+      for (int i = 0; i < NAW; ++i) {
+        const u32x4 ak = ld16(&Kt[((sa0 + i) * 16 + l16) * LDC + ks * 32 + g * 8]);
+        if (zown) zp[i] += sum_bf16x8(ak);
 #pragma unroll
-        for (int p = 0; p < NCW; ++p) accS[at][p] = mfma_bf16(ak, bv[p], accS[at][p]);
+        for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_bf16(ak, bv[j], accS[i][j]);
       }
     }
 
-    // ---- per query tile: masked intra-chunk part + inter-chunk part, normalise, store
+    // ---- this wave's query tile: masked intra-chunk part + inter-chunk part, normalise, store
+    f32x4 accA[NI];
 #pragma unroll
-    for (int p = 0; p < NIW; ++p) {
-      const int it = itile(p);
-      f32x4 accA[NI];
+    for (int jt = 0; jt < NI; ++jt) {
+      accA[jt] = zero4();
+      if (jt <= it) {
 #pragma unroll
-      for (int jt = 0; jt < NI; ++jt) {
-        accA[jt] = zero4();
-        if (jt <= it) {
-#pragma unroll
-          for (int ks = 0; ks < KA; ++ks)
-            accA[jt] = mfma_bf16(ld16(&Kn[(jt * 16 + l16) * LDK + ks * 32 + g * 8]), qf[p][ks], accA[jt]);
-        }
-        if (jt == it) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (g * 4 + r > l16) accA[jt][r] = 0.f;
-        }
+        for (int ks = 0; ks < KA; ++ks)
+          accA[jt] = mfma_bf16(ld16(&Kn[(jt * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], accA[jt]);
       }
-      f32x4 acco[NC];
-      f32x4 accd = zero4();
+      if (jt == it) {
 #pragma unroll
-      for (int ct = 0; ct < NC; ++ct) acco[ct] = zero4();
-      // inter-chunk: S^T phi(Q)^T and [z_hi; z_lo] phi(Q)^T
-#pragma unroll
-      for (int ks = 0; ks < KA; ++ks) {
-#pragma unroll
-        for (int ct = 0; ct < NC; ++ct)
-          acco[ct] = mfma_bf16(ld16(&St[(ct * 16 + l16) * LDK + ks * 32 + g * 8]), qf[p][ks], acco[ct]);
-        accd = mfma_bf16(ld16(&Zr[l16 * LDK + ks * 32 + g * 8]), qf[p][ks], accd);
+        for (int r = 0; r < 4; ++r)
+          if (g * 4 + r > l16) accA[jt][r] = 0.f;
       }
-      // intra-chunk: V^T A^T and ones A^T over key tiles 0..it (pairs of 16)
+    }
+    f32x4 acco[OCT];
+    f32x4 accd = zero4();
 #pragma unroll
-      for (int m = 0; m < NI / 2; ++m) {
-        if (2 * m <= it) {
-          u32x4 af;
-          af.x = pack_bf16(accA[2 * m][0], accA[2 * m][1]);
-          af.y = pack_bf16(accA[2 * m][2], accA[2 * m][3]);
-          af.z = pack_bf16(accA[2 * m + 1][0], accA[2 * m + 1][1]);
-          af.w = pack_bf16(accA[2 * m + 1][2], accA[2 * m + 1][3]);
+    for (int ct = 0; ct < OCT; ++ct) acco[ct] = zero4();
+    // inter-chunk: S^T phi(Q)^T and [z_hi; z_lo] phi(Q)^T
 #pragma unroll
-          for (int ct = 0; ct < NC; ++ct) {
-            const uint16_t* vrow = &Vt[(ct * 16 + l16) * LDC + m * 32 + g * 4];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-            u32x4 av;
-            av.x = lo.x;
-            av.y = lo.y;
-            av.z = hi.x;
-            av.w = hi.y;
-            acco[ct] = mfma_bf16(av, af, acco[ct]);
-          }
-          accd = mfma_bf16(ones, af, accd);
+    for (int ks = 0; ks < KA; ++ks) {
+#pragma unroll
+      for (int ct = 0; ct < OCT; ++ct)
+        acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], acco[ct]);
+      accd = mfma_bf16(ld16(&Zr[l16 * LDK + ks * 32 + g * 8]), qf[ks], accd);
+    }
+    // intra-chunk: V^T A^T and ones A^T over key tiles 0..it (pairs of 16)
+#pragma unroll
+    for (int m = 0; m < NI / 2; ++m) {
+      if (2 * m <= it) {
+        u32x4 af;
+        af.x = pack_bf16(accA[2 * m][0], accA[2 * m][1]);
+        af.y = pack_bf16(accA[2 * m][2], accA[2 * m][3]);
+        af.z = pack_bf16(accA[2 * m + 1][0], accA[2 * m + 1][1]);
+        af.w = pack_bf16(accA[2 * m + 1][2], accA[2 * m + 1][3]);
+#pragma unroll
+        for (int ct = 0; ct < OCT; ++ct) {
+          const uint16_t* vrow = &Vt[((oc0 + ct) * 16 + l16) * LDC + m * 32 + g * 4];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+          u32x4 av;
+          av.x = lo.x;
+          av.y = lo.y;
+          av.z = hi.x;
+          av.w = hi.y;
+          acco[ct] = mfma_bf16(av, af, acco[ct]);
         }
+        accd = mfma_bf16(ones, af, accd);
       }
-      const float den = __shfl(accd[0] + accd[1], l16);
-      const float inv = 1.0f / den;
-      const int64_t row = c0 + it * 16 + l16;
-      if (row < t1) {
+    }
+    const float den = __shfl(accd[0] + accd[1], l16);
+    const float inv = 1.0f / den;
+    const int64_t row = c0 + it * 16 + l16;
+    if (row < t1) {
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-          u32x2 o;
-          o.x = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
-          o.y = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
-          *reinterpret_cast<u32x2*>(O + row * D + ct * 16 + g * 4) = o;
-        }
+      for (int ct = 0; ct < OCT; ++ct) {
+        u32x2 o;
+        o.x = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
+        o.y = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
+        *reinterpret_cast<u32x2*>(O + row * D + (oc0 + ct) * 16 + g * 4) = o;
       }
     }
     __syncthreads();  // every wave is done reading this chunk's tiles, St and Zr
 
     // ---- publish the new state for the next chunk
     write_state_bf16();
+    if (zown) {
 #pragma unroll
-    for (int i = 0; i < NZW; ++i) {
-      const int at = wave + 4 * i;
-      const float zs = sum_over_groups(zp[i]);
-      zp[i] = 0.f;
-      if (g == 0) {
-        const float z = zf[at * 16 + l16] + zs;
-        zf[at * 16 + l16] = z;
-        const __bf16 hi = (__bf16)z;
-        Zr[at * 16 + l16] = __builtin_bit_cast(uint16_t, hi);
-        Zr[LDK + at * 16 + l16] = __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
+      for (int i = 0; i < NAW; ++i) {
+        const int at = sa0 + i;
+        const float zs = sum_over_groups(zp[i]);
+        zp[i] = 0.f;
+        if (g == 0) {
+          const float z = zf[at * 16 + l16] + zs;
+          zf[at * 16 + l16] = z;
+          const __bf16 hi = (__bf16)z;
+          Zr[at * 16 + l16] = __builtin_bit_cast(uint16_t, hi);
+          Zr[LDK + at * 16 + l16] = __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
+        }
       }
     }
   }
@@ -432,7 +433,7 @@ template <int D, int C>
 static hipError_t launch_causal_t(const CausalArgs& a, int dtype, hipStream_t s) {
   const unsigned blocks = (unsigned)(a.bh * a.segs);
   if (dtype == 1) {
-    hipLaunchKernelGGL((causal_bf16<D, C>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((causal_bf16<D, C>), dim3(blocks), dim3(512), 0, s, a);
   } else {
     if constexpr (D * C <= 8192)
       hipLaunchKernelGGL((causal_f32<D, C>), dim3(blocks), dim3(256), 0, s, a);

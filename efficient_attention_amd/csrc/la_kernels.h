@@ -57,6 +57,9 @@ hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s);
 hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
 
+// Queries per workgroup of the non-causal output kernel (4 waves x 256).
+constexpr int64_t kNcQueries = 1024;
+
 // Tile sizes the host needs for workspace planning.
 inline int64_t kv_state_tile(int d, int dtype) { return dtype == 1 ? 16384 / d : 64; }
 

@@ -45,16 +45,20 @@ __device__ __forceinline__ GroupRange group_range(const KvStateArgs& a) {
 template <int D>
 __device__ void publish_state(const KvStateArgs& a, const GroupRange& gr, const float* kv_lds,
                               const float* z_lds) {
-  constexpr int E = D * D + D;
+  constexpr int E = D * D + D;       // floats per state; kv_lds and z_lds are adjacent in LDS
+  constexpr int E4 = E / 4;
+  constexpr int NE = (E4 + 255) / 256;
+  static_assert(E % 4 == 0, "state size");
   const int tid = threadIdx.x;
   __shared__ int last_flag;
+  const f32x4* src = reinterpret_cast<const f32x4*>(kv_lds);
   if (a.slices == 1) {
-    float* dst = a.state + gr.g * E;
-    for (int e = tid; e < E; e += 256) dst[e] = e < D * D ? kv_lds[e] : z_lds[e - D * D];
+    f32x4* dst = reinterpret_cast<f32x4*>(a.state + gr.g * E);
+    for (int e = tid; e < E4; e += 256) dst[e] = src[e];
     return;
   }
-  float* part = a.partials + (gr.g * a.slices + gr.s) * E;
-  for (int e = tid; e < E; e += 256) part[e] = e < D * D ? kv_lds[e] : z_lds[e - D * D];
+  f32x4* part = reinterpret_cast<f32x4*>(a.partials + (gr.g * a.slices + gr.s) * E);
+  for (int e = tid; e < E4; e += 256) part[e] = src[e];
   __threadfence();
   __syncthreads();
   if (tid == 0) {
@@ -64,12 +68,31 @@ __device__ void publish_state(const KvStateArgs& a, const GroupRange& gr, const 
   __syncthreads();
   if (!last_flag) return;
   __threadfence();
-  const float* base = a.partials + gr.g * a.slices * E;
-  float* dst = a.state + gr.g * E;
-  for (int e = tid; e < E; e += 256) {
-    float acc = 0.f;
-    for (int p = 0; p < a.slices; ++p) acc += base[(int64_t)p * E + e];
-    dst[e] = acc;
+  // Last arrival: add the slices' partials in slice order.  Elements go in batches of 8
+  // float4 per thread, all 8 loaded for a slice before any is added, so a slice costs one
+  // memory latency per batch while staying below the main loop's register use.
+  const f32x4* base = reinterpret_cast<const f32x4*>(a.partials + gr.g * a.slices * E);
+  f32x4* dst = reinterpret_cast<f32x4*>(a.state + gr.g * E);
+  constexpr int NB = 8;
+  for (int i0 = 0; i0 < NE; i0 += NB) {
+    f32x4 acc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) acc[i] = zero4();
+    for (int64_t p = 0; p < a.slices; ++p) {
+      f32x4 x[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int e = tid + 256 * (i0 + i);
+        x[i] = e < E4 ? base[p * E4 + e] : zero4();
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] += x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int e = tid + 256 * (i0 + i);
+      if (e < E4) dst[e] = acc[i];
+    }
   }
 }
 
@@ -184,8 +207,8 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a) {
   constexpr int NC = D / 16;
   __shared__ __attribute__((aligned(16))) float Kn[T * LD];
   __shared__ __attribute__((aligned(16))) float Vn[T * LD];
-  __shared__ float kv_lds[D * D];
-  __shared__ float z_lds[D];
+  __shared__ __attribute__((aligned(16))) float kv_lds[D * D + D];  // [KV | z]
+  float* z_lds = kv_lds + D * D;
 
   const GroupRange gr = group_range(a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -256,15 +279,15 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
   constexpr int LD = D + 8;
   constexpr int NC = D / 16;
   constexpr int KS = D / 32;
-  constexpr int QPW = 64;  // queries per wave
+  constexpr int QPW = 256;  // queries per wave
   __shared__ __attribute__((aligned(16))) uint16_t KVt[D * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t tiles = (a.n + 255) / 256;
+  const int64_t tiles = (a.n + kNcQueries - 1) / kNcQueries;
   const int64_t bh = blockIdx.x / tiles;
-  const int64_t q0 = (blockIdx.x % tiles) * 256 + wave * QPW;
+  const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * QPW;
   const float* st = a.state + bh * (D * D + D);
 
   for (int e = tid; e < D * D; e += 256) {
@@ -331,15 +354,15 @@ template <int D>
 __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   constexpr int LD = D + 4;
   constexpr int NC = D / 16;
-  constexpr int QPW = 64;
+  constexpr int QPW = 256;
   __shared__ __attribute__((aligned(16))) float KVt[D * LD];
   __shared__ float zs[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t tiles = (a.n + 255) / 256;
+  const int64_t tiles = (a.n + kNcQueries - 1) / kNcQueries;
   const int64_t bh = blockIdx.x / tiles;
-  const int64_t q0 = (blockIdx.x % tiles) * 256 + wave * QPW;
+  const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * QPW;
   const float* st = a.state + bh * (D * D + D);
   for (int e = tid; e < D * D; e += 256) KVt[(e % D) * LD + e / D] = st[e];
   for (int e = tid; e < D; e += 256) zs[e] = st[D * D + e];
@@ -411,7 +434,7 @@ hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s
 
 template <int D>
 static hipError_t launch_nc_out_t(const NcOutArgs& a, int dtype, hipStream_t s) {
-  const int64_t blocks = a.bh * ((a.n + 255) / 256);
+  const int64_t blocks = a.bh * ((a.n + kNcQueries - 1) / kNcQueries);
   if (dtype == 1)
     hipLaunchKernelGGL(nc_out_bf16<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
