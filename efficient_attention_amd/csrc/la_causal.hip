@@ -139,19 +139,16 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
 #pragma unroll
     for (int x = 0; x < NKV; ++x) {
       const int b = tid + NT * x;
-      if (b < 2 * NB) {
+      if ((2 * NB) % NT == 0 || b < 2 * NB) {
         const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
         const uint16_t* src = b < NB ? K : V;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int64_t tok = c0 + tb * 8 + r;
-          kvr[x][r] = tok < t1 ? ld16(src + tok * D + fb * 8) : zero_u4();
-        }
+        for (int r = 0; r < 8; ++r) kvr[x][r] = ld16_clamp(src, c0 + tb * 8 + r, t1, D, fb * 8);
       }
     }
     const int64_t row = c0 + it * 16 + l16;
 #pragma unroll
-    for (int ks = 0; ks < KA; ++ks) qr[ks] = row < t1 ? ld16(Q + row * D + ks * 32 + g * 8) : zero_u4();
+    for (int ks = 0; ks < KA; ++ks) qr[ks] = ld16_clamp(Q, row, t1, D, ks * 32 + g * 8);  // rows >= t1 are never stored
   };
 
   float zp[NAW];
@@ -164,7 +161,7 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
 #pragma unroll
     for (int x = 0; x < NKV; ++x) {
       const int b = tid + NT * x;
-      if (b < 2 * NB) {
+      if ((2 * NB) % NT == 0 || b < 2 * NB) {
         const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
         u32x4 tr[8];
         if (b < NB) {
@@ -178,6 +175,9 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) st16(&Kt[(fb * 8 + e) * LDC + tb * 8], tr[e]);
         } else {
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (c0 + tb * 8 + r >= t1) kvr[x][r] = zero_u4();
           transpose8x8(kvr[x], tr);
 #pragma unroll
           for (int e = 0; e < 8; ++e) st16(&Vt[(fb * 8 + e) * LDC + tb * 8], tr[e]);
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
     u32x4 qf[KA];
 #pragma unroll
     for (int ks = 0; ks < KA; ++ks) qf[ks] = phi_bf16x8(qr[ks]);
+    if (c0 + C < t1) load_chunk(c0 + C);  // next chunk in flight through the whole compute phase
     __syncthreads();  // tiles, St, Zr ready
-    if (c0 + C < t1) load_chunk(c0 + C);
 
     // ---- (iv) state update in registers: S[own block] += phi(K_c)^T V_c ; z partial sums
 #pragma unroll

@@ -109,6 +109,16 @@ __device__ __forceinline__ u32x4 zero_u4() {
 
 // 16-byte global load / store
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Row load without control flow: a row at or beyond `end` reads row end-1 instead (always a
+// valid address); the caller masks such rows where it uses them.  Keeping loads out of
+// branches, and the masking away from the load, lets the compiler leave the load in flight
+// until the data is really needed.
+__device__ __forceinline__ u32x4 ld16_clamp(const uint16_t* base, int64_t row, int64_t end,
+                                            int64_t ld, int col) {
+  const int64_t r = row < end ? row : end - 1;
+  return ld16(base + r * ld + col);
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Wave-level sum over the 4 lanes that share l % 16 (lanes l, l^16, l^32, l^48).

@@ -134,14 +134,8 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
   auto load_tile = [&](int64_t t0) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      int64_t tok = t0 + tb * 8 + r;
-      if (tok < gr.t1) {
-        kr[r] = ld16(K + tok * D + fb * 8);
-        vr[r] = ld16(V + tok * D + fb * 8);
-      } else {
-        kr[r] = zero_u4();
-        vr[r] = zero_u4();
-      }
+      kr[r] = ld16_clamp(K, t0 + tb * 8 + r, gr.t1, D, fb * 8);
+      vr[r] = ld16_clamp(V, t0 + tb * 8 + r, gr.t1, D, fb * 8);
     }
   };
 
@@ -153,6 +147,7 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
     for (int r = 0; r < 8; ++r) {
       bool ok = t0 + tb * 8 + r < gr.t1;
       kr[r] = ok ? phi_bf16x8(kr[r]) : zero_u4();
+      vr[r] = ok ? vr[r] : zero_u4();
     }
     transpose8x8(kr, tk);
     transpose8x8(vr, tv);
@@ -161,8 +156,8 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
       st16(&Kt[(fb * 8 + e) * LDT + tb * 8], tk[e]);
       st16(&Vt[(fb * 8 + e) * LDT + tb * 8], tv[e]);
     }
+    if (t0 + T < gr.t1) load_tile(t0 + T);  // in flight through the MFMA phase
     __syncthreads();
-    if (t0 + T < gr.t1) load_tile(t0 + T);  // in flight during the MFMA phase
 #pragma unroll
     for (int s = 0; s < T / 32; ++s) {
       u32x4 bv[NC];
@@ -314,7 +309,7 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
   u32x4 qr[KS];
   auto load_q = [&](int64_t row) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qr[ks] = row < a.n ? ld16(Q + row * D + ks * 32 + g * 8) : zero_u4();
+    for (int ks = 0; ks < KS; ++ks) qr[ks] = ld16_clamp(Q, row, a.n, D, ks * 32 + g * 8);  // rows >= n are never stored
   };
   load_q(q0 + l16);
   for (int blk = 0; blk < QPW / 16; ++blk) {
