@@ -44,10 +44,11 @@ int check_shape(int64_t B, int64_t H, int64_t n, int64_t d, int dtype, int64_t* 
 }
 
 // Stage-1 plan: `groups` token ranges of `group_len` tokens, each split over `slices`
-// workgroups of `slice_len` tokens.  Scratch layout: [counters][partials].
+// workgroups of `slice_len` tokens.  With several slices the kernel writes per-slice partials
+// (scratch of groups * slices states) that state_reduce, or the causal kernel, adds up.
 struct StatePlan {
   int64_t groups = 0, slices = 0, slice_len = 0;
-  size_t counters_off = 0, partials_off = 0, scratch_bytes = 0;
+  size_t scratch_bytes = 0;
 };
 
 StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
@@ -59,16 +60,19 @@ StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
   p.slice_len = cdiv(tiles, slices) * tile;
   p.slices = cdiv(group_len, p.slice_len);
   const size_t E = (size_t)(d * d + d) * sizeof(float);
-  p.counters_off = 0;
-  p.partials_off = round256((size_t)groups * sizeof(unsigned));
-  p.scratch_bytes = p.partials_off + (p.slices > 1 ? (size_t)groups * (size_t)p.slices * E : 0);
+  p.scratch_bytes = p.slices > 1 ? (size_t)groups * (size_t)p.slices * E : 0;
   return p;
 }
 
-// Workspace of the fused forward calls: stage-1 scratch, then the group states.
-size_t state_region_off(const StatePlan& p) { return round256(p.scratch_bytes); }
-size_t forward_ws_bytes(const StatePlan& p, int d) {
-  return state_region_off(p) + (size_t)p.groups * (size_t)(d * d + d) * sizeof(float);
+size_t state_bytes(int64_t groups, int d) { return (size_t)groups * (size_t)(d * d + d) * sizeof(float); }
+
+// Non-causal workspace: [partials][states].
+size_t nc_state_off(const StatePlan& p) { return round256(p.scratch_bytes); }
+size_t nc_ws_bytes(const StatePlan& p, int d) { return nc_state_off(p) + state_bytes(p.groups, d); }
+
+// Causal workspace: the leading segments' partials (or their sums when one slice each).
+size_t causal_ws_bytes(const StatePlan& p, int d) {
+  return p.slices > 1 ? p.scratch_bytes : state_bytes(p.groups, d);
 }
 
 int64_t causal_seg_len(int64_t bh, int64_t n, int64_t chunk) {
@@ -78,14 +82,12 @@ int64_t causal_seg_len(int64_t bh, int64_t n, int64_t chunk) {
   return cdiv(nchunks, segs) * chunk;
 }
 
-la::KvStateArgs state_args(const StatePlan& p, const void* k, const void* v, void* scratch,
+la::KvStateArgs state_args(const StatePlan& p, const void* k, const void* v, float* partials,
                            float* states, int64_t n, int64_t group_len, int64_t groups_per_head) {
   la::KvStateArgs a;
-  char* base = reinterpret_cast<char*>(scratch);
   a.k = k;
   a.v = v;
-  a.counters = reinterpret_cast<unsigned*>(base + p.counters_off);
-  a.partials = reinterpret_cast<float*>(base + p.partials_off);
+  a.partials = partials;
   a.state = states;
   a.n = n;
   a.group_len = group_len;
@@ -133,7 +135,7 @@ size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, 
   size_t bytes = 0;
   if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
   if (bh == 0 || n == 0) return 0;
-  return forward_ws_bytes(plan_state(bh, n, (int)d, dtype), (int)d);
+  return nc_ws_bytes(plan_state(bh, n, (int)d, dtype), (int)d);
 }
 
 int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -147,17 +149,20 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   const StatePlan p = plan_state(bh, n, (int)d, dtype);
-  const size_t need = forward_ws_bytes(p, (int)d);
+  const size_t need = nc_ws_bytes(p, (int)d);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LA_ERR_ALIGN;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
       overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
     return LA_ERR_ALIAS;
-  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * ((n + la::kNcQueries - 1) / la::kNcQueries))) return LA_ERR_SHAPE;
+  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * ((n + la::kNcQueries - 1) / la::kNcQueries)))
+    return LA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  float* states = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + state_region_off(p));
-  la::KvStateArgs ka = state_args(p, k, v, workspace, states, n, n, 1);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* states = reinterpret_cast<float*>(ws + nc_state_off(p));
+  la::KvStateArgs ka = state_args(p, k, v, reinterpret_cast<float*>(ws), states, n, n, 1);
   if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  if (p.slices > 1 && la::launch_state_reduce(ka, (int)d, s) != hipSuccess) return LA_ERR_HIP;
   la::NcOutArgs oa;
   oa.q = q;
   oa.out = out;
@@ -177,7 +182,7 @@ size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
   const int64_t seg_len = causal_seg_len(bh, n, chunk);
   const int64_t segs = cdiv(n, seg_len);
   if (segs == 1) return 0;
-  return forward_ws_bytes(plan_state(bh * (segs - 1), seg_len, (int)d, dtype), (int)d);
+  return causal_ws_bytes(plan_state(bh * (segs - 1), seg_len, (int)d, dtype), (int)d);
 }
 
 int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
@@ -214,16 +219,19 @@ int la_state_sums(const void* k, const void* v, float* sums, int64_t B, int64_t 
   if (!k || !v || !sums) return LA_ERR_NULL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(sums)) return LA_ERR_ALIGN;
   const StatePlan p = plan_state(bh * nseg, seg_len, (int)d, dtype);
-  if (!workspace || workspace_bytes < p.scratch_bytes) return LA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return LA_ERR_ALIGN;
-  const size_t sbytes = (size_t)p.groups * (size_t)(d * d + d) * sizeof(float);
+  if (p.scratch_bytes > 0) {
+    if (!workspace || workspace_bytes < p.scratch_bytes) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  }
+  const size_t sbytes = state_bytes(p.groups, (int)d);
   if (overlaps(sums, sbytes, k, bytes) || overlaps(sums, sbytes, v, bytes) ||
       overlaps(sums, sbytes, workspace, p.scratch_bytes))
     return LA_ERR_ALIAS;
   if (!grid_ok(p.groups * p.slices)) return LA_ERR_SHAPE;
-  la::KvStateArgs ka = state_args(p, k, v, workspace, sums, n, seg_len, nseg);
-  if (la::launch_kv_state(ka, (int)d, dtype, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return LA_ERR_HIP;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  la::KvStateArgs ka = state_args(p, k, v, reinterpret_cast<float*>(workspace), sums, n, seg_len, nseg);
+  if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  if (p.slices > 1 && la::launch_state_reduce(ka, (int)d, s) != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
 }
 
@@ -252,6 +260,7 @@ int la_causal_segments(const void* q, const void* k, const void* v, void* out,
   ca.v = v;
   ca.out = out;
   ca.seg_state = segs > 1 ? sums : nullptr;
+  ca.seg_parts = 1;
   ca.n = n;
   ca.bh = bh;
   ca.segs = segs;
@@ -278,7 +287,7 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
   size_t need = 0;
   if (segs > 1) {
     p = plan_state(bh * (segs - 1), seg_len, (int)d, dtype);
-    need = forward_ws_bytes(p, (int)d);
+    need = causal_ws_bytes(p, (int)d);
     if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return LA_ERR_ALIGN;
   }
@@ -293,15 +302,18 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
   ca.v = v;
   ca.out = out;
   ca.seg_state = nullptr;
+  ca.seg_parts = 1;
   ca.n = n;
   ca.bh = bh;
   ca.segs = segs;
   ca.seg_len = seg_len;
   if (segs > 1) {
-    float* states = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + state_region_off(p));
-    la::KvStateArgs ka = state_args(p, k, v, workspace, states, n, seg_len, segs - 1);
+    // the chunked kernel adds the leading segments' slice partials itself
+    float* parts = reinterpret_cast<float*>(workspace);
+    la::KvStateArgs ka = state_args(p, k, v, parts, parts, n, seg_len, segs - 1);
     if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
-    ca.seg_state = states;
+    ca.seg_state = parts;
+    ca.seg_parts = p.slices;
   }
   if (la::launch_causal(ca, (int)d, (int)chunk, dtype, s) != hipSuccess) return LA_ERR_HIP;
   return LA_OK;

@@ -18,10 +18,11 @@
 
 namespace la {
 
-// Initial (S, z) of a segment: sum over the leading segments, in segment order.
-__device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64_t bh, int64_t s,
+// Initial (S, z) of a segment: the sum over the leading segments' parts, in order
+// (segment s', part p) -> index (s' * seg_parts + p).
+__device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64_t bh, int64_t sp,
                                                       int D) {
-  return a.seg_state + (bh * (a.segs - 1) + s) * (int64_t)(D * D + D);
+  return a.seg_state + (bh * (a.segs - 1) * a.seg_parts + sp) * (int64_t)(D * D + D);
 }
 
 // bf16 kernel, D = head dim, C = chunk.  512 threads = 8 waves; waves w and w+4 share SIMD w%4.
@@ -92,16 +93,31 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
 #pragma unroll
     for (int j = 0; j < NCW; ++j) accS[i][j] = zero4();
   float zinit = 0.f;
+  // per leading segment: add its parts in order, then add the segment (the same grouping as
+  // la_state_sums followed by la_causal_segments, so both paths round identically)
   for (int64_t s = 0; s < seg; ++s) {
-    const float* st = seg_state_ptr(a, bh, s, D);
+    f32x4 part[NAW][NCW];
+    float zpart = 0.f;
 #pragma unroll
     for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int j = 0; j < NCW; ++j)
+      for (int j = 0; j < NCW; ++j) part[i][j] = zero4();
+    for (int64_t p = 0; p < a.seg_parts; ++p) {
+      const float* st = seg_state_ptr(a, bh, s * a.seg_parts + p, D);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          accS[i][j][r] += st[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16];
-    if (tid < D) zinit += st[D * D + tid];
+      for (int i = 0; i < NAW; ++i)
+#pragma unroll
+        for (int j = 0; j < NCW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            part[i][j][r] += st[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16];
+      if (tid < D) zpart += st[D * D + tid];
+    }
+#pragma unroll
+    for (int i = 0; i < NAW; ++i)
+#pragma unroll
+      for (int j = 0; j < NCW; ++j) accS[i][j] += part[i][j];
+    zinit += zpart;
   }
   if (tid < D) zf[tid] = zinit;
   auto write_state_bf16 = [&]() {
@@ -323,16 +339,29 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a) {
 #pragma unroll
     for (int p = 0; p < NCW; ++p) accS[at][p] = zero4();
   float zinit = 0.f;
-  for (int64_t s = 0; s < seg; ++s) {
-    const float* st = seg_state_ptr(a, bh, s, D);
+  for (int64_t s = 0; s < seg; ++s) {      // same grouping as in the bf16 kernel
+    f32x4 part[NA][NCW];
+    float zpart = 0.f;
 #pragma unroll
     for (int at = 0; at < NA; ++at)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p)
+      for (int p = 0; p < NCW; ++p) part[at][p] = zero4();
+    for (int64_t q = 0; q < a.seg_parts; ++q) {
+      const float* st = seg_state_ptr(a, bh, s * a.seg_parts + q, D);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          accS[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
-    if (tid < D) zinit += st[D * D + tid];
+      for (int at = 0; at < NA; ++at)
+#pragma unroll
+        for (int p = 0; p < NCW; ++p)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            part[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
+      if (tid < D) zpart += st[D * D + tid];
+    }
+#pragma unroll
+    for (int at = 0; at < NA; ++at)
+#pragma unroll
+      for (int p = 0; p < NCW; ++p) accS[at][p] += part[at][p];
+    zinit += zpart;
   }
   if (tid < D) zf[tid] = zinit;
 

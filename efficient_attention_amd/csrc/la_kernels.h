@@ -13,7 +13,6 @@ struct KvStateArgs {
   const void* v;
   float* partials;      // [groups][slices][D*D + D] fp32 (unused when slices == 1)
   float* state;         // [groups][D*D + D] fp32: KV row-major, then z
-  unsigned* counters;   // [groups] arrival counters, cleared at the start of each call
   int64_t n;            // tokens per head
   int64_t group_len;    // tokens per group (the last group of a head may be shorter)
   int64_t groups_per_head;
@@ -35,7 +34,9 @@ struct CausalArgs {
   const void* k;
   const void* v;
   void* out;
-  const float* seg_state;  // [bh][segs-1][D*D + D]: sums over each leading segment (or null)
+  const float* seg_state;  // [bh][segs-1][seg_parts][D*D + D]: the leading segments' sums,
+                           // each split into seg_parts partials that add up to it (or null)
+  int64_t seg_parts;
   int64_t n;
   int64_t bh;
   int64_t segs;            // segments per head
@@ -53,12 +54,13 @@ struct DecodeArgs {
 };
 
 hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s);
+hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s);
 hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s);
 hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
 
-// Queries per workgroup of the non-causal output kernel (4 waves x 256).
-constexpr int64_t kNcQueries = 1024;
+// Queries per workgroup of the non-causal output kernel (4 waves x 128).
+constexpr int64_t kNcQueries = 512;
 
 // Tile sizes the host needs for workspace planning.
 inline int64_t kv_state_tile(int d, int dtype) { return dtype == 1 ? 16384 / d : 64; }

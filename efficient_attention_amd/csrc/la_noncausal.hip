@@ -39,61 +39,35 @@ __device__ __forceinline__ GroupRange group_range(const KvStateArgs& a) {
   return r;
 }
 
-// Write this workgroup's [KV | z] (or its partial) and, if it is the last of its group to
-// finish, add every slice's partial in slice order into state[group].  `kv` and `zq` live in
-// LDS as fp32 [D][D] and [D].
+// Write this workgroup's [KV | z] (fp32, adjacent in LDS) to its slot: the group state
+// when the group has one slice, otherwise the slice's partial, which state_reduce (or the
+// causal kernel's prologue) adds up after this kernel has finished.  There is no cross-
+// workgroup synchronisation inside the kernel: the kernel boundary orders the two steps.
 template <int D>
-__device__ void publish_state(const KvStateArgs& a, const GroupRange& gr, const float* kv_lds,
-                              const float* z_lds) {
-  constexpr int E = D * D + D;       // floats per state; kv_lds and z_lds are adjacent in LDS
+__device__ void publish_state(const KvStateArgs& a, const GroupRange& gr, const float* kv_lds) {
+  constexpr int E = D * D + D;
   constexpr int E4 = E / 4;
-  constexpr int NE = (E4 + 255) / 256;
   static_assert(E % 4 == 0, "state size");
-  const int tid = threadIdx.x;
-  __shared__ int last_flag;
   const f32x4* src = reinterpret_cast<const f32x4*>(kv_lds);
-  if (a.slices == 1) {
-    f32x4* dst = reinterpret_cast<f32x4*>(a.state + gr.g * E);
-    for (int e = tid; e < E4; e += 256) dst[e] = src[e];
-    return;
-  }
-  f32x4* part = reinterpret_cast<f32x4*>(a.partials + (gr.g * a.slices + gr.s) * E);
-  for (int e = tid; e < E4; e += 256) part[e] = src[e];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    unsigned prev = atomicAdd(a.counters + gr.g, 1u);
-    last_flag = (prev == (unsigned)(a.slices - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  // Last arrival: add the slices' partials in slice order.  Elements go in batches of 8
-  // float4 per thread, all 8 loaded for a slice before any is added, so a slice costs one
-  // memory latency per batch while staying below the main loop's register use.
-  const f32x4* base = reinterpret_cast<const f32x4*>(a.partials + gr.g * a.slices * E);
-  f32x4* dst = reinterpret_cast<f32x4*>(a.state + gr.g * E);
-  constexpr int NB = 8;
-  for (int i0 = 0; i0 < NE; i0 += NB) {
-    f32x4 acc[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) acc[i] = zero4();
-    for (int64_t p = 0; p < a.slices; ++p) {
-      f32x4 x[NB];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int e = tid + 256 * (i0 + i);
-        x[i] = e < E4 ? base[p * E4 + e] : zero4();
-      }
-#pragma unroll
-      for (int i = 0; i < NB; ++i) acc[i] += x[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int e = tid + 256 * (i0 + i);
-      if (e < E4) dst[e] = acc[i];
-    }
-  }
+  f32x4* dst = reinterpret_cast<f32x4*>(a.slices == 1 ? a.state + gr.g * E
+                                                       : a.partials + (gr.g * a.slices + gr.s) * E);
+  for (int e = threadIdx.x; e < E4; e += 256) dst[e] = src[e];
+}
+
+// Adds the slices' partials of every group in slice order (deterministic).  Grid: groups x
+// ceil(E/4/256) workgroups of 256 threads, one float4 of the state per thread.
+template <int D>
+__global__ __launch_bounds__(256) void state_reduce(KvStateArgs a) {
+  constexpr int E = D * D + D;
+  constexpr int E4 = E / 4;
+  constexpr int BPG = (E4 + 255) / 256;
+  const int64_t g = blockIdx.x / BPG;
+  const int e = (int)(blockIdx.x % BPG) * 256 + threadIdx.x;
+  if (e >= E4) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.partials + g * a.slices * E) + e;
+  f32x4 acc = zero4();
+  for (int64_t p = 0; p < a.slices; ++p) acc += src[p * E4];
+  reinterpret_cast<f32x4*>(a.state + g * E)[e] = acc;
 }
 
 // bf16 stage 1.  Tile = T tokens with T*D = 16384, so each of the 256 threads owns one 8x8
@@ -189,7 +163,7 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
     if (g == 0) z_lds[at * 16 + l16] = zs;
   }
   __syncthreads();
-  publish_state<D>(a, gr, kv_lds, z_lds);
+  publish_state<D>(a, gr, kv_lds);
 }
 
 // fp32 stage 1: tile of 64 tokens kept in natural layout (the fp32 MFMA takes one k value
@@ -260,7 +234,7 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a) {
     if (g == 0) z_lds[at * 16 + l16] = zs;
   }
   __syncthreads();
-  publish_state<D>(a, gr, kv_lds, z_lds);
+  publish_state<D>(a, gr, kv_lds);
 }
 
 // ----------------------------------------------------------------------------- stage 2
@@ -274,7 +248,7 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
   constexpr int LD = D + 8;
   constexpr int NC = D / 16;
   constexpr int KS = D / 32;
-  constexpr int QPW = 256;  // queries per wave
+  constexpr int QPW = kNcQueries / 4;  // queries per wave
   __shared__ __attribute__((aligned(16))) uint16_t KVt[D * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LD];
 
@@ -306,37 +280,49 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
 
-  u32x4 qr[KS];
-  auto load_q = [&](int64_t row) {
+  // query blocks of 16 rows go in batches of BB, the next batch in flight during compute
+  constexpr int BB = D == 64 ? 4 : 2;
+  constexpr int NBATCH = QPW / 16 / BB;
+  u32x4 qr[BB][KS];
+  auto load_batch = [&](int64_t r0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qr[ks] = ld16_clamp(Q, row, a.n, D, ks * 32 + g * 8);  // rows >= n are never stored
+    for (int b = 0; b < BB; ++b)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qr[b][ks] = ld16_clamp(Q, r0 + b * 16 + l16, a.n, D, ks * 32 + g * 8);  // rows >= n are never stored
   };
-  load_q(q0 + l16);
-  for (int blk = 0; blk < QPW / 16; ++blk) {
-    const int64_t row = q0 + blk * 16 + l16;
-    u32x4 qf[KS];
+  load_batch(q0);
+  for (int bt = 0; bt < NBATCH; ++bt) {
+    u32x4 qf[BB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = phi_bf16x8(qr[ks]);
-    if (blk + 1 < QPW / 16) load_q(row + 16);
-    f32x4 acc[NC];
-    f32x4 accd = zero4();
+    for (int b = 0; b < BB; ++b)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = zero4();
+      for (int ks = 0; ks < KS; ++ks) qf[b][ks] = phi_bf16x8(qr[b][ks]);
+    if (bt + 1 < NBATCH) load_batch(q0 + (bt + 1) * 16 * BB);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int b = 0; b < BB; ++b) {
+      const int64_t row = q0 + (bt * BB + b) * 16 + l16;
+      f32x4 acc[NC];
+      f32x4 accd = zero4();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = mfma_bf16(ld16(&KVt[(c * 16 + l16) * LD + ks * 32 + g * 8]), qf[ks], acc[c]);
-      accd = mfma_bf16(ld16(&Zr[l16 * LD + ks * 32 + g * 8]), qf[ks], accd);
-    }
-    float den = __shfl(accd[0] + accd[1], l16);
-    float inv = 1.0f / den;
-    if (row < a.n) {
+      for (int c = 0; c < NC; ++c) acc[c] = zero4();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        u32x2 o;
-        o.x = pack_bf16(acc[c][0] * inv, acc[c][1] * inv);
-        o.y = pack_bf16(acc[c][2] * inv, acc[c][3] * inv);
-        *reinterpret_cast<u32x2*>(O + row * D + c * 16 + g * 4) = o;
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc[c] = mfma_bf16(ld16(&KVt[(c * 16 + l16) * LD + ks * 32 + g * 8]), qf[b][ks], acc[c]);
+        accd = mfma_bf16(ld16(&Zr[l16 * LD + ks * 32 + g * 8]), qf[b][ks], accd);
+      }
+      const float den = __shfl(accd[0] + accd[1], l16);
+      const float inv = 1.0f / den;
+      if (row < a.n) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          u32x2 o;
+          o.x = pack_bf16(acc[c][0] * inv, acc[c][1] * inv);
+          o.y = pack_bf16(acc[c][2] * inv, acc[c][3] * inv);
+          *reinterpret_cast<u32x2*>(O + row * D + c * 16 + g * 4) = o;
+        }
       }
     }
   }
@@ -349,7 +335,7 @@ template <int D>
 __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   constexpr int LD = D + 4;
   constexpr int NC = D / 16;
-  constexpr int QPW = 256;
+  constexpr int QPW = kNcQueries / 4;
   __shared__ __attribute__((aligned(16))) float KVt[D * LD];
   __shared__ float zs[D];
 
@@ -397,25 +383,10 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   }
 }
 
-// Clears the per-group arrival counters before stage 1.  A workspace is reused across calls
-// of different shapes, so the bytes that serve as counters in this call may hold partial sums
-// of an earlier one; each call therefore zeroes its own counters first (a fill kernel rather
-// than a memset, so the sequence stays valid inside a captured graph).
-__global__ __launch_bounds__(256) void zero_counters(unsigned* c, int64_t count) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < count) c[i] = 0u;
-}
-
 // ----------------------------------------------------------------------------- launchers
 template <int D>
 static hipError_t launch_kv_state_t(const KvStateArgs& a, int dtype, hipStream_t s) {
   const int64_t blocks = a.groups * a.slices;
-  if (a.slices > 1) {
-    hipLaunchKernelGGL(zero_counters, dim3((unsigned)((a.groups + 255) / 256)), dim3(256), 0, s,
-                       a.counters, a.groups);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (dtype == 1)
     hipLaunchKernelGGL(kv_state_bf16<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
@@ -425,6 +396,17 @@ static hipError_t launch_kv_state_t(const KvStateArgs& a, int dtype, hipStream_t
 
 hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s) {
   return d == 64 ? launch_kv_state_t<64>(a, dtype, s) : launch_kv_state_t<128>(a, dtype, s);
+}
+
+template <int D>
+static hipError_t launch_state_reduce_t(const KvStateArgs& a, hipStream_t s) {
+  constexpr int64_t BPG = ((D * D + D) / 4 + 255) / 256;
+  hipLaunchKernelGGL(state_reduce<D>, dim3((unsigned)(a.groups * BPG)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s) {
+  return d == 64 ? launch_state_reduce_t<64>(a, s) : launch_state_reduce_t<128>(a, s);
 }
 
 template <int D>

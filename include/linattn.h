@@ -117,7 +117,8 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
  * S = sum phi(k_j) v_j^T row-major, then d values of z = sum phi(k_j)) over the tokens of
  * segment s ("The recurrent view": the state is a plain sum over tokens, so it splits over
  * segments).  sums is [B][H][nseg][d*d + d] fp32 and must not overlap k, v or workspace.
- * Needs la_state_sums_workspace_bytes(...) bytes of workspace (same rules as above).  Requires 1 <= nseg and (nseg-1)*seg_len < n.
+ * Needs la_state_sums_workspace_bytes(...) bytes of workspace (same rules as above; when
+ * that size is 0 the workspace may be NULL).  Requires 1 <= nseg and (nseg-1)*seg_len < n.
  *
  * la_causal_segments: the chunked causal pass.  Segment s starts from the state
  * sum_{s' < s} sums[b][h][s'] (zero for s = 0), so sums must hold ceil(n/seg_len) - 1 entries
