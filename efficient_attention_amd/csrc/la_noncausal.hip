@@ -259,21 +259,26 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
   const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * QPW;
   const float* st = a.state + bh * (D * D + D);
 
-  for (int e = tid; e < D * D; e += 256) {
-    int ar = e / D, c = e % D;
-    float x = st[e];
-    KVt[c * LD + ar] = __builtin_bit_cast(uint16_t, (__bf16)x);
+  // the head's fp32 state: every load issued before any is used (one memory latency)
+  constexpr int NKV4 = D * D / 4 / 256;
+  f32x4 kv4[NKV4];
+#pragma unroll
+  for (int i = 0; i < NKV4; ++i) kv4[i] = reinterpret_cast<const f32x4*>(st)[tid + 256 * i];
+  const float zv = tid < D ? st[D * D + tid] : 0.f;
+#pragma unroll
+  for (int i = 0; i < NKV4; ++i) {
+    const int e = (tid + 256 * i) * 4, ar = e / D, c = e % D;
+    KVt[(c + 0) * LD + ar] = __builtin_bit_cast(uint16_t, (__bf16)kv4[i].x);
+    KVt[(c + 1) * LD + ar] = __builtin_bit_cast(uint16_t, (__bf16)kv4[i].y);
+    KVt[(c + 2) * LD + ar] = __builtin_bit_cast(uint16_t, (__bf16)kv4[i].z);
+    KVt[(c + 3) * LD + ar] = __builtin_bit_cast(uint16_t, (__bf16)kv4[i].w);
   }
-  for (int e = tid; e < 16 * D; e += 256) {
-    int row = e / D, c = e % D;
-    uint16_t val = 0;
-    if (row < 2) {
-      float z = st[D * D + c];
-      __bf16 hi = (__bf16)z;
-      val = row == 0 ? __builtin_bit_cast(uint16_t, hi)
-                     : __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
-    }
-    Zr[row * LD + c] = val;
+  for (int e = tid; e < 16 * D; e += 256) Zr[e / D * LD + e % D] = 0;
+  __syncthreads();
+  if (tid < D) {
+    const __bf16 hi = (__bf16)zv;
+    Zr[tid] = __builtin_bit_cast(uint16_t, hi);
+    Zr[LD + tid] = __builtin_bit_cast(uint16_t, (__bf16)(zv - (float)hi));
   }
   __syncthreads();
 
@@ -345,8 +350,19 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   const int64_t bh = blockIdx.x / tiles;
   const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * QPW;
   const float* st = a.state + bh * (D * D + D);
-  for (int e = tid; e < D * D; e += 256) KVt[(e % D) * LD + e / D] = st[e];
-  for (int e = tid; e < D; e += 256) zs[e] = st[D * D + e];
+  constexpr int NKV4 = D * D / 4 / 256;
+  f32x4 kv4[NKV4];
+#pragma unroll
+  for (int i = 0; i < NKV4; ++i) kv4[i] = reinterpret_cast<const f32x4*>(st)[tid + 256 * i];
+#pragma unroll
+  for (int i = 0; i < NKV4; ++i) {
+    const int e = (tid + 256 * i) * 4, ar = e / D, c = e % D;
+    KVt[(c + 0) * LD + ar] = kv4[i].x;
+    KVt[(c + 1) * LD + ar] = kv4[i].y;
+    KVt[(c + 2) * LD + ar] = kv4[i].z;
+    KVt[(c + 3) * LD + ar] = kv4[i].w;
+  }
+  if (tid < D) zs[tid] = st[D * D + tid];
   __syncthreads();
 
   const float* Q = reinterpret_cast<const float*>(a.q) + bh * a.n * D;
