@@ -50,8 +50,7 @@ __device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64
 template <int D, int C>
 __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
   constexpr int NT = 512;
-  constexpr int LDK = D + 8;
-  constexpr int LDC = C + 8;
+  constexpr int LDK = D + 16;       // row stride of 8 mod 64 dwords: conflict-free 16-row reads
   constexpr int NI = C / 16;         // query (and key) tiles per chunk
   constexpr int NC = D / 16;         // value-column tiles
   constexpr int NA = D / 16;         // feature tiles
@@ -65,8 +64,8 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
   static_assert(NI == 8 || NI == 4, "chunk");
 
   __shared__ __attribute__((aligned(16))) uint16_t Kn[C * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * LDC];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDC];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[tsize<D, C>()];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[tsize<D, C>()];
   __shared__ __attribute__((aligned(16))) uint16_t St[D * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDK];
   __shared__ float zf[D];
@@ -189,14 +188,14 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
           }
           transpose8x8(kvr[x], tr);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) st16(&Kt[(fb * 8 + e) * LDC + tb * 8], tr[e]);
+          for (int e = 0; e < 8; ++e) st16(&Kt[tofs<C>(fb * 8 + e, tb * 8)], tr[e]);
         } else {
 #pragma unroll
           for (int r = 0; r < 8; ++r)
             if (c0 + tb * 8 + r >= t1) kvr[x][r] = zero_u4();
           transpose8x8(kvr[x], tr);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) st16(&Vt[(fb * 8 + e) * LDC + tb * 8], tr[e]);
+          for (int e = 0; e < 8; ++e) st16(&Vt[tofs<C>(fb * 8 + e, tb * 8)], tr[e]);
         }
       }
     }
@@ -211,32 +210,18 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
     for (int ks = 0; ks < KJ; ++ks) {
       u32x4 bv[NCW];
 #pragma unroll
-      for (int j = 0; j < NCW; ++j) bv[j] = ld16(&Vt[((sc0 + j) * 16 + l16) * LDC + ks * 32 + g * 8]);
+      for (int j = 0; j < NCW; ++j) bv[j] = ld16(&Vt[tofs<C>((sc0 + j) * 16 + l16, ks * 32 + g * 8)]);
 #pragma unroll
       for (int i = 0; i < NAW; ++i) {
-        const u32x4 ak = ld16(&Kt[((sa0 + i) * 16 + l16) * LDC + ks * 32 + g * 8]);
+        const u32x4 ak = ld16(&Kt[tofs<C>((sa0 + i) * 16 + l16, ks * 32 + g * 8)]);
         if (zown) zp[i] += sum_bf16x8(ak);
 #pragma unroll
         for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_bf16(ak, bv[j], accS[i][j]);
       }
     }
 
-    // ---- this wave's query tile: masked intra-chunk part + inter-chunk part, normalise, store
-    f32x4 accA[NI];
-#pragma unroll
-    for (int jt = 0; jt < NI; ++jt) {
-      accA[jt] = zero4();
-      if (jt <= it) {
-#pragma unroll
-        for (int ks = 0; ks < KA; ++ks)
-          accA[jt] = mfma_bf16(ld16(&Kn[(jt * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], accA[jt]);
-      }
-      if (jt == it) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (g * 4 + r > l16) accA[jt][r] = 0.f;
-      }
-    }
+    // ---- this wave's query tile: inter-chunk part, then the masked intra-chunk part one
+    // 32-key step at a time (A^T for key tiles 2m and 2m+1 goes straight into the V product)
     f32x4 acco[OCT];
     f32x4 accd = zero4();
 #pragma unroll
@@ -249,18 +234,32 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
         acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[l16 * LDK + ks * 32 + g * 8]), qf[ks], accd);
     }
-    // intra-chunk: V^T A^T and ones A^T over key tiles 0..it (pairs of 16)
+    // intra-chunk: A^T = phi(K) phi(Q)^T masked to key <= query, then V^T A^T and ones A^T
 #pragma unroll
     for (int m = 0; m < NI / 2; ++m) {
       if (2 * m <= it) {
+        f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KA; ++ks)
+          a0 = mfma_bf16(ld16(&Kn[(2 * m * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], a0);
+        if (2 * m + 1 <= it) {
+#pragma unroll
+          for (int ks = 0; ks < KA; ++ks)
+            a1 = mfma_bf16(ld16(&Kn[((2 * m + 1) * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], a1);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
+          if (2 * m + 1 == it && g * 4 + r > l16) a1[r] = 0.f;
+        }
         u32x4 af;
-        af.x = pack_bf16(accA[2 * m][0], accA[2 * m][1]);
-        af.y = pack_bf16(accA[2 * m][2], accA[2 * m][3]);
-        af.z = pack_bf16(accA[2 * m + 1][0], accA[2 * m + 1][1]);
-        af.w = pack_bf16(accA[2 * m + 1][2], accA[2 * m + 1][3]);
+        af.x = pack_bf16(a0[0], a0[1]);
+        af.y = pack_bf16(a0[2], a0[3]);
+        af.z = pack_bf16(a1[0], a1[1]);
+        af.w = pack_bf16(a1[2], a1[3]);
 #pragma unroll
         for (int ct = 0; ct < OCT; ++ct) {
-          const uint16_t* vrow = &Vt[((oc0 + ct) * 16 + l16) * LDC + m * 32 + g * 4];
+          const uint16_t* vrow = &Vt[tofs<C>((oc0 + ct) * 16 + l16, m * 32 + g * 4)];
           const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
           u32x4 av;

@@ -121,6 +121,23 @@ __device__ __forceinline__ u32x4 ld16_clamp(const uint16_t* base, int64_t row, i
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Token-major ("transposed") LDS tile layout, [rows][T] bf16 with rows = features: element
+// (a, j) sits at a*(T + 16) + (a / 8)*8 + j.  Two access patterns must be conflict-free on the
+// 64 four-byte banks, 16 lanes of a 16-byte access at a time:
+//   * MFMA operand reads: 16 consecutive rows, one column.  The row stride of T/2 + 8 dwords
+//     (an odd multiple of 8, mod 64) puts rows u = 0..7 on banks 8u (permuted), and the extra
+//     4 dwords after every 8 rows moves rows 8..15 onto the 4-bank groups in between;
+//   * transposed writes: 16 rows spaced 8 apart, one column.  Eight rows of stride add a
+//     multiple of 64 banks, so only the 4 dwords per 8-row group separate them: 16 distinct
+//     4-bank groups.
+template <int T>
+__device__ __forceinline__ int tofs(int a, int j) {
+  static_assert(((T / 2 + 8) / 8) % 2 == 1, "row stride must be an odd multiple of 8 dwords");
+  return a * (T + 16) + (a >> 3) * 8 + j;
+}
+template <int ROWS, int T>
+constexpr int tsize() { return ROWS * (T + 16) + ROWS; }
+
 // Wave-level sum over the 4 lanes that share l % 16 (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float sum_over_groups(float x) {
   x += __shfl_xor(x, 16);

@@ -78,15 +78,15 @@ __global__ __launch_bounds__(256) void state_reduce(KvStateArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
   constexpr int T = 16384 / D;       // tokens per tile
-  constexpr int LDT = T + 8;         // padded LDS row (bf16 elements)
+  constexpr int TS = tsize<D, T>();  // token-major tile (see tofs)
   constexpr int FB = D / 8;          // feature blocks per token row
   constexpr int NA = D / 64;         // a-tiles (of 16 rows) per wave
   constexpr int NC = D / 16;         // c-tiles
   // one buffer: the two token-major tiles, later reused for the fp32 result [KV | z]
-  static_assert(2 * D * LDT * 2 >= (D * D + D) * 4, "result must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * D * LDT];
+  static_assert(2 * TS * 2 >= (D * D + D) * 4, "result must fit in the tile buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TS];
   uint16_t* Kt = lds;
-  uint16_t* Vt = lds + D * LDT;
+  uint16_t* Vt = lds + TS;
 
   const GroupRange gr = group_range(a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
     transpose8x8(vr, tv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      st16(&Kt[(fb * 8 + e) * LDT + tb * 8], tk[e]);
-      st16(&Vt[(fb * 8 + e) * LDT + tb * 8], tv[e]);
+      st16(&Kt[tofs<T>(fb * 8 + e, tb * 8)], tk[e]);
+      st16(&Vt[tofs<T>(fb * 8 + e, tb * 8)], tv[e]);
     }
     if (t0 + T < gr.t1) load_tile(t0 + T);  // in flight through the MFMA phase
     __syncthreads();
@@ -136,11 +136,11 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
     for (int s = 0; s < T / 32; ++s) {
       u32x4 bv[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) bv[c] = ld16(&Vt[(c * 16 + l16) * LDT + s * 32 + g * 8]);
+      for (int c = 0; c < NC; ++c) bv[c] = ld16(&Vt[tofs<T>(c * 16 + l16, s * 32 + g * 8)]);
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int at = wave * NA + i;
-        u32x4 ak = ld16(&Kt[(at * 16 + l16) * LDT + s * 32 + g * 8]);
+        u32x4 ak = ld16(&Kt[tofs<T>(at * 16 + l16, s * 32 + g * 8)]);
         zacc[i] += sum_bf16x8(ak);
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[i][c] = mfma_bf16(ak, bv[c], acc[i][c]);
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a) {
 // column index: a lane's 16-byte load of a query row is directly its operand.
 template <int D>
 __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
-  constexpr int LD = D + 8;
+  constexpr int LD = D + 16;  // row stride of 8 mod 64 dwords: conflict-free 16-row reads
   constexpr int NC = D / 16;
   constexpr int KS = D / 32;
   constexpr int QPW = kNcQueries / 4;  // queries per wave
