@@ -27,11 +27,22 @@ __device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64
 
 // bf16 kernel, D = head dim, C = chunk.  512 threads = 8 waves; waves w and w+4 share SIMD w%4.
 //
-// LDS (bf16 unless noted):  Kn[C][D] phi(K) token-major rows (operand of phi(K) phi(Q)^T),
-// Kt[D][C] and Vt[D][C] feature-major rows (operands whose reduction index is the token),
-// St[D][D] the running state transposed, St[c][a] = S[a][c], rounded to bf16 (operand of
-// S^T phi(Q)^T), Zr[16][D] a normaliser tile: row 0 = bf16(z), row 1 = bf16(z - row 0),
-// rows 2..15 zero; zf[D] fp32 z.
+// LDS (bf16 unless noted), all row-major:
+//   Kn[C][D]      phi(K) of the chunk, token-major, row stride D + 16;
+//   Vn[2][C][D]   V of this chunk and of the next one (stored while this one is in use),
+//                 token-major, rows of D elements with the 16-byte pieces of row r permuted;
+//   St[D][D]      the running state transposed, St[c][a] = S[a][c], rounded to bf16;
+//   Zr[16][D]     a normaliser tile: row 0 = bf16(z), row 1 = bf16(z - row 0), rows 2..15 zero;
+//   zf[D]         fp32 z at the segment start.
+// Operands whose reduction index is the token (phi(K)^T and V in the state update, V^T in the
+// masked product) come straight from the token-major tiles through LDS transpose reads, so
+// nothing is transposed in registers and each tile is stored once.
+//
+// Pipeline: the K and V tiles and the query rows of chunk c + 1 are loaded into registers
+// while chunk c is computed (at points spread over the chunk, so that the memory queue does
+// not stall the issuing waves); V(c + 1) goes to the idle V buffer before the chunk's second
+// barrier, phi(K(c + 1)) to Kn after it, together with the new state and the outputs'
+// global stores.
 //
 // Work per wave:
 //   * one query tile of 16 rows (C = 128: tile w for w < 4, 11 - w otherwise, so the two waves
@@ -59,13 +70,13 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
   constexpr int OCT = NI == 8 ? NC : NC / 2;   // output column tiles per wave
   constexpr int KA = D / 32;         // k-steps over features
   constexpr int KJ = C / 32;         // k-steps over tokens
-  constexpr int NB = (C / 8) * (D / 8);        // 8x8 blocks per tile
-  constexpr int NKV = (2 * NB + NT - 1) / NT;  // K/V blocks per thread
+  constexpr int PPR = D / 8;          // 16-byte pieces per row
+  constexpr int RPK = C * PPR / NT;   // K pieces per thread
   static_assert(NI == 8 || NI == 4, "chunk");
+  static_assert(RPK >= 1, "tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t Kn[C * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[tsize<D, C>()];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[tsize<D, C>()];
+  __shared__ __attribute__((aligned(16))) uint16_t Vn[2 * C * D];
   __shared__ __attribute__((aligned(16))) uint16_t St[D * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDK];
   __shared__ float zf[D];
@@ -132,6 +143,17 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
   };
   write_state_bf16();
   __syncthreads();
+  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
+  u32x4 ones;                          // B operand with a column of ones (column 0)
+  ones.x = ones.y = ones.z = ones.w = (l16 == 0) ? one2 : 0u;
+  // z of this wave's feature tiles, kept as an MFMA accumulator: phi(K)^T [1 0 ... 0] puts the
+  // key sums in column 0, i.e. in lanes with l16 == 0, rows 4g + r
+  f32x4 accz[NAW];
+  const u32x4 zones = zown ? ones : zero_u4();
+#pragma unroll
+  for (int i = 0; i < NAW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accz[i][r] = (zown && l16 == 0) ? zf[(sa0 + i) * 16 + g * 4 + r] : 0.f;
   for (int e = tid; e < 16 * D; e += NT) {
     const int row = e / D, c = e % D;
     uint16_t val = 0;
@@ -143,82 +165,102 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
     Zr[row * LDK + c] = val;
   }
 
-  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
-  u32x4 ones;
-  ones.x = ones.y = ones.z = ones.w = (l16 == 0) ? one2 : 0u;
-
-  // ---- chunk loads (issued one chunk ahead)
-  u32x4 kvr[NKV][8];
-  u32x4 qr[KA];
-  auto load_chunk = [&](int64_t c0) {
+  // ---- K and V tiles: piece tid + 512 p of each (16 consecutive lanes cover one 256-byte row
+  // when D = 128)
+  u32x4 kv[RPK], vv[RPK];
+  u32x4 qr[KA];  // this wave's query rows (raw)
+  auto prow = [&](int p) { return tid / PPR + p * (NT / PPR); };
+  const int pcol = (tid % PPR) * 8;
+  auto load_k = [&](int64_t c0) {
 #pragma unroll
-    for (int x = 0; x < NKV; ++x) {
-      const int b = tid + NT * x;
-      if ((2 * NB) % NT == 0 || b < 2 * NB) {
-        const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
-        const uint16_t* src = b < NB ? K : V;
+    for (int p = 0; p < RPK; ++p) kv[p] = ld16_clamp(K, c0 + prow(p), t1, D, pcol);
+  };
+  auto load_v = [&](int64_t c0) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) kvr[x][r] = ld16_clamp(src, c0 + tb * 8 + r, t1, D, fb * 8);
-      }
+    for (int p = 0; p < RPK; ++p) vv[p] = ld16_clamp(V, c0 + prow(p), t1, D, pcol);
+  };
+  // feature map on K; rows past the segment end become zero in both tiles
+  auto prep_kv = [&](int64_t c0) {
+#pragma unroll
+    for (int p = 0; p < RPK; ++p) {
+      const bool ok = c0 + prow(p) < t1;
+      kv[p] = ok ? phi_bf16x8(kv[p]) : zero_u4();
+      vv[p] = ok ? vv[p] : zero_u4();
     }
+  };
+  auto store_k = [&]() {
+#pragma unroll
+    for (int p = 0; p < RPK; ++p) st16(&Kn[prow(p) * LDK + pcol], kv[p]);
+  };
+  auto load_q = [&](int64_t c0) {
     const int64_t row = c0 + it * 16 + l16;
 #pragma unroll
     for (int ks = 0; ks < KA; ++ks) qr[ks] = ld16_clamp(Q, row, t1, D, ks * 32 + g * 8);  // rows >= t1 are never stored
   };
 
-  float zp[NAW];
+  // ---- V tiles.  Piece permutation: the 8 rows that a half-wave transpose read touches fall
+  // on distinct bank groups (rows of 256 bytes: one row per 64 banks; of 128 bytes: two).
+  constexpr int VRL = 128 / D;
+  auto vofs = [&](int r, int c) { return r * D + ((((c >> 3) ^ (2 * ((r / VRL) % (D / 16))))) << 3) + (c & 7); };
+  // 16x16x32 operand with k over the rows of a V tile (the layout of ld_rows_operand); rows
+  // r and r + 16 share their permutation
+  auto ld_v_operand = [&](const uint16_t* Vt, int row0, int col0) {
+    const uint16_t* p0 = Vt + vofs(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3));
+    const u32x2 lo = ld_tr16(p0), hi = ld_tr16(p0 + 16 * D);
+    u32x4 r;
+    r.x = lo.x;
+    r.y = lo.y;
+    r.z = hi.x;
+    r.w = hi.y;
+    return r;
+  };
+  auto store_v = [&](uint16_t* Vt) {
 #pragma unroll
-  for (int i = 0; i < NAW; ++i) zp[i] = 0.f;
+    for (int p = 0; p < RPK; ++p) st16(&Vt[vofs(prow(p), pcol)], vv[p]);
+  };
 
-  if (t0 < t1) load_chunk(t0);
-  for (int64_t c0 = t0; c0 < t1; c0 += C) {
-    // ---- (a) tiles into LDS: phi(K) natural + transposed, V transposed; phi(Q) in registers
-#pragma unroll
-    for (int x = 0; x < NKV; ++x) {
-      const int b = tid + NT * x;
-      if ((2 * NB) % NT == 0 || b < 2 * NB) {
-        const int blk = b % NB, tb = blk / (D / 8), fb = blk % (D / 8);
-        u32x4 tr[8];
-        if (b < NB) {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const bool ok = c0 + tb * 8 + r < t1;
-            kvr[x][r] = ok ? phi_bf16x8(kvr[x][r]) : zero_u4();
-            st16(&Kn[(tb * 8 + r) * LDK + fb * 8], kvr[x][r]);
-          }
-          transpose8x8(kvr[x], tr);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st16(&Kt[tofs<C>(fb * 8 + e, tb * 8)], tr[e]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 8; ++r)
-            if (c0 + tb * 8 + r >= t1) kvr[x][r] = zero_u4();
-          transpose8x8(kvr[x], tr);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st16(&Vt[tofs<C>(fb * 8 + e, tb * 8)], tr[e]);
-        }
-      }
-    }
+  if (t0 < t1) {
+    load_k(t0);
+    load_v(t0);
+    load_q(t0);
+    prep_kv(t0);
+    store_k();
+    store_v(Vn);
+  }
+  int buf = 0;
+  for (int64_t c0 = t0; c0 < t1; c0 += C, buf ^= 1) {
+    __syncthreads();  // tiles of this chunk, St, Zr ready
+    const uint16_t* Vc = Vn + buf * (C * D);
+    // Loads for the next chunk go out in three groups (K here, V after the state update, the
+    // query rows after the inter-chunk product), pinned in place by scheduling barriers: one
+    // burst of all of them would fill the memory queue and stall the issuing waves.  Every
+    // thread loads at the same points, unconditionally (rows past the end are clamped):
+    // loads under a condition would join the loop-carried registers through copies that wait
+    // for the data on the spot.
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 qf[KA];
 #pragma unroll
     for (int ks = 0; ks < KA; ++ks) qf[ks] = phi_bf16x8(qr[ks]);
-    if (c0 + C < t1) load_chunk(c0 + C);  // next chunk in flight through the whole compute phase
-    __syncthreads();  // tiles, St, Zr ready
 
-    // ---- (iv) state update in registers: S[own block] += phi(K_c)^T V_c ; z partial sums
+    // ---- (iv) state update in registers: S[own block] += phi(K_c)^T V_c ; z
 #pragma unroll
     for (int ks = 0; ks < KJ; ++ks) {
       u32x4 bv[NCW];
 #pragma unroll
-      for (int j = 0; j < NCW; ++j) bv[j] = ld16(&Vt[tofs<C>((sc0 + j) * 16 + l16, ks * 32 + g * 8)]);
+      for (int j = 0; j < NCW; ++j) bv[j] = ld_v_operand(Vc, ks * 32, (sc0 + j) * 16);
 #pragma unroll
       for (int i = 0; i < NAW; ++i) {
-        const u32x4 ak = ld16(&Kt[tofs<C>((sa0 + i) * 16 + l16, ks * 32 + g * 8)]);
-        if (zown) zp[i] += sum_bf16x8(ak);
+        const u32x4 ak = ld_rows_operand(Kn, LDK, ks * 32, (sa0 + i) * 16, l16, g);
+        accz[i] = mfma_bf16(ak, zones, accz[i]);  // no branch: zones is zero where z is not kept
 #pragma unroll
         for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_bf16(ak, bv[j], accS[i][j]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- this wave's query tile: inter-chunk part, then the masked intra-chunk part one
     // 32-key step at a time (A^T for key tiles 2m and 2m+1 goes straight into the V product)
@@ -234,73 +276,97 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
         acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[l16 * LDK + ks * 32 + g * 8]), qf[ks], accd);
     }
-    // intra-chunk: A^T = phi(K) phi(Q)^T masked to key <= query, then V^T A^T and ones A^T
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
+    // intra-chunk: A^T = phi(K) phi(Q)^T masked to key <= query, then V^T A^T and ones A^T.
+    // Step m covers key tiles 2m and 2m+1; the A^T products of step m+1 are issued before the
+    // V products of step m so that the two overlap.  A key tile past the query tile is zeroed.
+    auto a_tiles = [&](int m, f32x4& a0, f32x4& a1) {
+      a0 = zero4();
+      a1 = zero4();
 #pragma unroll
-    for (int m = 0; m < NI / 2; ++m) {
-      if (2 * m <= it) {
-        f32x4 a0 = zero4(), a1 = zero4();
+      for (int ks = 0; ks < KA; ++ks) {
+        a0 = mfma_bf16(ld16(&Kn[(2 * m * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], a0);
+        a1 = mfma_bf16(ld16(&Kn[((2 * m + 1) * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], a1);
+      }
+    };
+    auto pack_a = [&](int m, f32x4 a0, f32x4 a1) {
 #pragma unroll
-        for (int ks = 0; ks < KA; ++ks)
-          a0 = mfma_bf16(ld16(&Kn[(2 * m * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], a0);
-        if (2 * m + 1 <= it) {
+      for (int r = 0; r < 4; ++r) {
+        if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
+        if (2 * m + 1 > it || (2 * m + 1 == it && g * 4 + r > l16)) a1[r] = 0.f;
+      }
+      u32x4 af;
+      af.x = pack_bf16(a0[0], a0[1]);
+      af.y = pack_bf16(a0[2], a0[3]);
+      af.z = pack_bf16(a1[0], a1[1]);
+      af.w = pack_bf16(a1[2], a1[3]);
+      return af;
+    };
+    auto av_step = [&](int m, u32x4 af) {
 #pragma unroll
-          for (int ks = 0; ks < KA; ++ks)
-            a1 = mfma_bf16(ld16(&Kn[((2 * m + 1) * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], a1);
-        }
+      for (int ct = 0; ct < OCT; ++ct)
+        acco[ct] = mfma_bf16(ld_v_operand(Vc, m * 32, (oc0 + ct) * 16), af, acco[ct]);
+      accd = mfma_bf16(ones, af, accd);
+    };
+    const int mlast = it >> 1;
+    f32x4 a0, a1;
+    a_tiles(0, a0, a1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
-          if (2 * m + 1 == it && g * 4 + r > l16) a1[r] = 0.f;
-        }
-        u32x4 af;
-        af.x = pack_bf16(a0[0], a0[1]);
-        af.y = pack_bf16(a0[2], a0[3]);
-        af.z = pack_bf16(a1[0], a1[1]);
-        af.w = pack_bf16(a1[2], a1[3]);
-#pragma unroll
-        for (int ct = 0; ct < OCT; ++ct) {
-          const uint16_t* vrow = &Vt[tofs<C>((oc0 + ct) * 16 + l16, m * 32 + g * 4)];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-          u32x4 av;
-          av.x = lo.x;
-          av.y = lo.y;
-          av.z = hi.x;
-          av.w = hi.y;
-          acco[ct] = mfma_bf16(av, af, acco[ct]);
-        }
-        accd = mfma_bf16(ones, af, accd);
+    for (int m = 0; m < NI / 2 - 1; ++m) {
+      if (m < mlast) {
+        const u32x4 af = pack_a(m, a0, a1);
+        a_tiles(m + 1, a0, a1);
+        av_step(m, af);
       }
     }
+    av_step(mlast, pack_a(mlast, a0, a1));
+
     const float den = __shfl(accd[0] + accd[1], l16);
     const float inv = 1.0f / den;
+    // Outputs: a lane holds 4 columns of each column tile.  For a pair of tiles (ct, ct + 1)
+    // lane rows g and g ^ 1 swap halves (v_permlane16_swap: odd rows of the first operand with
+    // even rows of the second), so that a lane of row g holds 8 consecutive columns of tile
+    // ct + (g & 1), starting at 8 (g / 2): one 16-byte store.
     const int64_t row = c0 + it * 16 + l16;
-    if (row < t1) {
 #pragma unroll
-      for (int ct = 0; ct < OCT; ++ct) {
-        u32x2 o;
-        o.x = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
-        o.y = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
-        *reinterpret_cast<u32x2*>(O + row * D + (oc0 + ct) * 16 + g * 4) = o;
-      }
+    for (int ct = 0; ct < OCT; ct += 2) {
+      const uint32_t ax = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
+      const uint32_t ay = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
+      const uint32_t bx = pack_bf16(acco[ct + 1][0] * inv, acco[ct + 1][1] * inv);
+      const uint32_t by = pack_bf16(acco[ct + 1][2] * inv, acco[ct + 1][3] * inv);
+      const auto sx = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
+      u32x4 o;
+      o.x = sx[0];
+      o.y = sy[0];
+      o.z = sx[1];
+      o.w = sy[1];
+      if (row < t1) st16(O + row * D + (oc0 + ct + (g & 1)) * 16 + 8 * (g >> 1), o);
     }
-    __syncthreads();  // every wave is done reading this chunk's tiles, St and Zr
+    // next chunk's tiles (past the last chunk these are zero tiles that nothing reads); its V
+    // goes to the idle buffer at once
+    prep_kv(c0 + C);
+    store_v(Vn + (buf ^ 1) * (C * D));
+    __syncthreads();  // every wave is done reading this chunk's Kn, St and Zr
 
-    // ---- publish the new state for the next chunk
+    // ---- the next chunk's phi(K), the new state
+    store_k();
     write_state_bf16();
-    if (zown) {
+    if (zown && l16 == 0) {
 #pragma unroll
       for (int i = 0; i < NAW; ++i) {
-        const int at = sa0 + i;
-        const float zs = sum_over_groups(zp[i]);
-        zp[i] = 0.f;
-        if (g == 0) {
-          const float z = zf[at * 16 + l16] + zs;
-          zf[at * 16 + l16] = z;
-          const __bf16 hi = (__bf16)z;
-          Zr[at * 16 + l16] = __builtin_bit_cast(uint16_t, hi);
-          Zr[LDK + at * 16 + l16] = __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
-        }
+        u32x2 hi2, lo2;
+        float hi[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hi[r] = (float)(__bf16)accz[i][r];
+        hi2.x = pack_bf16(hi[0], hi[1]);
+        hi2.y = pack_bf16(hi[2], hi[3]);
+        lo2.x = pack_bf16(accz[i][0] - hi[0], accz[i][1] - hi[1]);
+        lo2.y = pack_bf16(accz[i][2] - hi[2], accz[i][3] - hi[3]);
+        *reinterpret_cast<u32x2*>(&Zr[(sa0 + i) * 16 + g * 4]) = hi2;
+        *reinterpret_cast<u32x2*>(&Zr[LDK + (sa0 + i) * 16 + g * 4]) = lo2;
       }
     }
   }

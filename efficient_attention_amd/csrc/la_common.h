@@ -138,6 +138,34 @@ __device__ __forceinline__ int tofs(int a, int j) {
 template <int ROWS, int T>
 constexpr int tsize() { return ROWS * (T + 16) + ROWS; }
 
+// LDS transpose read (ds_read_b64_tr_b16, gfx950; lane layout checked on hardware).  Within each
+// group of 16 lanes, lane i receives element i % 4 of the four 16-bit values read by lane
+// 4e + i / 4, for e = 0..3.  So when lane j of the group addresses T[R + j / 4][C0 + 4 (j % 4)] of a
+// row-major tile T, lane i receives T[R + e][C0 + i]: four rows of one column.
+__device__ __forceinline__ u32x2 ld_tr16(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 16x16x32 MFMA operand whose reduction index runs over the rows of a row-major LDS tile T
+// (leading dimension ld): lane l holds column col0 + l % 16 and, in k slot 4h + e, row
+// row0 + 16h + 4(l / 16) + e.  The row order is the one in which an MFMA result holds its rows
+// (two 16-row tiles, rows 4(l / 16) + r), so such a result can be the other operand directly.
+// With a row stride of 8 (mod 64) dwords every half-wave reads 8 rows x 32 bytes, conflict-free.
+__device__ __forceinline__ u32x4 ld_rows_operand(const uint16_t* T, int ld, int row0, int col0,
+                                                 int l16, int g) {
+  const uint16_t* p = T + (row0 + 4 * g + (l16 >> 2)) * ld + col0 + 4 * (l16 & 3);
+  const u32x2 lo = ld_tr16(p), hi = ld_tr16(p + 16 * ld);
+  u32x4 r;
+  r.x = lo.x;
+  r.y = lo.y;
+  r.z = hi.x;
+  r.w = hi.y;
+  return r;
+}
+
 // Wave-level sum over the 4 lanes that share l % 16 (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float sum_over_groups(float x) {
   x += __shfl_xor(x, 16);
