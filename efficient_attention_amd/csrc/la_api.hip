@@ -67,8 +67,11 @@ StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
 size_t state_bytes(int64_t groups, int d) { return (size_t)groups * (size_t)(d * d + d) * sizeof(float); }
 
 // Non-causal workspace: [partials][states].
-size_t nc_state_off(const StatePlan& p) { return round256(p.scratch_bytes); }
-size_t nc_ws_bytes(const StatePlan& p, int d) { return nc_state_off(p) + state_bytes(p.groups, d); }
+// Non-causal workspace: the per-slice partials (summed by the output kernel), or the states
+// themselves when every head has one slice.
+size_t nc_ws_bytes(const StatePlan& p, int d) {
+  return p.slices > 1 ? p.scratch_bytes : state_bytes(p.groups, d);
+}
 
 // Causal workspace: the leading segments' partials (or their sums when one slice each).
 size_t causal_ws_bytes(const StatePlan& p, int d) {
@@ -159,14 +162,14 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
     return LA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  float* states = reinterpret_cast<float*>(ws + nc_state_off(p));
-  la::KvStateArgs ka = state_args(p, k, v, reinterpret_cast<float*>(ws), states, n, n, 1);
+  float* parts = reinterpret_cast<float*>(ws);
+  la::KvStateArgs ka = state_args(p, k, v, parts, parts, n, n, 1);
   if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
-  if (p.slices > 1 && la::launch_state_reduce(ka, (int)d, s) != hipSuccess) return LA_ERR_HIP;
-  la::NcOutArgs oa;
+  la::NcOutArgs oa;  // the output kernel adds each head's slices itself
   oa.q = q;
   oa.out = out;
-  oa.state = states;
+  oa.state = parts;
+  oa.slices = p.slices;
   oa.n = n;
   oa.bh = bh;
   if (la::launch_nc_out(oa, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;

@@ -184,8 +184,8 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
 #pragma unroll
     for (int p = 0; p < RPK; ++p) {
       const bool ok = c0 + prow(p) < t1;
-      kv[p] = ok ? phi_bf16x8(kv[p]) : zero_u4();
-      vv[p] = ok ? vv[p] : zero_u4();
+      kv[p] = keep_if(phi_bf16x8(kv[p]), ok);
+      vv[p] = keep_if(vv[p], ok);
     }
   };
   auto store_k = [&]() {

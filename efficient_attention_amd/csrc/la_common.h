@@ -31,11 +31,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // phi(x) = elu(x) + 1 with alpha = 1: x + 1 above zero, exp(x) at or below zero
 // ("Efficient Transformers: Linear Attention and Flash Attention", section "Linear attention",
-// feature map elu + 1).  exp is the hardware base-2 exponential of x*log2(e); for x < -87 the
-// result may flush to zero.
+// feature map elu + 1).  Since e^x >= 1 + x everywhere, phi(x) = max(x + 1, e^min(x, 0)), and
+// e^min(x, 0) = min(e^x, 1) is the exp instruction with its output clamp: four instructions,
+// no compare.  exp is the hardware base-2 exponential of x*log2(e) (it may flush to zero
+// below x = -87); maximum() propagates NaN.
 __device__ __forceinline__ float phi(float x) {
-  float e = __builtin_amdgcn_exp2f(x * kLog2e);
-  return x > 0.f ? x + 1.f : e;
+  const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * kLog2e), 0.f, 1.f);
+  return __builtin_elementwise_maximum(x + 1.f, e);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -119,7 +121,43 @@ __device__ __forceinline__ u32x4 ld16_clamp(const uint16_t* base, int64_t row, i
   const int64_t r = row < end ? row : end - 1;
   return ld16(base + r * ld + col);
 }
+// Row `row` of a tile whose first row is `tile` (a wave-uniform pointer), 16 bytes at column
+// `col`, reading row `last` instead of any row beyond it: the per-lane part of the address is a
+// small non-negative 32-bit offset, which the load adds to the uniform base itself.
+__device__ __forceinline__ u32x4 ld16_row(const uint16_t* tile, int row, int last, int ld, int col) {
+  const int r = row < last ? row : last;
+  const uint32_t bytes = (uint32_t)(r * ld + col) * 2u;
+  return ld16(reinterpret_cast<const char*>(tile) + bytes);
+}
+
+// First row and last valid row (relative, clamped to [0, rows - 1]) of a tile of `rows` rows
+// starting at token t of a sequence whose valid rows end at t_end (exclusive, t_end > 0).  A tile
+// wholly past the end reads row t_end - 1 only.
+struct TileRows {
+  int64_t first;
+  int last;
+};
+__device__ __forceinline__ TileRows tile_rows(int64_t t, int64_t t_end, int rows) {
+  TileRows tr;
+  tr.first = t < t_end ? t : t_end - 1;
+  const int64_t lim = t_end - 1 - tr.first;
+  tr.last = lim < rows - 1 ? (int)lim : rows - 1;
+  return tr;
+}
+
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// v, or zero when keep is false, without control flow.  A conditional expression here would
+// compile to a branch around the work that produced v, with register copies of loaded data
+// that make the compiler wait for every load in flight.
+__device__ __forceinline__ u32x4 keep_if(u32x4 v, bool keep) {
+  const uint32_t m = 0u - (uint32_t)keep;
+  v.x &= m;
+  v.y &= m;
+  v.z &= m;
+  v.w &= m;
+  return v;
+}
 
 // Token-major ("transposed") LDS tile layout, [rows][T] bf16 with rows = features: element
 // (a, j) sits at a*(T + 16) + (a / 8)*8 + j.  Two access patterns must be conflict-free on the

@@ -24,7 +24,8 @@ struct KvStateArgs {
 struct NcOutArgs {
   const void* q;
   void* out;
-  const float* state;   // [bh][D*D + D]
+  const float* state;   // [bh][slices][D*D + D]: a head's state is the sum of its slices
+  int64_t slices;
   int64_t n;
   int64_t bh;
 };
@@ -59,10 +60,14 @@ hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s);
 hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
 
-// Queries per workgroup of the non-causal output kernel (4 waves x 128).
-constexpr int64_t kNcQueries = 512;
+// Queries per workgroup of the non-causal output kernel (4 waves x 512).
+constexpr int64_t kNcQueries = 2048;
 
 // Tile sizes the host needs for workspace planning.
-inline int64_t kv_state_tile(int d, int dtype) { return dtype == 1 ? 16384 / d : 64; }
+constexpr int kStateTileBf16 = 64;  // kv_state_bf16: tokens per workgroup tile
+constexpr int kStateTileWave = 32;  // kv_state_bf16_waves (D = 64): tokens per wave tile
+inline int64_t kv_state_tile(int d, int dtype) {
+  return dtype == 1 ? (d == 64 ? 4 * kStateTileWave : kStateTileBf16) : 64;
+}
 
 }  // namespace la

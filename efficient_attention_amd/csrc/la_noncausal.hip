@@ -70,28 +70,47 @@ __global__ __launch_bounds__(256) void state_reduce(KvStateArgs a) {
   reinterpret_cast<f32x4*>(a.state + g * E)[e] = acc;
 }
 
-// bf16 stage 1.  Tile = T tokens with T*D = 16384, so each of the 256 threads owns one 8x8
-// block of K and one of V per tile.  A block is loaded as 8 rows of 16 bytes, phi is applied
-// to K in fp32 and rounded to bf16, and both blocks are transposed in registers so LDS holds
-// token-contiguous rows: Kt[a][t] = phi(K)[t][a], Vt[c][t] = V[t][c].  That is the layout the
-// MFMA wants, because the reduction index of phi(K)^T V is the token.
+// Writes a wave's block of the state straight from its MFMA accumulators: rows (features)
+// 16 at + 4g + r, columns 16 c + l16, and z (already summed over the lane groups) by the lanes
+// of group 0.
+template <int D, int NA, int NC>
+__device__ __forceinline__ void store_state_block(float* dst, int at0, const f32x4 (&acc)[NA][NC],
+                                                  const float (&z)[NA], int l16, int g) {
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int at = at0 + i;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(at * 16 + g * 4 + r) * D + c * 16 + l16] = acc[i][c][r];
+    if (g == 0) dst[D * D + at * 16 + l16] = z[i];
+  }
+}
+
+// bf16 stage 1.  Tiles of T tokens.  phi(K) and V are stored token-major in LDS, as they come
+// from HBM (16 consecutive lanes load one 256-byte row when D = 128), and the MFMA operands of
+// phi(K)^T V, whose reduction index is the token, are read through LDS transpose reads: no
+// transposes in registers.  Wave w accumulates feature tiles NA*w.. against all value columns.
+// Loads run NS - 1 tiles ahead in NS register sets (the tile loop is unrolled by NS; loads past
+// the end are clamped and their rows masked, so they need no condition).  Small LDS and
+// register footprints let several workgroups share a CU and overlap one another's loads,
+// feature map and MFMA work.
 template <int D>
 __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
-  constexpr int T = 16384 / D;       // tokens per tile
-  constexpr int TS = tsize<D, T>();  // token-major tile (see tofs)
-  constexpr int FB = D / 8;          // feature blocks per token row
-  constexpr int NA = D / 64;         // a-tiles (of 16 rows) per wave
-  constexpr int NC = D / 16;         // c-tiles
-  // one buffer: the two token-major tiles, later reused for the fp32 result [KV | z]
-  static_assert(2 * TS * 2 >= (D * D + D) * 4, "result must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TS];
-  uint16_t* Kt = lds;
-  uint16_t* Vt = lds + TS;
+  constexpr int T = kStateTileBf16;  // tokens per tile
+  constexpr int LDK = D + 16;        // row stride of 8 (mod 64) dwords x odd: conflict-free reads
+  constexpr int PPR = D / 8;         // 16-byte pieces per row
+  constexpr int NP = T * PPR / 256;  // pieces per thread and tensor
+  constexpr int NA = D / 64;         // feature tiles per wave
+  constexpr int NC = D / 16;         // value-column tiles
+  constexpr int NS = D == 64 ? 3 : 2;  // register sets of loads in flight
+  static_assert(NP >= 1 && T % 32 == 0, "tile");
+  __shared__ __attribute__((aligned(16))) uint16_t Kn[T * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Vn[T * LDK];
 
   const GroupRange gr = group_range(a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int tb = tid / FB, fb = tid % FB;  // this thread's 8x8 block in the tile
   const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + gr.bh * a.n * D;
   const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + gr.bh * a.n * D;
 
@@ -104,66 +123,221 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
     for (int c = 0; c < NC; ++c) acc[i][c] = zero4();
   }
 
-  u32x4 kr[8], vr[8];
-  auto load_tile = [&](int64_t t0) {
+  auto prow = [&](int p) { return tid / PPR + p * (256 / PPR); };
+  const int pcol = (tid % PPR) * 8;
+  u32x4 kq[NS][NP], vq[NS][NP];
+  auto load = [&](int64_t t0, u32x4 (&k)[NP], u32x4 (&v)[NP]) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      kr[r] = ld16_clamp(K, t0 + tb * 8 + r, gr.t1, D, fb * 8);
-      vr[r] = ld16_clamp(V, t0 + tb * 8 + r, gr.t1, D, fb * 8);
+    for (int p = 0; p < NP; ++p) {
+      k[p] = ld16_clamp(K, t0 + prow(p), gr.t1, D, pcol);
+      v[p] = ld16_clamp(V, t0 + prow(p), gr.t1, D, pcol);
     }
   };
-
-  if (gr.t0 < gr.t1) load_tile(gr.t0);
-  for (int64_t t0 = gr.t0; t0 < gr.t1; t0 += T) {
-    // phi on K (invalid rows forced to zero after phi), transpose, write LDS
-    u32x4 tk[8], tv[8];
+  auto tile = [&](int64_t t0, u32x4 (&k)[NP], u32x4 (&v)[NP]) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      bool ok = t0 + tb * 8 + r < gr.t1;
-      kr[r] = ok ? phi_bf16x8(kr[r]) : zero_u4();
-      vr[r] = ok ? vr[r] : zero_u4();
+    for (int p = 0; p < NP; ++p) {  // phi on K; rows past the end are zero in both tiles
+      const bool ok = t0 + prow(p) < gr.t1;
+      k[p] = keep_if(phi_bf16x8(k[p]), ok);
+      v[p] = keep_if(v[p], ok);
     }
-    transpose8x8(kr, tk);
-    transpose8x8(vr, tv);
+    __syncthreads();  // the previous tile's operands have been read
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st16(&Kt[tofs<T>(fb * 8 + e, tb * 8)], tk[e]);
-      st16(&Vt[tofs<T>(fb * 8 + e, tb * 8)], tv[e]);
+    for (int p = 0; p < NP; ++p) {
+      st16(&Kn[prow(p) * LDK + pcol], k[p]);
+      st16(&Vn[prow(p) * LDK + pcol], v[p]);
     }
-    if (t0 + T < gr.t1) load_tile(t0 + T);  // in flight through the MFMA phase
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < T / 32; ++s) {
       u32x4 bv[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) bv[c] = ld16(&Vt[tofs<T>(c * 16 + l16, s * 32 + g * 8)]);
+      for (int c = 0; c < NC; ++c) bv[c] = ld_rows_operand(Vn, LDK, s * 32, c * 16, l16, g);
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int at = wave * NA + i;
-        u32x4 ak = ld16(&Kt[tofs<T>(at * 16 + l16, s * 32 + g * 8)]);
+        const u32x4 ak = ld_rows_operand(Kn, LDK, s * 32, (wave * NA + i) * 16, l16, g);
         zacc[i] += sum_bf16x8(ak);
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[i][c] = mfma_bf16(ak, bv[c], acc[i][c]);
       }
     }
-    __syncthreads();
+  };
+
+  // The sets go out strictly in order (scheduling barriers): the compiler's wait counts for a
+  // set assume the loads issued after it, and an interleaved order would make it wait for
+  // later sets as well.
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    load(gr.t0 + u * T, kq[u], vq[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t t0 = gr.t0; t0 < gr.t1; t0 += NS * T) {  // spare tiles past the end are all zero
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      tile(t0 + u * T, kq[u], vq[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      load(t0 + (u + NS) * T, kq[u], vq[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // results -> LDS (fp32, reusing the tile buffers) -> global
-  float* kv_lds = reinterpret_cast<float*>(lds);
-  float* z_lds = kv_lds + D * D;
+  float z[NA];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int at = wave * NA + i;
+  for (int i = 0; i < NA; ++i) z[i] = sum_over_groups(zacc[i]);
+  float* dst = a.slices == 1 ? a.state + gr.g * (D * D + D)
+                             : a.partials + (gr.g * a.slices + gr.s) * (D * D + D);
+  store_state_block<D, NA, NC>(dst, wave * NA, acc, z, l16, g);
+}
+
+// bf16 stage 1 for D = 64, one wave per token stream.  Wave w of the workgroup takes tiles
+// w, w + 4, ... of TW tokens; it stores phi(K) and V token-major in its own LDS area and reads
+// them back as MFMA operands with transpose reads.  A wave's LDS accesses are executed in
+// order, so the loop needs no barrier: waves stream independently instead of waiting for the
+// slowest at every tile.  Each wave accumulates the whole 64 x 64 state (16 MFMA tiles) and z,
+// phi(K)^T times a column of ones: one more MFMA per feature tile, from the same bf16 phi(K)
+// operands as the state, on the MFMA pipe instead of the vector ALU (which the feature map
+// keeps busy).  The four partial states are added at the end in a fixed order,
+// ((w0 + w2) + (w1 + w3)).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_state_bf16_waves(KvStateArgs a) {
+  constexpr int TW = kStateTileWave;  // tokens per wave tile
+  constexpr int LDK = D + 16;          // row stride of 8 (mod 64) dwords x odd: conflict-free reads
+  constexpr int PPR = D / 8;           // 16-byte pieces per row
+  constexpr int NP = TW * PPR / 64;    // pieces per lane and tensor
+  constexpr int NT = D / 16;           // feature tiles = value-column tiles
+  constexpr int NS = 2;                // register sets of loads in flight
+  constexpr int WL = 2 * TW * LDK;     // LDS elements per wave
+  static_assert(D == 64 && TW == 32, "one 32-token k-step per tile");
+  static_assert(4 * WL * 2 >= 2 * (D * D + D) * 4, "the final combine reuses the tile areas");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * WL];
+
+  const GroupRange gr = group_range(a);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
+  const int l16 = lane & 15, g = lane >> 4;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + gr.bh * a.n * D;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + gr.bh * a.n * D;
+  uint16_t* Kw = lds + wave * WL;
+  uint16_t* Vw = Kw + TW * LDK;
+
+  f32x4 acc[NT][NT];
+  f32x4 accz[NT];  // z of feature tile i: column 0, i.e. lanes l16 == 0, rows 4g + r
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+  for (int i = 0; i < NT; ++i) {
+    accz[i] = zero4();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) kv_lds[(at * 16 + g * 4 + r) * D + c * 16 + l16] = acc[i][c][r];
-    float zs = sum_over_groups(zacc[i]);
-    if (g == 0) z_lds[at * 16 + l16] = zs;
+    for (int c = 0; c < NT; ++c) acc[i][c] = zero4();
   }
+  u32x4 ones;  // B operand: a column of bf16 ones (column 0)
+  ones.x = ones.y = ones.z = ones.w = l16 == 0 ? 0x3F803F80u : 0u;
+
+  auto prow = [&](int p) { return lane / PPR + p * (64 / PPR); };
+  const int pcol = (lane % PPR) * 8;
+  u32x4 kq[NS][NP], vq[NS][NP];
+  auto load = [&](int64_t t0, u32x4 (&k)[NP], u32x4 (&v)[NP]) {
+    const TileRows tr = tile_rows(t0, gr.t1, TW);
+    const uint16_t* kt = K + tr.first * D;
+    const uint16_t* vt = V + tr.first * D;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      k[p] = ld16_row(kt, prow(p), tr.last, D, pcol);
+      v[p] = ld16_row(vt, prow(p), tr.last, D, pcol);
+    }
+  };
+  auto tile = [&](int64_t t0, u32x4 (&k)[NP], u32x4 (&v)[NP]) {
+    const int lim = t0 < gr.t1 ? (gr.t1 - t0 < TW ? (int)(gr.t1 - t0) : TW) : 0;  // valid rows
+    if (lim == TW) {  // uniform: only the last tiles need the row mask
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        st16(&Kw[prow(p) * LDK + pcol], phi_bf16x8(k[p]));
+        st16(&Vw[prow(p) * LDK + pcol], v[p]);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {  // phi on K; rows past the end are zero in both tiles
+        const bool ok = prow(p) < lim;
+        st16(&Kw[prow(p) * LDK + pcol], keep_if(phi_bf16x8(k[p]), ok));
+        st16(&Vw[prow(p) * LDK + pcol], keep_if(v[p], ok));
+      }
+    }
+    u32x4 bv[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) bv[c] = ld_rows_operand(Vw, LDK, 0, c * 16, l16, g);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const u32x4 ak = ld_rows_operand(Kw, LDK, 0, i * 16, l16, g);
+      accz[i] = mfma_bf16(ak, ones, accz[i]);
+#pragma unroll
+      for (int c = 0; c < NT; ++c) acc[i][c] = mfma_bf16(ak, bv[c], acc[i][c]);
+    }
+  };
+
+  // wave tiles: t = gr.t0 + (4 j + wave) TW; loads go out strictly in order (see kv_state_bf16)
+  const int64_t step = 4 * TW;
+  const int64_t w0 = gr.t0 + wave * TW;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    load(w0 + u * step, kq[u], vq[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t t = w0; t - wave * TW < gr.t1; t += NS * step) {  // spare tiles are all zero
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      tile(t + u * step, kq[u], vq[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      load(t + (u + NS) * step, kq[u], vq[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- combine the four partial states: ((w0 + w2) + (w1 + w3))
+  float* xf = reinterpret_cast<float*>(lds);  // two slots of [KV | z] fp32
+  constexpr int E = D * D + D;
+  auto put = [&](float* slot) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) slot[(i * 16 + g * 4 + r) * D + c * 16 + l16] = acc[i][c][r];
+      if (l16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) slot[D * D + i * 16 + g * 4 + r] = accz[i][r];
+      }
+    }
+  };
+  auto add = [&](const float* slot) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][c][r] += slot[(i * 16 + g * 4 + r) * D + c * 16 + l16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accz[i][r] += slot[D * D + i * 16 + g * 4 + r];
+    }
+  };
+  __syncthreads();  // every wave is done with its tile area
+  if (wave >= 2) put(xf + (wave - 2) * E);
   __syncthreads();
-  publish_state<D>(a, gr, kv_lds);
+  if (wave < 2) add(xf + wave * E);
+  __syncthreads();
+  if (wave == 1) put(xf);
+  __syncthreads();
+  if (wave == 0) {
+    add(xf);
+    float* dst = a.slices == 1 ? a.state + gr.g * E : a.partials + (gr.g * a.slices + gr.s) * E;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(i * 16 + g * 4 + r) * D + c * 16 + l16] = acc[i][c][r];
+      if (l16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[D * D + i * 16 + g * 4 + r] = accz[i][r];
+      }
+    }
+  }
 }
 
 // fp32 stage 1: tile of 64 tokens kept in natural layout (the fp32 MFMA takes one k value
@@ -238,13 +412,37 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a) {
 }
 
 // ----------------------------------------------------------------------------- stage 2
+// The head's fp32 [KV | z] as the sum of its `slices` parts in slice order (the same order as
+// state_reduce, so the sums are bitwise equal), thread tid taking float4 tid + 256 i of KV and,
+// for tid < D, z[tid].  The loads of each part are all issued before they are added.
+template <int D>
+__device__ __forceinline__ void head_state(const NcOutArgs& a, int64_t bh, int tid,
+                                           f32x4 (&kv4)[D * D / 1024], float& zv) {
+  constexpr int E = D * D + D;
+  constexpr int NKV4 = D * D / 1024;
+  const float* base = a.state + bh * a.slices * E;
+#pragma unroll
+  for (int i = 0; i < NKV4; ++i) kv4[i] = zero4();
+  zv = 0.f;
+  for (int64_t p = 0; p < a.slices; ++p) {
+    const float* st = base + p * E;
+    f32x4 part[NKV4];
+#pragma unroll
+    for (int i = 0; i < NKV4; ++i) part[i] = reinterpret_cast<const f32x4*>(st)[tid + 256 * i];
+    const float zp = tid < D ? st[D * D + tid] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NKV4; ++i) kv4[i] += part[i];
+    zv += zp;
+  }
+}
+
 // bf16 output.  The workgroup turns its head's fp32 [KV | z] into bf16 MFMA operands in LDS:
 // KVt[c][a] = KV[a][c], and a 16-row "normaliser" tile whose rows 0 and 1 hold z split into a
 // bf16 high part and a bf16 residual (so phi(q).z keeps ~16 significant bits).  Each wave then
 // takes 16 queries at a time and computes out^T = [KV^T ; z] phi(Q)^T with queries as the MFMA
 // column index: a lane's 16-byte load of a query row is directly its operand.
 template <int D>
-__global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void nc_out_bf16(NcOutArgs a) {
   constexpr int LD = D + 16;  // row stride of 8 mod 64 dwords: conflict-free 16-row reads
   constexpr int NC = D / 16;
   constexpr int KS = D / 32;
@@ -252,19 +450,47 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t KVt[D * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LD];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t tiles = (a.n + kNcQueries - 1) / kNcQueries;
   const int64_t bh = blockIdx.x / tiles;
-  const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * QPW;
-  const float* st = a.state + bh * (D * D + D);
+  const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * 16;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
+  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
 
-  // the head's fp32 state: every load issued before any is used (one memory latency)
-  constexpr int NKV4 = D * D / 4 / 256;
-  f32x4 kv4[NKV4];
+  // Queries go in batches: in batch b the four waves take consecutive runs of QPB queries.
+  // NS register sets keep the next NS - 1 batches in flight (the loop is unrolled by NS; the
+  // loads past the last batch re-read it, which costs no HBM traffic, so no load is
+  // conditional).  The first sets go out before the head's state is read, so the prologue
+  // overlaps their latency.
+  constexpr int BB = 1;                     // blocks of 16 queries per batch and wave
+  constexpr int QPB = 16 * BB;
+  constexpr int NBATCH = QPW / QPB;
+  constexpr int NS = D == 64 ? 4 : 2;
+  static_assert(NBATCH % NS == 0, "batches come in groups of NS");
+  auto batch_row = [&](int b) { return q0 + (int64_t)b * 4 * QPB; };
+  u32x4 qs[NS][BB][KS];
+  auto load = [&](int b, u32x4 (&q)[BB][KS]) {
+    const TileRows tr = tile_rows(batch_row(b < NBATCH ? b : NBATCH - 1), a.n, QPB);
+    const uint16_t* qt = Q + tr.first * D;
 #pragma unroll
-  for (int i = 0; i < NKV4; ++i) kv4[i] = reinterpret_cast<const f32x4*>(st)[tid + 256 * i];
-  const float zv = tid < D ? st[D * D + tid] : 0.f;
+    for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        q[bb][ks] = ld16_row(qt, bb * 16 + l16, tr.last, D, ks * 32 + g * 8);  // rows >= n are never stored
+  };
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {  // in order, as in kv_state_bf16
+    load(u, qs[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // the head's fp32 state -> bf16 operands in LDS
+  constexpr int NKV4 = D * D / 1024;
+  f32x4 kv4[NKV4];
+  float zv;
+  head_state<D>(a, bh, tid, kv4, zv);
 #pragma unroll
   for (int i = 0; i < NKV4; ++i) {
     const int e = (tid + 256 * i) * 4, ar = e / D, c = e % D;
@@ -282,31 +508,12 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
   }
   __syncthreads();
 
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
-  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
-
-  // query blocks of 16 rows go in batches of BB, the next batch in flight during compute
-  constexpr int BB = D == 64 ? 4 : 2;
-  constexpr int NBATCH = QPW / 16 / BB;
-  u32x4 qr[BB][KS];
-  auto load_batch = [&](int64_t r0) {
+  auto compute = [&](int b, const u32x4 (&q)[BB][KS]) {
 #pragma unroll
-    for (int b = 0; b < BB; ++b)
+    for (int bb = 0; bb < BB; ++bb) {
+      u32x4 qf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qr[b][ks] = ld16_clamp(Q, r0 + b * 16 + l16, a.n, D, ks * 32 + g * 8);  // rows >= n are never stored
-  };
-  load_batch(q0);
-  for (int bt = 0; bt < NBATCH; ++bt) {
-    u32x4 qf[BB][KS];
-#pragma unroll
-    for (int b = 0; b < BB; ++b)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[b][ks] = phi_bf16x8(qr[b][ks]);
-    if (bt + 1 < NBATCH) load_batch(q0 + (bt + 1) * 16 * BB);
-#pragma unroll
-    for (int b = 0; b < BB; ++b) {
-      const int64_t row = q0 + (bt * BB + b) * 16 + l16;
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = phi_bf16x8(q[bb][ks]);
       f32x4 acc[NC];
       f32x4 accd = zero4();
 #pragma unroll
@@ -315,20 +522,41 @@ __global__ __launch_bounds__(256) void nc_out_bf16(NcOutArgs a) {
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          acc[c] = mfma_bf16(ld16(&KVt[(c * 16 + l16) * LD + ks * 32 + g * 8]), qf[b][ks], acc[c]);
-        accd = mfma_bf16(ld16(&Zr[l16 * LD + ks * 32 + g * 8]), qf[b][ks], accd);
+          acc[c] = mfma_bf16(ld16(&KVt[(c * 16 + l16) * LD + ks * 32 + g * 8]), qf[ks], acc[c]);
+        accd = mfma_bf16(ld16(&Zr[l16 * LD + ks * 32 + g * 8]), qf[ks], accd);
       }
-      const float den = __shfl(accd[0] + accd[1], l16);
-      const float inv = 1.0f / den;
-      if (row < a.n) {
+      const float inv = __builtin_amdgcn_rcpf(__shfl(accd[0] + accd[1], l16));  // den > 0
+      // a lane holds 4 columns of each tile; rows g and g ^ 1 swap halves of tile pairs
+      // (v_permlane16_swap) so that each lane stores 8 consecutive columns
+      const int64_t r0 = batch_row(b);
+      uint16_t* ot = O + r0 * D;                                     // uniform tile base
+      const bool valid = (int64_t)(bb * 16 + l16) < a.n - r0;        // rows >= n are not stored
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          u32x2 o;
-          o.x = pack_bf16(acc[c][0] * inv, acc[c][1] * inv);
-          o.y = pack_bf16(acc[c][2] * inv, acc[c][3] * inv);
-          *reinterpret_cast<u32x2*>(O + row * D + c * 16 + g * 4) = o;
-        }
+      for (int c = 0; c < NC; c += 2) {
+        const auto sx = __builtin_amdgcn_permlane16_swap(pack_bf16(acc[c][0] * inv, acc[c][1] * inv),
+                                                         pack_bf16(acc[c + 1][0] * inv, acc[c + 1][1] * inv),
+                                                         false, false);
+        const auto sy = __builtin_amdgcn_permlane16_swap(pack_bf16(acc[c][2] * inv, acc[c][3] * inv),
+                                                         pack_bf16(acc[c + 1][2] * inv, acc[c + 1][3] * inv),
+                                                         false, false);
+        u32x4 o;
+        o.x = sx[0];
+        o.y = sy[0];
+        o.z = sx[1];
+        o.w = sy[1];
+        if (valid)
+          st16(reinterpret_cast<char*>(ot) +
+                   (uint32_t)(((bb * 16 + l16) * D + (c + (g & 1)) * 16 + 8 * (g >> 1)) * 2), o);
       }
+    }
+  };
+  for (int b = 0; b < NBATCH; b += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      compute(b + u, qs[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      load(b + u + NS, qs[u]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -349,11 +577,10 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   const int64_t tiles = (a.n + kNcQueries - 1) / kNcQueries;
   const int64_t bh = blockIdx.x / tiles;
   const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * QPW;
-  const float* st = a.state + bh * (D * D + D);
-  constexpr int NKV4 = D * D / 4 / 256;
+  constexpr int NKV4 = D * D / 1024;
   f32x4 kv4[NKV4];
-#pragma unroll
-  for (int i = 0; i < NKV4; ++i) kv4[i] = reinterpret_cast<const f32x4*>(st)[tid + 256 * i];
+  float zv;
+  head_state<D>(a, bh, tid, kv4, zv);
 #pragma unroll
   for (int i = 0; i < NKV4; ++i) {
     const int e = (tid + 256 * i) * 4, ar = e / D, c = e % D;
@@ -362,7 +589,7 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
     KVt[(c + 2) * LD + ar] = kv4[i].z;
     KVt[(c + 3) * LD + ar] = kv4[i].w;
   }
-  if (tid < D) zs[tid] = st[D * D + tid];
+  if (tid < D) zs[tid] = zv;
   __syncthreads();
 
   const float* Q = reinterpret_cast<const float*>(a.q) + bh * a.n * D;
@@ -403,7 +630,9 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
 template <int D>
 static hipError_t launch_kv_state_t(const KvStateArgs& a, int dtype, hipStream_t s) {
   const int64_t blocks = a.groups * a.slices;
-  if (dtype == 1)
+  if (dtype == 1 && D == 64)
+    hipLaunchKernelGGL(kv_state_bf16_waves<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else if (dtype == 1)
     hipLaunchKernelGGL(kv_state_bf16<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(kv_state_f32<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);

@@ -143,7 +143,7 @@ def test_causal_plan_and_stage_validation():
     assert ss(sums=0x80004) == -5
     assert ss(sums=0x2000) == -7
     assert ss(n=0, k=0) == 0
-    assert ea.la_state_sums_workspace_bytes(1, 1, 1000, 64, 1, 100, 3) == 0       # one slice each
+    assert ea.la_state_sums_workspace_bytes(1, 1, 1000, 64, 1, 50, 3) == 0        # one tile, one slice each
     assert ea.la_state_sums_workspace_bytes(1, 1, 100000, 64, 1, 50000, 2) > 0    # split slices
     # la_causal_segments
     cs = lambda **kw: lib.la_causal_segments(P(kw.get("q", 0x1000)), P(0x2000), P(0x3000), P(kw.get("out", 0x4000)),
