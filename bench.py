@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "tokens/sec + HBM GB/s (% peak), linear-attn fwd n=16K/64K, d=64/128, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "causal_bf16_d128_c128_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "causal_bf16_d128_c128_traffic.txt")
 ROOFLINE_SOURCES = ["efficient_attention_amd/csrc/la_causal.hip", "efficient_attention_amd/csrc/la_common.h"]
 
 
@@ -58,12 +58,13 @@ def measured_traffic():
     or None when absent or taken on different kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            t = dict(line.split(": ", 1) for line in f.read().splitlines()
+                     if line and not line.startswith("#") and ": " in line)
+        if t.get("source_sha256") != source_digest():
+            return None
+        return int(t["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
         return None
-    if t.get("source_sha256") != source_digest():
-        return None
-    return t.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
@@ -204,6 +205,35 @@ def main():
     stage_ms = {s: float(np.mean([evs[t][i].elapsed_time(evs[t][i + 1]) for t in range(args.steps)]))
                 for i, s in enumerate(stages)}
 
+    # Each stage alone as well, after evicting the caches with a 2 GiB read (which leaves no
+    # dirty lines behind): inside the step a stage also pays for writing back the previous
+    # stage's outputs (the decode step rewrites its 512 MiB state just before the non-causal
+    # stage of the next step), which the per-kernel bandwidth should not include.
+    log("isolated stages")
+    flush = torch.ones(1 << 28, dtype=torch.float64, device=dev)
+
+    def isolated(fn, reps=5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(reps):
+            flush.sum()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    iso_ms = {
+        "noncausal": isolated(lambda: ea.la_forward_noncausal(Q3, K3, V3, out=O3)),
+        "causal_state_sums": isolated(lambda: ea.la_state_sums(K4, V4, seg_len, nseg - 1, sums=sums4))
+        if nseg > 1 else 0.0,
+        "causal_chunked": isolated(lambda: ea.la_causal_segments(Q4, K4, V4, sums4 if nseg > 1 else None,
+                                                                 seg_len, C4.chunk, out=O4)),
+        "decode_step": isolated(lambda: ea.la_decode_step(DQ[0], DK[0], DV[0], S5, Z5, out=O5)),
+    }
+    del flush
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
@@ -219,17 +249,28 @@ def main():
     def gbs(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
 
+    iso_c4 = iso_ms["causal_state_sums"] + iso_ms["causal_chunked"]
+
+    def pct(nbytes, ms):
+        return 100 * gbs(nbytes, ms) / HBM_PEAK_GBS
+
+    # "ms"/"pct_hbm_peak": inside the timed steps; "isolated_*": the stage alone, caches evicted
     breakdown = {
         "noncausal_C3": {"ms": stage_ms["noncausal"], "tokens_per_s": C3.B * C3.n / (stage_ms["noncausal"] * 1e-3),
                          "algorithmic_GBps": gbs(b3, stage_ms["noncausal"]),
-                         "pct_hbm_peak": 100 * gbs(b3, stage_ms["noncausal"]) / HBM_PEAK_GBS},
+                         "pct_hbm_peak": pct(b3, stage_ms["noncausal"]),
+                         "isolated_ms": iso_ms["noncausal"], "isolated_pct_hbm_peak": pct(b3, iso_ms["noncausal"])},
         "causal_C4": {"ms": c4_ms, "state_sums_ms": stage_ms["causal_state_sums"],
                       "chunked_ms": stage_ms["causal_chunked"], "segments_per_head": nseg,
                       "tokens_per_s": C4.B * C4.n / (c4_ms * 1e-3),
-                      "algorithmic_GBps": gbs(b4, c4_ms), "pct_hbm_peak": 100 * gbs(b4, c4_ms) / HBM_PEAK_GBS},
+                      "algorithmic_GBps": gbs(b4, c4_ms), "pct_hbm_peak": pct(b4, c4_ms),
+                      "isolated_ms": iso_c4, "isolated_state_sums_ms": iso_ms["causal_state_sums"],
+                      "isolated_chunked_ms": iso_ms["causal_chunked"], "isolated_pct_hbm_peak": pct(b4, iso_c4),
+                      "isolated_chunked_pct_hbm_peak": pct(b4, iso_ms["causal_chunked"])},
         "decode_C5": {"ms": stage_ms["decode_step"], "tokens_per_s": C5.B / (stage_ms["decode_step"] * 1e-3),
                       "algorithmic_GBps": gbs(b5, stage_ms["decode_step"]),
-                      "pct_hbm_peak": 100 * gbs(b5, stage_ms["decode_step"]) / HBM_PEAK_GBS},
+                      "pct_hbm_peak": pct(b5, stage_ms["decode_step"]),
+                      "isolated_ms": iso_ms["decode_step"], "isolated_pct_hbm_peak": pct(b5, iso_ms["decode_step"])},
     }
     # dominant kernel: the chunked causal kernel (one launch per la_causal_segments call)
     ach = gbs(b4, stage_ms["causal_chunked"])
