@@ -6,9 +6,10 @@
 //     KV = sum_j phi(k_j) v_j^T  (D x d),  z = sum_j phi(k_j)  (D),
 //     out_i = phi(q_i) KV / phi(q_i) z.
 // Because the sums split over any partition of the keys (associativity, section "Worked
-// example"), stage 1 sums slices of keys in parallel and the last workgroup of each group
-// adds the slices in a fixed order (deterministic, no float atomics); stage 2 streams the
-// queries.
+// example"), stage 1 sums slices of keys in parallel into per-slice partials; whoever needs a
+// group's state adds its slices in a fixed order (deterministic, no float atomics): the
+// output kernel's prologue, state_reduce, or the causal kernel's prologue.  Stage 2 streams
+// the queries.
 //
 // Kernels
 //   kv_state_*   stage 1.  Grid = groups x slices (1-D).  A group is a contiguous token range
