@@ -465,9 +465,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
   const int l16 = lane & 15, g = lane >> 4;
   const int prow = lane / BPR, pblk = lane % BPR;              // this lane's row / block of an access
+  // Workgroups go to the 8 XCDs round-robin.  When the heads come in multiples of 8, workgroup
+  // b = 8 j + x (on XCD x) takes tile j % tiles of head 8 (j / tiles) + x: all tiles of a head
+  // run on one XCD, whose L2 then serves the head's partial states to all of them.  (Giving
+  // each XCD a contiguous block of heads instead measured slower.)
   const int64_t tiles = (a.n + kNcQueries - 1) / kNcQueries;
-  const int64_t bh = blockIdx.x / tiles;
-  const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * 16;
+  int64_t bh, tile;
+  if (a.bh % 8 == 0) {
+    const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+    bh = (j / tiles) * 8 + x;
+    tile = j % tiles;
+  } else {
+    bh = blockIdx.x / tiles;
+    tile = blockIdx.x % tiles;
+  }
+  const int64_t q0 = tile * kNcQueries + wave * 16;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
   uint16_t* Qs = stage + wave * 2 * ST;  // phi(Q) tile
@@ -481,8 +493,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // Queries go in batches: in batch b the four waves take consecutive runs of 16 queries.
   // NS register sets keep the next NS - 1 batches in flight (the loop is unrolled by NS; the
   // loads past the last batch re-read it, which costs no HBM traffic, so no load is
-  // conditional).  The first sets go out before the head's state is read, so the prologue
-  // overlaps their latency.
+  // conditional).  Every workgroup starts at once and first waits for its head's state, so
+  // the state is read first, ahead of the query sets in the memory queue; the first query
+  // sets then load while the state is converted.
   constexpr int NBATCH = QPW / 16;
   constexpr int NS = D == 64 ? 4 : 2;
   static_assert(NBATCH % NS == 0, "batches come in groups of NS");
@@ -494,17 +507,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
     for (int i = 0; i < KS; ++i) q[i] = ld16_row(qt, i * RPI + prow, tr.last, D, pblk * 8);  // rows >= n are never stored
   };
-#pragma unroll
-  for (int u = 0; u < NS; ++u) {  // in order, as in kv_state_bf16
-    load(u, qs[u]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
   // the head's fp32 state -> bf16 operands in LDS
   constexpr int NKV4 = D * D / 1024;
   f32x4 kv4[NKV4];
   float zv;
   head_state<D>(a, bh, tid, kv4, zv);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {  // in order, as in kv_state_bf16
+    load(u, qs[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int i = 0; i < NKV4; ++i) {
     const int e = (tid + 256 * i) * 4, ar = e / D, c = e % D;

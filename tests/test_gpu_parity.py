@@ -135,6 +135,20 @@ def test_shape_sweep(ea, form, dtype, d, n, chunk):
     assert e <= TOL[dtype], e
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,n", [(2, 8, 5000), (1, 8, 4113), (3, 8, 2048)])
+def test_noncausal_heads_in_multiples_of_8(ea, d, B, H, n):
+    # B*H a multiple of 8 takes the output kernel's head-per-XCD workgroup order; several query
+    # tiles per head, the last one ragged
+    q, k, v = random_inputs(zlib.crc32(repr(("nc8", d, B, H, n)).encode()) % 100000, (B, H, n, d), "bf16",
+                            1.0 / np.sqrt(d))
+    say("noncausal bf16 B=%d H=%d n=%d d=%d" % (B, H, n, d))
+    g = run_forward(ea, "noncausal", q, k, v, "bf16", 64)
+    ref = oracle_forward("noncausal", q, k, v, "bf16")
+    e = normwise_err(g, ref)
+    assert e <= TOL["bf16"], e
+
+
 @pytest.mark.parametrize("dtype,d,chunk", [("bf16", 64, 64), ("bf16", 128, 128), ("f32", 64, 64),
                                            ("bf16", 64, 128), ("bf16", 128, 64), ("f32", 128, 64)])
 def test_causal_many_segments_ragged(ea, dtype, d, chunk):
