@@ -207,7 +207,7 @@ def main():
 
     # Each stage alone as well, after evicting the caches with a 2 GiB read (which leaves no
     # dirty lines behind): inside the step a stage also pays for writing back the previous
-    # stage's outputs (the decode step rewrites its 512 MiB state just before the non-causal
+    # stage's outputs (the decode step rewrites its 516 MiB state just before the non-causal
     # stage of the next step), which the per-kernel bandwidth should not include.
     log("isolated stages")
     flush = torch.ones(1 << 28, dtype=torch.float64, device=dev)

@@ -66,7 +66,6 @@ StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
 
 size_t state_bytes(int64_t groups, int d) { return (size_t)groups * (size_t)(d * d + d) * sizeof(float); }
 
-// Non-causal workspace: [partials][states].
 // Non-causal workspace: the per-slice partials (summed by the output kernel), or the states
 // themselves when every head has one slice.
 size_t nc_ws_bytes(const StatePlan& p, int d) {
