@@ -232,6 +232,15 @@ def main():
                                                                  seg_len, C4.chunk, out=O4)),
         "decode_step": isolated(lambda: ea.la_decode_step(DQ[0], DK[0], DV[0], S5, Z5, out=O5)),
     }
+    # the causal forward continuing from a state and handing on the final one (a prefill that
+    # feeds a decode): C4 from the state of 1024 earlier tokens (their sums), final state written
+    st4 = ea.la_state_sums(K4[:, :, :1024].contiguous(), V4[:, :, :1024].contiguous(), 1024, 1)
+    S4in = st4[:, :, 0, : C4.d * C4.d].reshape(C4.B, C4.H, C4.d, C4.d).contiguous()
+    Z4in = st4[:, :, 0, C4.d * C4.d:].contiguous()
+    S4out, Z4out = torch.empty_like(S4in), torch.empty_like(Z4in)
+    del st4
+    iso_ms["causal_state_io"] = isolated(lambda: ea.la_forward_causal_state(
+        Q4, K4, V4, C4.chunk, S4in, Z4in, out=O4, Sn=S4out, zn=Z4out))
     del flush
 
     if args.copy_calibration:
@@ -267,6 +276,11 @@ def main():
                       "isolated_ms": iso_c4, "isolated_state_sums_ms": iso_ms["causal_state_sums"],
                       "isolated_chunked_ms": iso_ms["causal_chunked"], "isolated_pct_hbm_peak": pct(b4, iso_c4),
                       "isolated_chunked_pct_hbm_peak": pct(b4, iso_ms["causal_chunked"])},
+        "causal_C4_state_in_out": {
+            "isolated_ms": iso_ms["causal_state_io"],
+            "isolated_pct_hbm_peak": pct(b4 + 2 * C4.B * C4.H * (C4.d * C4.d + C4.d) * 4, iso_ms["causal_state_io"]),
+            "note": "la_forward_causal_state on C4 from a given (S0, z0), final state written; "
+                    "compare causal_C4.isolated_ms"},
         "decode_C5": {"ms": stage_ms["decode_step"], "tokens_per_s": C5.B / (stage_ms["decode_step"] * 1e-3),
                       "algorithmic_GBps": gbs(b5, stage_ms["decode_step"]),
                       "pct_hbm_peak": pct(b5, stage_ms["decode_step"]),

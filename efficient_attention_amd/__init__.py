@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     la_causal_workspace_bytes,
     la_decode_step,
     la_forward_causal,
+    la_forward_causal_state,
     la_forward_noncausal,
     la_noncausal_workspace_bytes,
     la_state_sums,

@@ -23,7 +23,7 @@ LA_OK = 0
 EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
            "la_forward_noncausal", "la_causal_workspace_bytes", "la_forward_causal",
            "la_causal_plan", "la_state_sums_workspace_bytes", "la_state_sums",
-           "la_causal_segments", "la_decode_step")
+           "la_causal_segments", "la_decode_step", "la_forward_causal_state")
 
 _lib = None
 _lock = threading.Lock()
@@ -60,6 +60,8 @@ def load():
         lib.la_causal_workspace_bytes.restype = SZ
         lib.la_forward_causal.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
         lib.la_forward_causal.restype = I
+        lib.la_forward_causal_state.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
+        lib.la_forward_causal_state.restype = I
         lib.la_causal_plan.argtypes = [I64, I64, I64, I64, I64, I, ctypes.POINTER(I64)]
         lib.la_causal_plan.restype = I
         lib.la_state_sums_workspace_bytes.argtypes = [I64, I64, I64, I64, I, I64, I64]
@@ -183,6 +185,42 @@ def la_forward_causal(q, k, v, chunk: int = 128, out=None, ws=None, stream=None)
     if st != LA_OK:
         raise LinAttnError(st, "la_forward_causal")
     return out
+
+
+def la_forward_causal_state(q, k, v, chunk: int = 128, S0=None, z0=None, out=None, Sn=None, zn=None,
+                            final_state: bool = True, ws=None, stream=None):
+    """Causal forward continuing from the state (S0 [B, H, d, d], z0 [B, H, d], fp32; None for
+    the zero state).  Returns (out, Sn, zn) with the state after the last token (allocated
+    unless given), or (out, None, None) when final_state is False."""
+    _check_qkv(q, k, v, 4)
+    B, H, n, d = q.shape
+    if (S0 is None) != (z0 is None):
+        raise ValueError("give both S0 and z0, or neither")
+    if final_state:
+        if Sn is None:
+            Sn = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+        if zn is None:
+            zn = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    else:
+        Sn = zn = None
+    for name, t, shape in (("S0", S0, (B, H, d, d)), ("z0", z0, (B, H, d)),
+                           ("Sn", Sn, (B, H, d, d)), ("zn", zn, (B, H, d))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape
+                              or not t.is_contiguous() or t.device != q.device):
+            raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s" % (name, shape, q.device))
+    out = _out_like(q, out)
+    code = _dtype_code(q)
+    sh = _stream_handle(q.device, stream)
+    need = la_causal_workspace_bytes(B, H, n, d, chunk, code)
+    if ws is None:
+        ws = workspace(need, q.device, sh)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = load().la_forward_causal_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        ptr(S0), ptr(z0), ptr(Sn), ptr(zn), B, H, n, d, chunk, code,
+                                        ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_forward_causal_state")
+    return out, Sn, zn
 
 
 def la_decode_step(q, k, v, S, z, out=None, stream=None):

@@ -263,6 +263,8 @@ int la_causal_segments(const void* q, const void* k, const void* v, void* out,
   ca.out = out;
   ca.seg_state = segs > 1 ? sums : nullptr;
   ca.seg_parts = 1;
+  ca.s0 = ca.z0 = nullptr;
+  ca.sn = ca.zn = nullptr;
   ca.n = n;
   ca.bh = bh;
   ca.segs = segs;
@@ -276,11 +278,46 @@ int la_causal_segments(const void* q, const void* k, const void* v, void* out,
 int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream) {
+  return la_forward_causal_state(q, k, v, out, nullptr, nullptr, nullptr, nullptr, B, H, n, d,
+                                 chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int la_forward_causal_state(const void* q, const void* k, const void* v, void* out,
+                            const float* S0, const float* z0, float* Sn, float* zn, int64_t B,
+                            int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
   int st = check_causal(B, H, n, d, chunk, dtype, &bh, &bytes);
   if (st != LA_OK) return st;
-  if (bh == 0 || n == 0) return LA_OK;
+  if (!S0 != !z0 || !Sn != !zn) return LA_ERR_NULL;  // each state is given whole or not at all
+  if (bh == 0) return LA_OK;
+  const size_t sbytes = (size_t)bh * (size_t)(d * d) * sizeof(float);
+  const size_t zbytes = (size_t)bh * (size_t)d * sizeof(float);
+  if ((S0 && (!aligned16(S0) || !aligned16(z0))) || (Sn && (!aligned16(Sn) || !aligned16(zn))))
+    return LA_ERR_ALIGN;
+  if (Sn && (overlaps(Sn, sbytes, zn, zbytes) || overlaps(Sn, sbytes, S0, sbytes) ||
+             overlaps(Sn, sbytes, z0, zbytes) || overlaps(zn, zbytes, S0, sbytes) ||
+             overlaps(zn, zbytes, z0, zbytes)))
+    return LA_ERR_ALIAS;
+  la::CausalArgs ca;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.out = out;
+  ca.seg_state = nullptr;
+  ca.seg_parts = 1;
+  ca.s0 = S0;
+  ca.z0 = z0;
+  ca.sn = Sn;
+  ca.zn = zn;
+  ca.n = n;
+  ca.bh = bh;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (n == 0) {  // no tokens: the final state is the initial one
+    if (Sn && la::launch_state_copy(ca, (int)d, s) != hipSuccess) return LA_ERR_HIP;
+    return LA_OK;
+  }
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   const int64_t seg_len = causal_seg_len(bh, n, chunk);
@@ -294,19 +331,18 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
     if (!aligned16(workspace)) return LA_ERR_ALIGN;
   }
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need) ||
+      overlaps(out, bytes, S0, sbytes) || overlaps(out, bytes, z0, zbytes) ||
+      overlaps(out, bytes, Sn, sbytes) || overlaps(out, bytes, zn, zbytes))
+    return LA_ERR_ALIAS;
+  if (Sn && (overlaps(Sn, sbytes, q, bytes) || overlaps(Sn, sbytes, k, bytes) ||
+             overlaps(Sn, sbytes, v, bytes) || overlaps(Sn, sbytes, workspace, need) ||
+             overlaps(zn, zbytes, q, bytes) || overlaps(zn, zbytes, k, bytes) ||
+             overlaps(zn, zbytes, v, bytes) || overlaps(zn, zbytes, workspace, need)))
+    return LA_ERR_ALIAS;
+  if (S0 && (overlaps(S0, sbytes, workspace, need) || overlaps(z0, zbytes, workspace, need)))
     return LA_ERR_ALIAS;
   if (!grid_ok(bh * segs) || (segs > 1 && !grid_ok(p.groups * p.slices))) return LA_ERR_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  la::CausalArgs ca;
-  ca.q = q;
-  ca.k = k;
-  ca.v = v;
-  ca.out = out;
-  ca.seg_state = nullptr;
-  ca.seg_parts = 1;
-  ca.n = n;
-  ca.bh = bh;
   ca.segs = segs;
   ca.seg_len = seg_len;
   if (segs > 1) {

@@ -11,8 +11,10 @@
 //
 // Work split.  One workgroup walks one segment of one head chunk by chunk; a head is cut into
 // `segs` segments so that short batches still fill the GPU.  The state entering segment s is
-// the sum of the leading segments' state sums, computed beforehand by the stage-1 kernel of
-// la_noncausal.hip (any partition of the keys gives the same sums).
+// the state before the sequence (zero, or a caller's (S0, z0)) plus the leading segments'
+// state sums, computed beforehand by the stage-1 kernel of la_noncausal.hip (any partition of
+// the keys gives the same sums).  The workgroup of the last segment can write the state after
+// the last token: the recurrence's state, handed on to a later call or to the decode step.
 #include "la_common.h"
 #include "la_kernels.h"
 
@@ -103,6 +105,16 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
 #pragma unroll
     for (int j = 0; j < NCW; ++j) accS[i][j] = zero4();
   float zinit = 0.f;
+  if (a.s0) {  // the state before the sequence
+    const float* s0 = a.s0 + bh * D * D;
+#pragma unroll
+    for (int i = 0; i < NAW; ++i)
+#pragma unroll
+      for (int j = 0; j < NCW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accS[i][j][r] = s0[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16];
+    if (tid < D) zinit = a.z0[bh * D + tid];
+  }
   // per leading segment: add its parts in order, then add the segment (the same grouping as
   // la_state_sums followed by la_causal_segments, so both paths round identically)
   for (int64_t s = 0; s < seg; ++s) {
@@ -370,6 +382,23 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
       }
     }
   }
+
+  // the state after the last token, from the last segment's workgroup
+  if (a.sn && seg == a.segs - 1) {
+    float* sn = a.sn + bh * D * D;
+#pragma unroll
+    for (int i = 0; i < NAW; ++i)
+#pragma unroll
+      for (int j = 0; j < NCW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sn[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16] = accS[i][j][r];
+    if (zown && l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < NAW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.zn[bh * D + (sa0 + i) * 16 + g * 4 + r] = accz[i][r];
+    }
+  }
 }
 
 // fp32 kernel (no bf16 rounding anywhere).  The fp32 MFMA takes one k value per lane, so every
@@ -404,6 +433,16 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a) {
 #pragma unroll
     for (int p = 0; p < NCW; ++p) accS[at][p] = zero4();
   float zinit = 0.f;
+  if (a.s0) {  // the state before the sequence
+    const float* s0 = a.s0 + bh * D * D;
+#pragma unroll
+    for (int at = 0; at < NA; ++at)
+#pragma unroll
+      for (int p = 0; p < NCW; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accS[at][p][r] = s0[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
+    if (tid < D) zinit = a.z0[bh * D + tid];
+  }
   for (int64_t s = 0; s < seg; ++s) {      // same grouping as in the bf16 kernel
     f32x4 part[NA][NCW];
     float zpart = 0.f;
@@ -521,6 +560,44 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a) {
     }
     __syncthreads();  // before the next chunk overwrites the tiles
   }
+
+  // the state after the last token, from the last segment's workgroup
+  if (a.sn && seg == a.segs - 1) {
+    float* sn = a.sn + bh * D * D;
+#pragma unroll
+    for (int at = 0; at < NA; ++at)
+#pragma unroll
+      for (int p = 0; p < NCW; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sn[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16] = accS[at][p][r];
+    if (tid < D) a.zn[bh * D + tid] = zf[tid];
+  }
+}
+
+// The final state of an empty sequence is the initial one: sn, zn = s0, z0 (or zeros).  One
+// float4 per thread, grid-stride over all heads.
+template <int D>
+__global__ __launch_bounds__(256) void state_copy(CausalArgs a) {
+  constexpr int64_t S4 = D * D / 4, Z4 = D / 4;
+  const int64_t total = a.bh * (S4 + Z4);
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    if (e < a.bh * S4) {
+      reinterpret_cast<f32x4*>(a.sn)[e] = a.s0 ? reinterpret_cast<const f32x4*>(a.s0)[e] : zero4();
+    } else {
+      const int64_t f = e - a.bh * S4;
+      reinterpret_cast<f32x4*>(a.zn)[f] = a.z0 ? reinterpret_cast<const f32x4*>(a.z0)[f] : zero4();
+    }
+  }
+}
+
+hipError_t launch_state_copy(const CausalArgs& a, int d, hipStream_t s) {
+  const int64_t total = a.bh * (d * d + d) / 4;
+  const int64_t blocks = total / 256 + 1 < 4096 ? total / 256 + 1 : 4096;
+  if (d == 64)
+    hipLaunchKernelGGL(state_copy<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(state_copy<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int D, int C>

@@ -38,6 +38,10 @@ struct CausalArgs {
   const float* seg_state;  // [bh][segs-1][seg_parts][D*D + D]: the leading segments' sums,
                            // each split into seg_parts partials that add up to it (or null)
   int64_t seg_parts;
+  const float* s0;         // [bh][D][D] state before token 0 and its key sums z0 [bh][D]
+  const float* z0;         //   (both null: zero state)
+  float* sn;               // [bh][D][D] and [bh][D]: receive the state after token n-1
+  float* zn;               //   (both null: not written)
   int64_t n;
   int64_t bh;
   int64_t segs;            // segments per head
@@ -59,6 +63,8 @@ hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s);
 hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s);
 hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
+// sn, zn = s0, z0 (zeros where s0, z0 are null) for every head: the final state of an empty sequence.
+hipError_t launch_state_copy(const CausalArgs& a, int d, hipStream_t s);
 
 // Queries per workgroup of the non-causal output kernel (4 waves x 512).
 constexpr int64_t kNcQueries = 2048;

@@ -25,7 +25,8 @@
  *
  * Errors.  Every entry point validates its arguments before launching anything and
  * returns LA_OK or a negative LA_ERR_* code; on an error nothing is written.  Empty
- * shapes (B*H*n == 0) are successful no-ops.  Kernels run asynchronously on `stream`:
+ * shapes (B*H*n == 0) are successful no-ops (except that la_forward_causal_state with n = 0
+ * still hands on the state).  Kernels run asynchronously on `stream`:
  * results are valid after the caller synchronises.  A launch failure returns LA_ERR_HIP.
  * Inputs whose phi underflows to zero for every feature (entries below about -87 in fp32)
  * give the IEEE result of 0/0, as the formula would.
@@ -103,6 +104,27 @@ size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
 int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal forward that continues from a given state and hands on the final one (the prefill
+ * side of a decode, or one piece of a sequence cut into pieces): with (S0, z0) the state
+ * before token 0 ("The recurrent view": S_t = S_{t-1} + phi(k_t) v_t^T from S_{-1} = S0),
+ *     out_i = phi(q_i)^T (S0 + sum_{j<=i} phi(k_j) v_j^T) / phi(q_i)^T (z0 + sum_{j<=i} phi(k_j))
+ * and (Sn, zn) receive S0 + sum_j phi(k_j) v_j^T and z0 + sum_j phi(k_j) over all n tokens.
+ * Running the pieces of a sequence in order, each from the previous piece's final state,
+ * gives the outputs and final state of one call over the whole sequence (up to rounding).
+ *   S0, z0 : [B][H][d][d] and [B][H][d] fp32, read only; both NULL for the zero state
+ *   Sn, zn : [B][H][d][d] and [B][H][d] fp32, written; both NULL to skip.  They must not
+ *            overlap any other argument (no update in place of S0, z0): the final state is
+ *            written while other workgroups may still read the initial one.
+ *   other arguments and the workspace: as for la_forward_causal, which is this call with
+ *   all four state pointers NULL.  With n = 0 the call writes Sn, zn = S0, z0 (zeros when
+ *   S0 is NULL) and reads no other tensor.  Giving only one pointer of a pair is LA_ERR_NULL.
+ */
+int la_forward_causal_state(const void* q, const void* k, const void* v, void* out,
+                            const float* S0, const float* z0, float* Sn, float* zn, int64_t B,
+                            int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The two stages of la_forward_causal, callable on their own (a caller can time them apart,

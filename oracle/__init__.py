@@ -87,7 +87,8 @@ def _heads(x):
     """View [..., n, d] as [BH, n, d]."""
     x = _f64(x)
     n, d = x.shape[-2], x.shape[-1]
-    return x.reshape(-1, n, d), x.shape
+    bh = int(np.prod(x.shape[:-2], dtype=np.int64))  # explicit, so that n = 0 works too
+    return x.reshape(bh, n, d), x.shape
 
 
 def phi(x, feature_map: int = PHI_ELU1):

@@ -111,6 +111,28 @@ def test_validation_causal():
     assert _ca(lib, out=0x2000) == -7
 
 
+def _cs(lib, q=0x1000, k=0x2000, v=0x3000, out=0x4000, S0=0, z0=0, Sn=0, zn=0, B=1, H=1, n=8, d=64,
+        chunk=64, dtype=1, ws=0x100000, wsb=1 << 30):
+    return lib.la_forward_causal_state(P(q), P(k), P(v), P(out), P(S0 or None), P(z0 or None), P(Sn or None),
+                                       P(zn or None), B, H, n, d, chunk, dtype, P(ws), wsb, None)
+
+
+def test_validation_causal_state():
+    lib = _lib()
+    S, Z = 0x200000, 0x300000
+    assert _cs(lib, S0=S) == -1                                # z0 missing
+    assert _cs(lib, Sn=S) == -1                                # zn missing
+    assert _cs(lib, S0=S, z0=Z, Sn=S, zn=Z + 0x40000) == -7    # final state over the initial one
+    assert _cs(lib, Sn=S, zn=S + 0x100) == -7                  # Sn and zn overlap
+    assert _cs(lib, Sn=S + 4, zn=Z) == -5                      # misaligned
+    assert _cs(lib, Sn=S, zn=Z, out=S) == -7                   # out over the final state
+    assert _cs(lib, Sn=S, zn=Z, k=Z) == -7                     # final state over an input
+    assert _cs(lib, S0=S, z0=Z, out=Z) == -7                   # out over the initial state
+    assert _cs(lib, B=0, S0=S) == -1                           # pairs are checked first
+    assert _cs(lib, B=0, Sn=S, zn=Z) == 0                      # no heads: nothing to write
+    assert _cs(lib, chunk=96, Sn=S, zn=Z) == -4
+
+
 def test_validation_decode():
     lib = _lib()
     assert _dec(lib, dtype=5) == -3

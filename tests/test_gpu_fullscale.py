@@ -124,3 +124,46 @@ def test_c5_decode_full(ea):
         zref = z0[b].astype(np.float64) + za
         assert normwise_err(Sg[b], Sref) <= 1e-4
         assert normwise_err(zg[b], zref, head_axes_last=1) <= 1e-5
+
+
+def test_c4_causal_in_two_pieces_with_state(ea):
+    # C4 run as two calls, the second continuing from the first one's final state (cut inside
+    # a chunk): sampled rows against the quadratic definition over the whole sequence, the
+    # outputs against the one-call forward, and the final state of every head against the
+    # fp64 sum over all tokens
+    import torch
+    w = WORKLOADS["C4"]
+    say("C4 pieces generating inputs")
+    q, k, v = forward_inputs(w)
+    tq, tk, tv = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype)
+    cut = 40000
+    say("C4 pieces GPU runs")
+    a, S1, z1 = ea.la_forward_causal_state(tq[:, :, :cut].contiguous(), tk[:, :, :cut].contiguous(),
+                                           tv[:, :, :cut].contiguous(), w.chunk)
+    b_, S2, z2 = ea.la_forward_causal_state(tq[:, :, cut:].contiguous(), tk[:, :, cut:].contiguous(),
+                                            tv[:, :, cut:].contiguous(), w.chunk, S1, z1)
+    g = np.concatenate([from_dev(a, w.dtype), from_dev(b_, w.dtype)], axis=2)
+    del a, b_
+    assert np.all(np.isfinite(g))
+    say("C4 pieces vs one call")
+    whole = from_dev(ea.la_forward_causal(tq, tk, tv, chunk=w.chunk), w.dtype)
+    e = normwise_err(g, whole)
+    print("C4 two pieces vs one call normwise err %.3e" % e)
+    assert e <= TOL_BF16
+    rng = np.random.default_rng(11)
+    extra = [0, cut - 1, cut, cut + 1, w.n - 1]
+    for _ in range(6):
+        b, h = int(rng.integers(0, w.B)), int(rng.integers(0, w.H))
+        rows = _sample_rows(w.n, extra, rng)
+        say("C4 pieces oracle rows", b, h, len(rows))
+        Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
+        ref = oracle.rows(Q, K, V, rows, causal=True)
+        assert normwise_err(g[b, h][rows][None], ref[None]) <= TOL_BF16
+    say("C4 pieces final state of every head")
+    Sg, zg = S2.cpu().numpy(), z2.cpu().numpy()
+    worst = 0.0
+    for b in range(w.B):
+        Sa, za = oracle.state_from_tokens_matmul(f64(k[b], w.dtype), f64(v[b], w.dtype))
+        worst = max(worst, normwise_err(Sg[b], Sa), normwise_err(zg[b], za, head_axes_last=1))
+    print("C4 final state normwise err %.3e" % worst)
+    assert worst <= TOL_BF16

@@ -303,6 +303,125 @@ def test_decode_resume_bitwise(ea):
 
 
 # ----------------------------------------------------------------------------- causal stages
+# ----------------------------------------------------------------------------- causal with state in/out
+def _state_err(g, r):
+    """Normwise error per head of [B, H, d, d] (or [B, H, d]) states."""
+    return normwise_err(g, r, head_axes_last=2 if np.ndim(r) == 4 else 1)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 64, 128),
+                                           ("bf16", 128, 64), ("f32", 64, 64), ("f32", 128, 64)])
+def test_causal_state_vs_oracle(ea, dtype, d, chunk):
+    # out and final state from an initial state built from prior tokens; few heads, so the
+    # sequence is cut into segments (the state enters every segment)
+    import torch
+    B, H, prior, n = 2, 3, 90, 700
+    scale = 1.0 if dtype == "f32" else 1.0 / np.sqrt(d)
+    pk, pv, _ = random_inputs(40 + d + chunk, (B, H, prior, d), dtype, scale)
+    q, k, v = random_inputs(41 + d + chunk, (B, H, n, d), dtype, scale)
+    S0, z0 = _state_from_prior(pk, pv, dtype)
+    say("causal state in/out", dtype, d, chunk)
+    out, Sn, zn = ea.la_forward_causal_state(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), chunk,
+                                             torch.from_numpy(S0).cuda(), torch.from_numpy(z0).cuda())
+    ref, Sr, zr = oracle.causal_recurrent(f64(q, dtype), f64(k, dtype), f64(v, dtype),
+                                          s0=S0.astype(np.float64), z0=z0.astype(np.float64), return_state=True)
+    assert normwise_err(from_dev(out, dtype), ref) <= TOL[dtype]
+    assert _state_err(Sn.cpu().numpy(), Sr) <= TOL[dtype]
+    assert _state_err(zn.cpu().numpy(), zr) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 128), ("f32", 64, 64)])
+def test_causal_state_from_zero_matches_forward(ea, dtype, d, chunk):
+    # no initial state: the outputs are those of la_forward_causal, bit for bit, and the final
+    # state is the plain sum over all tokens
+    B, H, n = 2, 4, 1000
+    scale = 1.0 if dtype == "f32" else 1.0 / np.sqrt(d)
+    q, k, v = random_inputs(50 + d, (B, H, n, d), dtype, scale)
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    say("causal state from zero", dtype, d, chunk)
+    out, Sn, zn = ea.la_forward_causal_state(tq, tk, tv, chunk)
+    plain = ea.la_forward_causal(tq, tk, tv, chunk=chunk)
+    assert np.array_equal(from_dev(out, dtype), from_dev(plain, dtype))
+    Sr, zr = oracle.state_from_tokens_matmul(f64(k, dtype), f64(v, dtype))
+    assert _state_err(Sn.cpu().numpy(), Sr) <= TOL[dtype]
+    assert _state_err(zn.cpu().numpy(), zr) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 64, 64), ("bf16", 128, 128), ("f32", 64, 128)])
+def test_causal_state_pieces_bitwise(ea, dtype, d, chunk):
+    # 256 heads give one segment per head; cut at a chunk boundary, two calls with the state
+    # carried do the same arithmetic as one call: outputs and final state agree bit for bit
+    import torch
+    B, H, n1, n2 = 16, 16, 2 * chunk, 150
+    scale = 1.0 if dtype == "f32" else 1.0 / np.sqrt(d)
+    q, k, v = random_inputs(60 + d + chunk, (B, H, n1 + n2, d), dtype, scale)
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    assert ea.la_causal_plan(B, H, n1 + n2, d, chunk, tq.dtype) >= n1 + n2  # one segment
+    say("causal state pieces", dtype, d, chunk)
+    full, Sf, zf = ea.la_forward_causal_state(tq, tk, tv, chunk)
+    a, S1, z1 = ea.la_forward_causal_state(tq[:, :, :n1].contiguous(), tk[:, :, :n1].contiguous(),
+                                           tv[:, :, :n1].contiguous(), chunk)
+    b, S2, z2 = ea.la_forward_causal_state(tq[:, :, n1:].contiguous(), tk[:, :, n1:].contiguous(),
+                                           tv[:, :, n1:].contiguous(), chunk, S1, z1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a, b], dim=2), full)
+    assert torch.equal(S2, Sf) and torch.equal(z2, zf)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 128), ("bf16", 64, 64), ("f32", 128, 64)])
+def test_causal_state_pieces_segmented(ea, dtype, d, chunk):
+    # few heads (several segments per head) and a cut inside a chunk: agreement to rounding
+    B, H, n1, n2 = 1, 2, 1000, 1333
+    scale = 1.0 if dtype == "f32" else 1.0 / np.sqrt(d)
+    q, k, v = random_inputs(70 + d + chunk, (B, H, n1 + n2, d), dtype, scale)
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    say("causal state pieces, segmented", dtype, d, chunk)
+    a, S1, z1 = ea.la_forward_causal_state(tq[:, :, :n1].contiguous(), tk[:, :, :n1].contiguous(),
+                                           tv[:, :, :n1].contiguous(), chunk)
+    b, S2, z2 = ea.la_forward_causal_state(tq[:, :, n1:].contiguous(), tk[:, :, n1:].contiguous(),
+                                           tv[:, :, n1:].contiguous(), chunk, S1, z1)
+    ref, Sr, zr = oracle.causal_recurrent(f64(q, dtype), f64(k, dtype), f64(v, dtype), return_state=True)
+    g = np.concatenate([from_dev(a, dtype), from_dev(b, dtype)], axis=2)
+    assert normwise_err(g, ref) <= TOL[dtype]
+    assert _state_err(S2.cpu().numpy(), Sr) <= TOL[dtype]
+    assert _state_err(z2.cpu().numpy(), zr) <= TOL[dtype]
+
+
+def test_prefill_then_decode(ea):
+    # the final state of a causal prefill is the decode step's state: decoding the next tokens
+    # continues the causal outputs of the whole sequence
+    B, H, n, steps, d = 2, 4, 517, 20, 128
+    q, k, v = random_inputs(80, (B, H, n + steps, d), "bf16", 1.0 / np.sqrt(d))
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    say("prefill then decode")
+    _, S, z = ea.la_forward_causal_state(tq[:, :, :n].contiguous(), tk[:, :, :n].contiguous(),
+                                         tv[:, :, :n].contiguous(), 128)
+    outs = []
+    for t in range(n, n + steps):
+        o = ea.la_decode_step(tq[:, :, t].contiguous(), tk[:, :, t].contiguous(), tv[:, :, t].contiguous(), S, z)
+        outs.append(from_dev(o, "bf16"))
+    ref = oracle.causal_recurrent(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"))
+    assert normwise_err(np.stack(outs, axis=2), ref[:, :, n:]) <= TOL_BF16
+
+
+def test_causal_state_empty_sequence(ea):
+    # n = 0: the final state is the initial one (zeros without one), nothing else is touched
+    import torch
+    B, H, d = 3, 2, 64
+    e = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    S0 = torch.randn(B, H, d, d, device="cuda")
+    z0 = torch.rand(B, H, d, device="cuda")
+    say("causal state, empty sequence")
+    out, Sn, zn = ea.la_forward_causal_state(e, e, e, 64, S0, z0)
+    torch.cuda.synchronize()
+    assert out.shape == e.shape and torch.equal(Sn, S0) and torch.equal(zn, z0)
+    Sn.fill_(7.0)
+    zn.fill_(7.0)
+    _, Sn, zn = ea.la_forward_causal_state(e, e, e, 64, Sn=Sn, zn=zn)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(Sn) == 0 and torch.count_nonzero(zn) == 0
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
 def test_state_sums_vs_oracle(ea, dtype, d):
     import torch

@@ -282,6 +282,25 @@ def test_causal_from_state_splits():
     np.testing.assert_allclose(z2, zf, rtol=1e-13)
 
 
+def test_causal_from_state_equals_masked_pairwise_form_on_concatenation():
+    # an initial state that sums prior tokens stands exactly for those tokens: the outputs are
+    # the masked pairwise form's rows over [prior | tokens], and the final state is the plain
+    # sum over all of them
+    prior, n, d = 13, 21, 5
+    q, k, v = _rand(22, prior + n, d, bh=2)
+    S0, z0 = oracle.state_from_tokens_matmul(k[:, :prior], v[:, :prior])
+    out, Sn, zn = oracle.causal_recurrent(q[:, prior:], k[:, prior:], v[:, prior:], s0=S0, z0=z0,
+                                          return_state=True)
+    ref = oracle.quadratic(q, k, v, causal=True)
+    np.testing.assert_allclose(out, ref[:, prior:], rtol=1e-11, atol=1e-13)
+    Sa, za = oracle.state_from_tokens_matmul(k, v)
+    np.testing.assert_allclose(Sn, Sa, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(zn, za, rtol=1e-13)
+    # no tokens: the final state is the initial one
+    _, Se, ze = oracle.causal_recurrent(q[:, :0], k[:, :0], v[:, :0], s0=S0, z0=z0, return_state=True)
+    assert np.array_equal(Se, S0) and np.array_equal(ze, z0)
+
+
 def test_decode_resume_bitwise():
     # the state is the whole checkpoint: 6 + save/restore + 6 steps == 12 steps
     d = 4
