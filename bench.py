@@ -1,6 +1,7 @@
 """Throughput of the kernelized linear-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
+    python bench.py --grid      # the metric's grid of shapes, each forward alone (see run_grid)
 
 One step = the whole hot path over one batch of each synthetic workload:
   * non-causal forward, bf16, B=8 H=16 n=16384 d=64 (feature map, split-n KV/z sums, output);
@@ -22,6 +23,7 @@ import os
 import platform
 import sys
 import time
+import zlib
 
 import numpy as np
 
@@ -107,6 +109,57 @@ def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
     }
 
 
+def run_grid():
+    """The metric's grid: {non-causal, causal} x n in {16K, 64K} x d in {64, 128}, bf16 and fp32,
+    128 heads each (B=8, H=16), seeded N(0,1)/sqrt(d) inputs drawn on the device.  Each forward
+    is timed alone after a cache-evicting read (median of 5), against its algorithmic bytes."""
+    import torch
+
+    import efficient_attention_amd as ea
+
+    dev = torch.device("cuda:0")
+    flush = torch.ones(1 << 28, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B, H = 8, 16
+    points = []
+    for dtype in ("bf16", "f32"):
+        for form in ("noncausal", "causal"):
+            for n in (16384, 65536):
+                for d in (64, 128):
+                    chunk = 128 if (dtype == "bf16" or d == 64) else 64  # fp32 supports d*chunk <= 8192
+                    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+                    gen = torch.Generator(device=dev)
+                    gen.manual_seed(zlib.crc32(repr((form, dtype, n, d)).encode()))
+                    q, k, v = [(torch.randn(B, H, n, d, device=dev, generator=gen) * d ** -0.5).to(tdt)
+                               for _ in range(3)]
+                    out = torch.empty_like(q)
+                    if form == "noncausal":
+                        fn = lambda: ea.la_forward_noncausal(q, k, v, out=out)
+                    else:
+                        fn = lambda: ea.la_forward_causal(q, k, v, chunk=chunk, out=out)
+                    fn()
+                    times = []
+                    for _ in range(5):
+                        flush.sum()
+                        e0.record(stream)
+                        fn()
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        times.append(e0.elapsed_time(e1))
+                    ms = float(np.median(times))
+                    nbytes = algorithmic_bytes(B, H, n, d, 2 if dtype == "bf16" else 4)
+                    points.append({"form": form, "dtype": dtype, "B": B, "H": H, "n": n, "d": d,
+                                   "chunk": chunk if form == "causal" else None, "isolated_ms": ms,
+                                   "tokens_per_s": B * n / (ms * 1e-3),
+                                   "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+                                   "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+                    print("[bench] grid %s" % json.dumps(points[-1]), file=sys.stderr, flush=True)
+                    del q, k, v, out
+    print(json.dumps({"metric": METRIC, "mode": "grid", "n_gpus": 1, "data": "synthetic (seeded, on device)",
+                      "grid": points}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,11 +168,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 2 GiB (reference for HBM counters)")
+    ap.add_argument("--grid", action="store_true",
+                    help="time every forward of the metric's shape grid instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.grid:
+        run_grid()
+        return
 
     import torch
 

@@ -167,3 +167,46 @@ def test_c4_causal_in_two_pieces_with_state(ea):
         worst = max(worst, normwise_err(Sg[b], Sa), normwise_err(zg[b], za, head_axes_last=1))
     print("C4 final state normwise err %.3e" % worst)
     assert worst <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------- the metric's grid
+GRID = [(form, dtype, n, d) for dtype in ("bf16", "f32") for form in ("noncausal", "causal")
+        for n in (16384, 65536) for d in (64, 128)]
+
+
+@pytest.mark.parametrize("form,dtype,n,d", GRID)
+def test_grid_point_full_size(ea, form, dtype, n, d):
+    # every shape of the metric's grid, in the launch configuration `bench.py --grid` times
+    # (128 heads, inputs drawn on the device from a seeded generator): sampled rows of two heads
+    # against the quadratic definition, and one whole head against the oracle at n = 16K
+    import zlib
+
+    import torch
+    B, H = 8, 16
+    chunk = 128 if (dtype == "bf16" or d == 64) else 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(zlib.crc32(repr((form, dtype, n, d)).encode()))
+    say("grid", form, dtype, n, d, "GPU run")
+    q, k, v = [(torch.randn(B, H, n, d, device="cuda", generator=gen) * d ** -0.5).to(tdt) for _ in range(3)]
+    out = ea.la_forward_noncausal(q, k, v) if form == "noncausal" else ea.la_forward_causal(q, k, v, chunk=chunk)
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else 1e-4
+
+    def host(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    seg_len = ea.la_causal_plan(B, H, n, d, chunk, tdt) if form == "causal" else n
+    rng = np.random.default_rng(zlib.crc32(repr(("rows", form, dtype, n, d)).encode()))
+    extra = [0, 1, chunk - 1, chunk, seg_len - 1, seg_len, n - 1]
+    for (b, h) in [(0, 0), (B - 1, H - 1)]:
+        Q, K, V, G = host(q[b, h]), host(k[b, h]), host(v[b, h]), host(out[b, h])
+        assert np.all(np.isfinite(G))
+        rows = _sample_rows(n, extra, rng, count=10)
+        say("grid", form, dtype, n, d, "oracle rows", b, h)
+        ref = oracle.rows(Q, K, V, rows, causal=(form == "causal"))
+        assert normwise_err(G[rows][None], ref[None]) <= tol, (b, h)
+        if n == 16384 and (b, h) == (0, 0):
+            say("grid", form, dtype, n, d, "oracle head")
+            whole = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
+            assert normwise_err(G, whole) <= tol
