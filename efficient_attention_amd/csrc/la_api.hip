@@ -157,7 +157,7 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
       overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
     return LA_ERR_ALIAS;
-  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * ((n + la::kNcQueries - 1) / la::kNcQueries)))
+  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * cdiv(n, la::nc_queries((int)d, dtype))))
     return LA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);

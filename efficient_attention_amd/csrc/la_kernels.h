@@ -66,8 +66,10 @@ hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
 // sn, zn = s0, z0 (zeros where s0, z0 are null) for every head: the final state of an empty sequence.
 hipError_t launch_state_copy(const CausalArgs& a, int d, hipStream_t s);
 
-// Queries per workgroup of the non-causal output kernel (4 waves x 512).
-constexpr int64_t kNcQueries = 2048;
+// Queries per workgroup of the non-causal output kernel: 4 waves x 512, or 4 waves x 1024 for
+// bf16 with d = 128, whose workgroups fit only two per compute unit (LDS): 128 heads x 16K
+// queries are then one round of workgroups.
+constexpr int64_t nc_queries(int d, int dtype) { return dtype == 1 && d == 128 ? 4096 : 2048; }
 
 // Tile sizes the host needs for workspace planning.
 constexpr int kStateTileBf16 = 64;  // kv_state_bf16: tokens per workgroup tile

@@ -449,17 +449,21 @@ __device__ __forceinline__ void head_state(const NcOutArgs& a, int64_t bh, int t
 // so does the output tile on its way out.  On this device streaming whole rows is ~8% faster
 // than streaming the 64-byte row pieces the operand layout would load directly.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void nc_out_bf16(NcOutArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2))) void nc_out_bf16(NcOutArgs a) {
   constexpr int LD = D + 16;  // row stride of 8 mod 64 dwords: conflict-free 16-row reads
   constexpr int NC = D / 16;
-  constexpr int KS = D / 32;           // MFMA k-steps; also wave-wide accesses per 16-row tile
+  constexpr int KS = D / 32;           // MFMA k-steps
+  constexpr int BB = D == 64 ? 1 : 2;  // 16-query blocks per batch and wave (see below)
+  constexpr int QB = 16 * BB;          // queries per batch and wave
   constexpr int BPR = D / 8;           // 16-byte blocks per row
   constexpr int RPI = 64 / BPR;        // rows per wave-wide access
-  constexpr int ST = 16 * D;           // staging tile (16 rows x D) elements
-  constexpr int QPW = kNcQueries / 4;  // queries per wave
+  constexpr int NL = QB / RPI;         // wave-wide accesses per batch
+  constexpr int ST = QB * D;           // staging tile (QB rows x D) elements
+  constexpr int64_t QT = nc_queries(D, 1);  // queries per workgroup
+  constexpr int QPW = (int)QT / 4;          // queries per wave
   __shared__ __attribute__((aligned(16))) uint16_t KVt[D * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t stage[4 * 2 * ST];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4 * ST];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // b = 8 j + x (on XCD x) takes tile j % tiles of head 8 (j / tiles) + x: all tiles of a head
   // run on one XCD, whose L2 then serves the head's partial states to all of them.  (Giving
   // each XCD a contiguous block of heads instead measured slower.)
-  const int64_t tiles = (a.n + kNcQueries - 1) / kNcQueries;
+  const int64_t tiles = (a.n + QT - 1) / QT;
   int64_t bh, tile;
   if (a.bh % 8 == 0) {
     const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
@@ -479,33 +483,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     bh = blockIdx.x / tiles;
     tile = blockIdx.x % tiles;
   }
-  const int64_t q0 = tile * kNcQueries + wave * 16;
+  const int64_t q0 = tile * QT + wave * QB;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
-  uint16_t* Qs = stage + wave * 2 * ST;  // phi(Q) tile
-  uint16_t* Os = Qs + ST;                // output tile
+  uint16_t* Ts = stage + wave * ST;  // this wave's staging tile: phi(Q) in, then the outputs
 
-  // Staging tile layout: row r, 16-byte block b at r * D + 8 (b ^ f(r)).  The XOR makes three
-  // patterns conflict-free on the 64 banks: whole rows (the HBM side), 16 rows of one block
-  // (operand reads) and 16 rows x 8 bytes (accumulator writes).
-  auto sofs = [](int r, int b) { return r * D + ((b ^ (D == 64 ? ((r & 7) ^ (r >> 3)) : r)) << 3); };
+  // Staging tile layout: row r, 16-byte block b at r * D + 8 (b ^ f(r % 16)).  The XOR makes
+  // three patterns conflict-free on the 64 banks: whole rows (the HBM side), 16 rows of one
+  // block (operand reads) and 16 rows x 8 bytes (accumulator writes).
+  auto sofs = [](int r, int b) {
+    const int r16 = r & 15;
+    return r * D + ((b ^ (D == 64 ? ((r16 & 7) ^ (r16 >> 3)) : r16)) << 3);
+  };
 
-  // Queries go in batches: in batch b the four waves take consecutive runs of 16 queries.
-  // NS register sets keep the next NS - 1 batches in flight (the loop is unrolled by NS; the
-  // loads past the last batch re-read it, which costs no HBM traffic, so no load is
-  // conditional).  Every workgroup starts at once and first waits for its head's state, so
-  // the state is read first, ahead of the query sets in the memory queue; the first query
-  // sets then load while the state is converted.
-  constexpr int NBATCH = QPW / 16;
-  constexpr int NS = D == 64 ? 4 : 2;
-  static_assert(NBATCH % NS == 0, "batches come in groups of NS");
-  auto batch_row = [&](int b) { return q0 + (int64_t)b * 64; };
-  u32x4 qs[NS][KS];
-  auto load = [&](int b, u32x4 (&q)[KS]) {
-    const TileRows tr = tile_rows(batch_row(b < NBATCH ? b : NBATCH - 1), a.n, 16);
+  // Queries go in batches: in batch b the four waves take consecutive runs of QB queries.  For
+  // D = 128 a batch holds two 16-query blocks, which share every KV^T operand read from LDS:
+  // with one block per batch the 32 KB of KV^T would be read from LDS for every 8 KB of HBM
+  // traffic.  NS register sets keep the next NS - 1 batches in flight (the loop is unrolled by
+  // NS; the loads past the last batch re-read it, which costs no HBM traffic, so no load is
+  // conditional).  Every workgroup starts at once and first waits for its head's state, so the
+  // state is read first, ahead of the query sets in the memory queue; the first query sets then
+  // load while the state is converted.
+  constexpr int NBATCH = QPW / QB;
+  constexpr int NS = 4;
+  static_assert(NBATCH % NS == 0 && QB % RPI == 0, "batches come in groups of NS");
+  auto batch_row = [&](int b) { return q0 + (int64_t)b * 4 * QB; };
+  u32x4 qs[NS][NL];
+  auto load = [&](int b, u32x4 (&q)[NL]) {
+    const TileRows tr = tile_rows(batch_row(b < NBATCH ? b : NBATCH - 1), a.n, QB);
     const uint16_t* qt = Q + tr.first * D;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) q[i] = ld16_row(qt, i * RPI + prow, tr.last, D, pblk * 8);  // rows >= n are never stored
+    for (int i = 0; i < NL; ++i) q[i] = ld16_row(qt, i * RPI + prow, tr.last, D, pblk * 8);  // rows >= n are never stored
   };
   // the head's fp32 state -> bf16 operands in LDS
   constexpr int NKV4 = D * D / 1024;
@@ -535,44 +543,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   __syncthreads();
 
-  // A wave's LDS accesses execute in order, so its private tiles need no barrier.
-  auto compute = [&](int b, const u32x4 (&q)[KS]) {
+  // A wave's LDS accesses execute in order, so its private tile needs no barrier, and the
+  // outputs can overwrite phi(Q) once its operands are read.
+  auto compute = [&](int b, const u32x4 (&q)[NL]) {
 #pragma unroll
-    for (int i = 0; i < KS; ++i) st16(&Qs[sofs(i * RPI + prow, pblk)], phi_bf16x8(q[i]));
-    u32x4 qf[KS];
+    for (int i = 0; i < NL; ++i) st16(&Ts[sofs(i * RPI + prow, pblk)], phi_bf16x8(q[i]));
+    u32x4 qf[BB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(&Qs[sofs(l16, 4 * ks + g)]);
-    f32x4 acc[NC];
-    f32x4 accd = zero4();
+    for (int bb = 0; bb < BB; ++bb)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = zero4();
+      for (int ks = 0; ks < KS; ++ks) qf[bb][ks] = ld16(&Ts[sofs(bb * 16 + l16, 4 * ks + g)]);
+    f32x4 acc[BB][NC];
+    f32x4 accd[BB];
+#pragma unroll
+    for (int bb = 0; bb < BB; ++bb) {
+      accd[bb] = zero4();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[bb][c] = zero4();
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        acc[c] = mfma_bf16(ld16(&KVt[(c * 16 + l16) * LD + ks * 32 + g * 8]), qf[ks], acc[c]);
-      accd = mfma_bf16(ld16(&Zr[l16 * LD + ks * 32 + g * 8]), qf[ks], accd);
-    }
-    const float inv = __builtin_amdgcn_rcpf(__shfl(accd[0] + accd[1], l16));  // den > 0
-    // lane (l16, g) holds features 16 c + 4 g + r of query l16: 8 bytes of its output row
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 kvop = ld16(&KVt[(c * 16 + l16) * LD + ks * 32 + g * 8]);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x2 o;
-      o.x = pack_bf16(acc[c][0] * inv, acc[c][1] * inv);
-      o.y = pack_bf16(acc[c][2] * inv, acc[c][3] * inv);
-      *reinterpret_cast<u32x2*>(&Os[sofs(l16, 2 * c + (g >> 1)) + 4 * (g & 1)]) = o;
+        for (int bb = 0; bb < BB; ++bb) acc[bb][c] = mfma_bf16(kvop, qf[bb][ks], acc[bb][c]);
+      }
+      const u32x4 zop = ld16(&Zr[l16 * LD + ks * 32 + g * 8]);
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb) accd[bb] = mfma_bf16(zop, qf[bb][ks], accd[bb]);
+    }
+#pragma unroll
+    for (int bb = 0; bb < BB; ++bb) {
+      const float inv = __builtin_amdgcn_rcpf(__shfl(accd[bb][0] + accd[bb][1], l16));  // den > 0
+      // lane (l16, g) holds features 16 c + 4 g + r of query l16: 8 bytes of its output row
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x2 o;
+        o.x = pack_bf16(acc[bb][c][0] * inv, acc[bb][c][1] * inv);
+        o.y = pack_bf16(acc[bb][c][2] * inv, acc[bb][c][3] * inv);
+        *reinterpret_cast<u32x2*>(&Ts[sofs(bb * 16 + l16, 2 * c + (g >> 1)) + 4 * (g & 1)]) = o;
+      }
     }
     const int64_t r0 = batch_row(b);
     char* ot = reinterpret_cast<char*>(O + r0 * D);  // uniform tile base
-    u32x4 v[KS];
+    u32x4 v[NL];
 #pragma unroll
-    for (int i = 0; i < KS; ++i) v[i] = ld16(&Os[sofs(i * RPI + prow, pblk)]);
-    if (r0 + 16 <= a.n) {  // uniform: only the last tile of a head can be partial
+    for (int i = 0; i < NL; ++i) v[i] = ld16(&Ts[sofs(i * RPI + prow, pblk)]);
+    if (r0 + QB <= a.n) {  // uniform: only the last tile of a head can be partial
 #pragma unroll
-      for (int i = 0; i < KS; ++i) st16(ot + (uint32_t)(((i * RPI + prow) * D + pblk * 8) * 2), v[i]);
+      for (int i = 0; i < NL; ++i) st16(ot + (uint32_t)(((i * RPI + prow) * D + pblk * 8) * 2), v[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < KS; ++i)
+      for (int i = 0; i < NL; ++i)
         if ((int64_t)(i * RPI + prow) < a.n - r0)  // rows >= n are not stored
           st16(ot + (uint32_t)(((i * RPI + prow) * D + pblk * 8) * 2), v[i]);
     }
@@ -595,15 +618,16 @@ template <int D>
 __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   constexpr int LD = D + 4;
   constexpr int NC = D / 16;
-  constexpr int QPW = kNcQueries / 4;
+  constexpr int64_t QT = nc_queries(D, 0);  // queries per workgroup
+  constexpr int QPW = (int)QT / 4;
   __shared__ __attribute__((aligned(16))) float KVt[D * LD];
   __shared__ float zs[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t tiles = (a.n + kNcQueries - 1) / kNcQueries;
+  const int64_t tiles = (a.n + QT - 1) / QT;
   const int64_t bh = blockIdx.x / tiles;
-  const int64_t q0 = (blockIdx.x % tiles) * kNcQueries + wave * QPW;
+  const int64_t q0 = (blockIdx.x % tiles) * QT + wave * QPW;
   constexpr int NKV4 = D * D / 1024;
   f32x4 kv4[NKV4];
   float zv;
@@ -683,7 +707,8 @@ hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_nc_out_t(const NcOutArgs& a, int dtype, hipStream_t s) {
-  const int64_t blocks = a.bh * ((a.n + kNcQueries - 1) / kNcQueries);
+  const int64_t qt = nc_queries(D, dtype);
+  const int64_t blocks = a.bh * ((a.n + qt - 1) / qt);
   if (dtype == 1)
     hipLaunchKernelGGL(nc_out_bf16<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
