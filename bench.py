@@ -111,8 +111,9 @@ def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
 
 def run_grid():
     """The metric's grid: {non-causal, causal} x n in {16K, 64K} x d in {64, 128}, bf16 and fp32,
-    128 heads each (B=8, H=16), seeded N(0,1)/sqrt(d) inputs drawn on the device.  Each forward
-    is timed alone after a cache-evicting read (median of 5), against its algorithmic bytes."""
+    128 heads each (B=8, H=16), seeded N(0,1)/sqrt(d) inputs drawn on the device; then two
+    ragged batches (variable-length calls).  Each forward is timed alone after a cache-evicting
+    read (median of 5), against its algorithmic bytes."""
     import torch
 
     import efficient_attention_amd as ea
@@ -156,6 +157,39 @@ def run_grid():
                                    "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
                     print("[bench] grid %s" % json.dumps(points[-1]), file=sys.stderr, flush=True)
                     del q, k, v, out
+    # ragged batches: 8 sequences of 15K-40K tokens (the document lengths the pages mention),
+    # packed back to back, each [H][n_s][d]
+    rng = np.random.default_rng(15)
+    lengths = [int(x) for x in rng.integers(15000, 40001, size=8)]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    for form, H, d in (("noncausal", 16, 64), ("causal", 32, 128)):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(zlib.crc32(repr(("varlen", form, H, d)).encode()))
+        rows = H * int(cu[-1])
+        q, k, v = [(torch.randn(rows, d, device=dev, generator=gen) * d ** -0.5).to(torch.bfloat16) for _ in range(3)]
+        out = torch.empty_like(q)
+        if form == "noncausal":
+            fn = lambda: ea.la_forward_noncausal_varlen(q, k, v, cu, H, out=out)
+        else:
+            fn = lambda: ea.la_forward_causal_varlen(q, k, v, cu, H, chunk=128, out=out)
+        fn()
+        times = []
+        for _ in range(5):
+            flush.sum()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        nbytes = 4 * rows * d * 2
+        points.append({"form": form + "_varlen", "dtype": "bf16", "B": len(lengths), "H": H, "n": lengths, "d": d,
+                       "chunk": 128 if form == "causal" else None, "isolated_ms": ms,
+                       "tokens_per_s": int(cu[-1]) / (ms * 1e-3),
+                       "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+                       "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        print("[bench] grid %s" % json.dumps(points[-1]), file=sys.stderr, flush=True)
+        del q, k, v, out
     print(json.dumps({"metric": METRIC, "mode": "grid", "n_gpus": 1, "data": "synthetic (seeded, on device)",
                       "grid": points}), flush=True)
 

@@ -15,9 +15,14 @@ from ._binding import (  # noqa: F401
     la_causal_segments,
     la_causal_workspace_bytes,
     la_decode_step,
+    la_decode_step_masked,
     la_forward_causal,
     la_forward_causal_state,
+    la_forward_causal_varlen,
     la_forward_noncausal,
+    la_forward_noncausal_varlen,
+    la_noncausal_varlen_workspace_bytes,
+    la_causal_varlen_workspace_bytes,
     la_noncausal_workspace_bytes,
     la_state_sums,
     la_state_sums_workspace_bytes,

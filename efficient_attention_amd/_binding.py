@@ -10,6 +10,7 @@ import ctypes
 import os
 import threading
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +24,9 @@ LA_OK = 0
 EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
            "la_forward_noncausal", "la_causal_workspace_bytes", "la_forward_causal",
            "la_causal_plan", "la_state_sums_workspace_bytes", "la_state_sums",
-           "la_causal_segments", "la_decode_step", "la_forward_causal_state")
+           "la_causal_segments", "la_decode_step", "la_forward_causal_state",
+           "la_noncausal_varlen_workspace_bytes", "la_forward_noncausal_varlen",
+           "la_causal_varlen_workspace_bytes", "la_forward_causal_varlen", "la_decode_step_masked")
 
 _lib = None
 _lock = threading.Lock()
@@ -72,6 +75,16 @@ def load():
         lib.la_causal_segments.restype = I
         lib.la_decode_step.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, P]
         lib.la_decode_step.restype = I
+        lib.la_decode_step_masked.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, P]
+        lib.la_decode_step_masked.restype = I
+        lib.la_noncausal_varlen_workspace_bytes.argtypes = [P, I64, I64, I64, I]
+        lib.la_noncausal_varlen_workspace_bytes.restype = SZ
+        lib.la_forward_noncausal_varlen.argtypes = [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]
+        lib.la_forward_noncausal_varlen.restype = I
+        lib.la_causal_varlen_workspace_bytes.argtypes = [P, I64, I64, I64, I64, I]
+        lib.la_causal_varlen_workspace_bytes.restype = SZ
+        lib.la_forward_causal_varlen.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]
+        lib.la_forward_causal_varlen.restype = I
         _lib = lib
     return _lib
 
@@ -290,4 +303,100 @@ def la_causal_segments(q, k, v, sums, seg_len: int, chunk: int = 128, out=None, 
                                    B, H, n, d, chunk, _dtype_code(q), seg_len, sh)
     if st != LA_OK:
         raise LinAttnError(st, "la_causal_segments")
+    return out
+
+
+# ----------------------------------------------------------------------------- variable lengths
+def _offsets(cu_seqlens):
+    """Host int64 array of sequence offsets (list, numpy array or CPU tensor)."""
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    if cu.ndim != 1 or cu.size < 1:
+        raise ValueError("cu_seqlens must be a 1-D array of nseq + 1 offsets")
+    return cu
+
+
+def _check_varlen(q, k, v, cu, heads):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have the same shape and dtype")
+    d = q.shape[-1]
+    if q.numel() != int(heads) * int(cu[-1]) * d:
+        raise ValueError("q holds %d elements, the offsets call for H * cu[-1] * d = %d"
+                         % (q.numel(), int(heads) * int(cu[-1]) * d))
+    return d
+
+
+def la_noncausal_varlen_workspace_bytes(cu_seqlens, heads: int, d: int, dtype) -> int:
+    cu = _offsets(cu_seqlens)
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().la_noncausal_varlen_workspace_bytes(cu.ctypes.data, cu.size - 1, heads, d, code))
+
+
+def la_causal_varlen_workspace_bytes(cu_seqlens, heads: int, d: int, chunk: int, dtype) -> int:
+    cu = _offsets(cu_seqlens)
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().la_causal_varlen_workspace_bytes(cu.ctypes.data, cu.size - 1, heads, d, chunk, code))
+
+
+def la_forward_noncausal_varlen(q, k, v, cu_seqlens, heads: int, out=None, ws=None, stream=None):
+    """Non-causal forward over a variable-length batch: sequence s is the [heads, n_s, d] block
+    at token offset cu_seqlens[s] (q, k, v hold heads * cu_seqlens[-1] rows of d); returns out."""
+    cu = _offsets(cu_seqlens)
+    d = _check_varlen(q, k, v, cu, heads)
+    out = _out_like(q, out)
+    code = _dtype_code(q)
+    sh = _stream_handle(q.device, stream)
+    need = la_noncausal_varlen_workspace_bytes(cu, heads, d, code)
+    if ws is None:
+        ws = workspace(need, q.device, sh)
+    st = load().la_forward_noncausal_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                            cu.ctypes.data, cu.size - 1, heads, d, code,
+                                            ws.data_ptr() if ws is not None else None,
+                                            ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_forward_noncausal_varlen")
+    return out
+
+
+def la_forward_causal_varlen(q, k, v, cu_seqlens, heads: int, chunk: int = 128, out=None, ws=None, stream=None):
+    """Causal forward over a variable-length batch (layout as la_forward_noncausal_varlen)."""
+    cu = _offsets(cu_seqlens)
+    d = _check_varlen(q, k, v, cu, heads)
+    out = _out_like(q, out)
+    code = _dtype_code(q)
+    sh = _stream_handle(q.device, stream)
+    need = la_causal_varlen_workspace_bytes(cu, heads, d, chunk, code)
+    if ws is None:
+        ws = workspace(need, q.device, sh)
+    st = load().la_forward_causal_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         cu.ctypes.data, cu.size - 1, heads, d, chunk, code,
+                                         ws.data_ptr() if ws is not None else None,
+                                         ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_forward_causal_varlen")
+    return out
+
+
+def la_decode_step_masked(q, k, v, S, z, active, out=None, stream=None):
+    """la_decode_step for the sequences whose flag in `active` (uint8/bool GPU tensor [B]) is set;
+    the others keep their state and out."""
+    _check_qkv(q, k, v, 3)
+    B, H, d = q.shape
+    for name, t, shape in (("S", S, (B, H, d, d)), ("z", z, (B, H, d))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s" % (name, shape, q.device))
+    if active.dtype not in (torch.uint8, torch.bool) or tuple(active.shape) != (B,) or active.device != q.device \
+            or not active.is_contiguous():
+        raise ValueError("active must be a contiguous uint8/bool tensor of shape (%d,) on %s" % (B, q.device))
+    out = _out_like(q, out)
+    sh = _stream_handle(q.device, stream)
+    st = load().la_decode_step_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), S.data_ptr(), z.data_ptr(),
+                                      out.data_ptr(), active.data_ptr(), B, H, d, _dtype_code(q), sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_decode_step_masked")
     return out

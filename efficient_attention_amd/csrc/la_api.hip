@@ -111,6 +111,39 @@ int check_causal(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, int 
   return LA_OK;
 }
 
+// A variable-length batch: validates the host offsets and fills the kernels' head table, the
+// longest sequence, the head count nseq * H and the bytes of one [sum_s H n_s d] tensor.
+struct Varlen {
+  la::SeqTable tab;
+  int64_t maxn = 0, bh = 0;
+  size_t bytes = 0;
+};
+
+int make_varlen(const int64_t* cu, int64_t nseq, int64_t H, int64_t d, int dtype, Varlen* v) {
+  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16) return LA_ERR_DTYPE;
+  if (nseq < 0 || H < 0 || d < 0) return LA_ERR_SHAPE;
+  if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+  if (nseq > la::kMaxSeqs) return LA_ERR_UNSUPPORTED;
+  if (!cu) return LA_ERR_NULL;
+  if (cu[0] != 0) return LA_ERR_SHAPE;
+  memset(&v->tab, 0, sizeof(v->tab));
+  v->tab.heads = H;
+  v->tab.cu[0] = 0;
+  v->maxn = 0;
+  for (int64_t s = 0; s < nseq; ++s) {
+    if (cu[s + 1] < cu[s]) return LA_ERR_SHAPE;
+    const int64_t ns = cu[s + 1] - cu[s];
+    v->maxn = ns > v->maxn ? ns : v->maxn;
+    v->tab.cu[s + 1] = cu[s + 1];
+  }
+  int64_t e = 0;
+  if (__builtin_mul_overflow(nseq, H, &v->bh) || __builtin_mul_overflow(H, cu[nseq], &e) ||
+      __builtin_mul_overflow(e, d, &e) || __builtin_mul_overflow(e, (int64_t)elem_bytes(dtype), &e))
+    return LA_ERR_SHAPE;
+  v->bytes = (size_t)e;
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -357,8 +390,8 @@ int la_forward_causal_state(const void* q, const void* k, const void* v, void* o
   return LA_OK;
 }
 
-int la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
-                   int64_t B, int64_t H, int64_t d, int dtype, void* stream) {
+static int decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
+                       const uint8_t* active, int64_t B, int64_t H, int64_t d, int dtype, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
   int st = check_shape(B, H, 1, d, dtype, &bh, &bytes);
@@ -374,6 +407,9 @@ int la_decode_step(const void* q, const void* k, const void* v, float* S, float*
       overlaps(out, bytes, v, bytes) || overlaps(out, bytes, S, sbytes) ||
       overlaps(out, bytes, z, zbytes) || overlaps(S, sbytes, z, zbytes))
     return LA_ERR_ALIAS;
+  if (active && (overlaps(active, (size_t)B, out, bytes) || overlaps(active, (size_t)B, S, sbytes) ||
+                 overlaps(active, (size_t)B, z, zbytes)))
+    return LA_ERR_ALIAS;
   if (!grid_ok(bh)) return LA_ERR_SHAPE;
   la::DecodeArgs da;
   da.q = q;
@@ -382,9 +418,127 @@ int la_decode_step(const void* q, const void* k, const void* v, float* S, float*
   da.S = S;
   da.z = z;
   da.out = out;
+  da.active = active;
+  da.heads = H;
   da.bh = bh;
   if (la::launch_decode(da, (int)d, dtype, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return LA_ERR_HIP;
+  return LA_OK;
+}
+
+int la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
+                   int64_t B, int64_t H, int64_t d, int dtype, void* stream) {
+  return decode_step(q, k, v, S, z, out, nullptr, B, H, d, dtype, stream);
+}
+
+int la_decode_step_masked(const void* q, const void* k, const void* v, float* S, float* z,
+                          void* out, const uint8_t* active, int64_t B, int64_t H, int64_t d,
+                          int dtype, void* stream) {
+  if (!active && B * H > 0) return LA_ERR_NULL;
+  return decode_step(q, k, v, S, z, out, active, B, H, d, dtype, stream);
+}
+
+size_t la_noncausal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
+                                           int64_t d, int dtype) {
+  Varlen vl;
+  if (make_varlen(cu_seqlens, nseq, H, d, dtype, &vl) != LA_OK || vl.bh == 0 || vl.maxn == 0) return 0;
+  return nc_ws_bytes(plan_state(vl.bh, vl.maxn, (int)d, dtype), (int)d);
+}
+
+int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, void* out,
+                                const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
+                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  Varlen vl;
+  int st = make_varlen(cu_seqlens, nseq, H, d, dtype, &vl);
+  if (st != LA_OK) return st;
+  if (vl.bh == 0 || vl.maxn == 0) return LA_OK;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
+  const StatePlan p = plan_state(vl.bh, vl.maxn, (int)d, dtype);
+  const size_t need = nc_ws_bytes(p, (int)d);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  const size_t bytes = vl.bytes;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(p.groups * p.slices) || !grid_ok(vl.bh * cdiv(vl.maxn, la::nc_queries((int)d, dtype))))
+    return LA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* parts = reinterpret_cast<float*>(workspace);
+  la::KvStateArgs ka = state_args(p, k, v, parts, parts, vl.maxn, vl.maxn, 1);
+  if (la::launch_kv_state(ka, (int)d, dtype, s, &vl.tab) != hipSuccess) return LA_ERR_HIP;
+  la::NcOutArgs oa;
+  oa.q = q;
+  oa.out = out;
+  oa.state = parts;
+  oa.slices = p.slices;
+  oa.n = vl.maxn;
+  oa.bh = vl.bh;
+  if (la::launch_nc_out(oa, (int)d, dtype, s, &vl.tab) != hipSuccess) return LA_ERR_HIP;
+  return LA_OK;
+}
+
+size_t la_causal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
+                                        int64_t d, int64_t chunk, int dtype) {
+  Varlen vl;
+  if (make_varlen(cu_seqlens, nseq, H, d, dtype, &vl) != LA_OK || vl.bh == 0 || vl.maxn == 0) return 0;
+  if (chunk != 64 && chunk != 128) return 0;
+  const int64_t seg_len = causal_seg_len(vl.bh, vl.maxn, chunk);
+  const int64_t segs = cdiv(vl.maxn, seg_len);
+  if (segs == 1) return 0;
+  return causal_ws_bytes(plan_state(vl.bh * (segs - 1), seg_len, (int)d, dtype), (int)d);
+}
+
+int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* out,
+                             const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
+                             int64_t chunk, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Varlen vl;
+  int st = make_varlen(cu_seqlens, nseq, H, d, dtype, &vl);
+  if (st != LA_OK) return st;
+  if (chunk != 64 && chunk != 128) return LA_ERR_UNSUPPORTED;
+  if (dtype == LA_DTYPE_F32 && d * chunk > 8192) return LA_ERR_UNSUPPORTED;
+  if (vl.bh == 0 || vl.maxn == 0) return LA_OK;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
+  const int64_t seg_len = causal_seg_len(vl.bh, vl.maxn, chunk);
+  const int64_t segs = cdiv(vl.maxn, seg_len);
+  StatePlan p;
+  size_t need = 0;
+  if (segs > 1) {
+    p = plan_state(vl.bh * (segs - 1), seg_len, (int)d, dtype);
+    need = causal_ws_bytes(p, (int)d);
+    if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  }
+  const size_t bytes = vl.bytes;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(vl.bh * segs) || (segs > 1 && !grid_ok(p.groups * p.slices))) return LA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  la::CausalArgs ca;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.out = out;
+  ca.seg_state = nullptr;
+  ca.seg_parts = 1;
+  ca.s0 = ca.z0 = nullptr;
+  ca.sn = ca.zn = nullptr;
+  ca.n = vl.maxn;
+  ca.bh = vl.bh;
+  ca.segs = segs;
+  ca.seg_len = seg_len;
+  if (segs > 1) {
+    float* parts = reinterpret_cast<float*>(workspace);
+    la::KvStateArgs ka = state_args(p, k, v, parts, parts, vl.maxn, seg_len, segs - 1);
+    if (la::launch_kv_state(ka, (int)d, dtype, s, &vl.tab) != hipSuccess) return LA_ERR_HIP;
+    ca.seg_state = parts;
+    ca.seg_parts = p.slices;
+  }
+  if (la::launch_causal(ca, (int)d, (int)chunk, dtype, s, &vl.tab) != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
 }
 

@@ -60,8 +60,8 @@ __device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64
 //     V is read with the same permutation, and A never goes through LDS;
 //   * the normaliser rides along as one extra 16-row output tile: z (hi, lo) rows against
 //     phi(Q) and a row of ones against A give phi(q).z + sum_j A_ij in rows 0 and 1.
-template <int D, int C>
-__global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
+template <int D, int C, class TB>
+__global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
   constexpr int NT = 512;
   constexpr int LDK = D + 16;       // row stride of 8 mod 64 dwords: conflict-free 16-row reads
   constexpr int NI = C / 16;         // query (and key) tiles per chunk
@@ -86,12 +86,14 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
+  const HeadSpan sp = head_span(tb, a.n, bh);
   const int64_t t0 = seg * a.seg_len;
-  const int64_t t1 = t0 + a.seg_len < a.n ? t0 + a.seg_len : a.n;
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + bh * a.n * D;
-  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + bh * a.n * D;
-  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
+  if (t0 >= sp.n) return;  // a segment past a shorter sequence's end (variable lengths)
+  const int64_t t1 = t0 + a.seg_len < sp.n ? t0 + a.seg_len : sp.n;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + sp.row0 * D;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + sp.row0 * D;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + sp.row0 * D;
+  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + sp.row0 * D;
 
   const int it = wave < 4 ? wave : (NI == 8 ? 11 - wave : 7 - wave);   // this wave's query tile
   const int oc0 = (NI == 8 || wave < 4) ? 0 : NC / 2;                 // its first output column tile
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
   }
 
   // the state after the last token, from the last segment's workgroup
-  if (a.sn && seg == a.segs - 1) {
+  if (a.sn && seg == (sp.n - 1) / a.seg_len) {
     float* sn = a.sn + bh * D * D;
 #pragma unroll
     for (int i = 0; i < NAW; ++i)
@@ -406,8 +408,8 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a) {
 // {w, w+4, ...} in fp32 accumulators and produces the outputs of those columns for every
 // query of the chunk; the masked tile A^T is recomputed per wave (cheap at the sizes fp32 is
 // meant for) and, as in the bf16 kernel, fed back as an operand with permuted k.
-template <int D, int C>
-__global__ __launch_bounds__(256) void causal_f32(CausalArgs a) {
+template <int D, int C, class TB>
+__global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
   constexpr int LD = D + 4;
   constexpr int NI = C / 16;
   constexpr int NCW = D / 64;
@@ -420,12 +422,14 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
+  const HeadSpan sp = head_span(tb, a.n, bh);
   const int64_t t0 = seg * a.seg_len;
-  const int64_t t1 = t0 + a.seg_len < a.n ? t0 + a.seg_len : a.n;
-  const float* Q = reinterpret_cast<const float*>(a.q) + bh * a.n * D;
-  const float* K = reinterpret_cast<const float*>(a.k) + bh * a.n * D;
-  const float* V = reinterpret_cast<const float*>(a.v) + bh * a.n * D;
-  float* O = reinterpret_cast<float*>(a.out) + bh * a.n * D;
+  if (t0 >= sp.n) return;  // a segment past a shorter sequence's end (variable lengths)
+  const int64_t t1 = t0 + a.seg_len < sp.n ? t0 + a.seg_len : sp.n;
+  const float* Q = reinterpret_cast<const float*>(a.q) + sp.row0 * D;
+  const float* K = reinterpret_cast<const float*>(a.k) + sp.row0 * D;
+  const float* V = reinterpret_cast<const float*>(a.v) + sp.row0 * D;
+  float* O = reinterpret_cast<float*>(a.out) + sp.row0 * D;
 
   f32x4 accS[NA][NCW];
 #pragma unroll
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a) {
   }
 
   // the state after the last token, from the last segment's workgroup
-  if (a.sn && seg == a.segs - 1) {
+  if (a.sn && seg == (sp.n - 1) / a.seg_len) {
     float* sn = a.sn + bh * D * D;
 #pragma unroll
     for (int at = 0; at < NA; ++at)
@@ -600,23 +604,28 @@ hipError_t launch_state_copy(const CausalArgs& a, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int C>
-static hipError_t launch_causal_t(const CausalArgs& a, int dtype, hipStream_t s) {
+template <int D, int C, class TB>
+static hipError_t launch_causal_tb(const CausalArgs& a, int dtype, hipStream_t s, const TB& tb) {
   const unsigned blocks = (unsigned)(a.bh * a.segs);
   if (dtype == 1) {
-    hipLaunchKernelGGL((causal_bf16<D, C>), dim3(blocks), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((causal_bf16<D, C, TB>), dim3(blocks), dim3(512), 0, s, a, tb);
   } else {
     if constexpr (D * C <= 8192)
-      hipLaunchKernelGGL((causal_f32<D, C>), dim3(blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((causal_f32<D, C, TB>), dim3(blocks), dim3(256), 0, s, a, tb);
     else
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s) {
-  if (d == 64) return chunk == 64 ? launch_causal_t<64, 64>(a, dtype, s) : launch_causal_t<64, 128>(a, dtype, s);
-  return chunk == 64 ? launch_causal_t<128, 64>(a, dtype, s) : launch_causal_t<128, 128>(a, dtype, s);
+template <int D, int C>
+static hipError_t launch_causal_t(const CausalArgs& a, int dtype, hipStream_t s, const SeqTable* tab) {
+  return tab ? launch_causal_tb<D, C>(a, dtype, s, *tab) : launch_causal_tb<D, C>(a, dtype, s, NoTable{});
+}
+
+hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s, const SeqTable* tab) {
+  if (d == 64) return chunk == 64 ? launch_causal_t<64, 64>(a, dtype, s, tab) : launch_causal_t<64, 128>(a, dtype, s, tab);
+  return chunk == 64 ? launch_causal_t<128, 64>(a, dtype, s, tab) : launch_causal_t<128, 128>(a, dtype, s, tab);
 }
 
 }  // namespace la

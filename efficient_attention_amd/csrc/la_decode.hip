@@ -35,6 +35,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   __shared__ float dwave[4];
 
   const int64_t h = blockIdx.x;
+  if (a.active && !a.active[h / a.heads]) return;  // an inactive sequence: state and out untouched
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
   float* S = a.S + h * D * D;

@@ -6,6 +6,28 @@
 
 namespace la {
 
+// The heads of a batch.  Fixed length (NoTable): head bh is rows [bh * n, (bh + 1) * n) of the
+// [B][H][n][d] tensors.  Variable length (SeqTable): each sequence s is the fixed layout's
+// [H][n_s][d] block, the blocks packed back to back; with the offsets cu (cu[0] = 0,
+// n_s = cu[s + 1] - cu[s]) head bh = s * H + h starts at row H * cu[s] + h * n_s.  The table
+// travels by value in the kernel arguments (validated on the host), so it needs no device memory.
+constexpr int kMaxSeqs = 256;
+struct NoTable {};
+struct SeqTable {
+  int64_t heads;               // H
+  int64_t cu[kMaxSeqs + 1];    // sequence offsets in tokens
+};
+struct HeadSpan {
+  int64_t row0;  // first row of the head
+  int64_t n;     // its tokens
+};
+__device__ __forceinline__ HeadSpan head_span(const NoTable&, int64_t n, int64_t bh) { return {bh * n, n}; }
+__device__ __forceinline__ HeadSpan head_span(const SeqTable& t, int64_t, int64_t bh) {
+  const int64_t s = bh / t.heads, h = bh % t.heads;
+  const int64_t c0 = t.cu[s], ns = t.cu[s + 1] - c0;
+  return {t.heads * c0 + h * ns, ns};
+}
+
 // Stage-1 state sums over token ranges ("groups": one per head for the non-causal form, one
 // per head and leading segment for the causal form), split into `slices` workgroups each.
 struct KvStateArgs {
@@ -55,13 +77,18 @@ struct DecodeArgs {
   float* S;
   float* z;
   void* out;
+  const uint8_t* active;   // [B] device flags: sequences with 0 are skipped (null: all active)
+  int64_t heads;           // H (to find a head's sequence)
   int64_t bh;
 };
 
-hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s);
+// `tab` null: fixed-length batch (n = a.n for every head); else a variable-length batch whose
+// heads are described by *tab, and a.n is the longest sequence (the grids are planned for it;
+// workgroups beyond a shorter sequence exit at once).
+hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s, const SeqTable* tab = nullptr);
 hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s);
-hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s);
-hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s);
+hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s, const SeqTable* tab = nullptr);
+hipError_t launch_causal(const CausalArgs& a, int d, int chunk, int dtype, hipStream_t s, const SeqTable* tab = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
 // sn, zn = s0, z0 (zeros where s0, z0 are null) for every head: the final state of an empty sequence.
 hipError_t launch_state_copy(const CausalArgs& a, int d, hipStream_t s);

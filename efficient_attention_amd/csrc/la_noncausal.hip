@@ -24,17 +24,24 @@ namespace la {
 // Group bookkeeping shared by the bf16 and fp32 variants.
 struct GroupRange {
   int64_t g, bh, s;   // group, head, slice
+  int64_t row0, hn;   // the head's first row and its tokens
   int64_t t0, t1;     // token range [t0, t1) of this slice within the head
 };
 
-__device__ __forceinline__ GroupRange group_range(const KvStateArgs& a) {
+// A slice past its head's end is empty (t0 >= t1); its workgroup still writes a zero partial,
+// reading only row hn - 1 (a head without tokens has no workgroup that reads anything).
+template <class TB>
+__device__ __forceinline__ GroupRange group_range(const KvStateArgs& a, const TB& tb) {
   GroupRange r;
   r.g = blockIdx.x / a.slices;
   r.s = blockIdx.x % a.slices;
   r.bh = r.g / a.groups_per_head;
+  const HeadSpan sp = head_span(tb, a.n, r.bh);
+  r.row0 = sp.row0;
+  r.hn = sp.n;
   int64_t seg = r.g % a.groups_per_head;
   int64_t gs = seg * a.group_len;
-  int64_t ge = gs + a.group_len < a.n ? gs + a.group_len : a.n;
+  int64_t ge = gs + a.group_len < sp.n ? gs + a.group_len : sp.n;
   r.t0 = gs + r.s * a.slice_len;
   r.t1 = r.t0 + a.slice_len < ge ? r.t0 + a.slice_len : ge;
   return r;
@@ -96,8 +103,8 @@ __device__ __forceinline__ void store_state_block(float* dst, int at0, const f32
 // the end are clamped and their rows masked, so they need no condition).  Small LDS and
 // register footprints let several workgroups share a CU and overlap one another's loads,
 // feature map and MFMA work.
-template <int D>
-__global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
+template <int D, class TB>
+__global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a, TB tb) {
   constexpr int T = kStateTileBf16;  // tokens per tile
   constexpr int LDK = D + 16;        // row stride of 8 (mod 64) dwords x odd: conflict-free reads
   constexpr int PPR = D / 8;         // 16-byte pieces per row
@@ -109,11 +116,12 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Kn[T * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Vn[T * LDK];
 
-  const GroupRange gr = group_range(a);
+  const GroupRange gr = group_range(a, tb);
+  if (gr.hn == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + gr.bh * a.n * D;
-  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + gr.bh * a.n * D;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + gr.row0 * D;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + gr.row0 * D;
 
   f32x4 acc[NA][NC];
   float zacc[NA];
@@ -198,8 +206,8 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a) {
 // operands as the state, on the MFMA pipe instead of the vector ALU (which the feature map
 // keeps busy).  The four partial states are added at the end in a fixed order,
 // ((w0 + w2) + (w1 + w3)).
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_state_bf16_waves(KvStateArgs a) {
+template <int D, class TB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_state_bf16_waves(KvStateArgs a, TB tb) {
   constexpr int TW = kStateTileWave;  // tokens per wave tile
   constexpr int LDK = D + 16;          // row stride of 8 (mod 64) dwords x odd: conflict-free reads
   constexpr int PPR = D / 8;           // 16-byte pieces per row
@@ -211,12 +219,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(4 * WL * 2 >= 2 * (D * D + D) * 4, "the final combine reuses the tile areas");
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * WL];
 
-  const GroupRange gr = group_range(a);
+  const GroupRange gr = group_range(a, tb);
+  if (gr.hn == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
   const int l16 = lane & 15, g = lane >> 4;
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + gr.bh * a.n * D;
-  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + gr.bh * a.n * D;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + gr.row0 * D;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + gr.row0 * D;
   uint16_t* Kw = lds + wave * WL;
   uint16_t* Vw = Kw + TW * LDK;
 
@@ -343,8 +352,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // fp32 stage 1: tile of 64 tokens kept in natural layout (the fp32 MFMA takes one k value
 // per lane, so no transpose is needed).
-template <int D>
-__global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a) {
+template <int D, class TB>
+__global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a, TB tb) {
   constexpr int T = 64;
   constexpr int LD = D + 4;
   constexpr int NA = D / 64;
@@ -354,11 +363,12 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a) {
   __shared__ __attribute__((aligned(16))) float kv_lds[D * D + D];  // [KV | z]
   float* z_lds = kv_lds + D * D;
 
-  const GroupRange gr = group_range(a);
+  const GroupRange gr = group_range(a, tb);
+  if (gr.hn == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const float* K = reinterpret_cast<const float*>(a.k) + gr.bh * a.n * D;
-  const float* V = reinterpret_cast<const float*>(a.v) + gr.bh * a.n * D;
+  const float* K = reinterpret_cast<const float*>(a.k) + gr.row0 * D;
+  const float* V = reinterpret_cast<const float*>(a.v) + gr.row0 * D;
 
   f32x4 acc[NA][NC];
   float zacc[NA];
@@ -448,8 +458,8 @@ __device__ __forceinline__ void head_state(const NcOutArgs& a, int64_t bh, int t
 // so the query tile passes through a wave-private LDS tile (phi applied on the way in), and
 // so does the output tile on its way out.  On this device streaming whole rows is ~8% faster
 // than streaming the 64-byte row pieces the operand layout would load directly.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2))) void nc_out_bf16(NcOutArgs a) {
+template <int D, class TB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2))) void nc_out_bf16(NcOutArgs a, TB tb) {
   constexpr int LD = D + 16;  // row stride of 8 mod 64 dwords: conflict-free 16-row reads
   constexpr int NC = D / 16;
   constexpr int KS = D / 32;           // MFMA k-steps
@@ -483,9 +493,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     bh = blockIdx.x / tiles;
     tile = blockIdx.x % tiles;
   }
+  const HeadSpan sp = head_span(tb, a.n, bh);
+  if (tile * QT >= sp.n) return;  // a tile past a shorter sequence's end (variable lengths)
+  const int64_t n = sp.n;
   const int64_t q0 = tile * QT + wave * QB;
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
-  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + sp.row0 * D;
+  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + sp.row0 * D;
   uint16_t* Ts = stage + wave * ST;  // this wave's staging tile: phi(Q) in, then the outputs
 
   // Staging tile layout: row r, 16-byte block b at r * D + 8 (b ^ f(r % 16)).  The XOR makes
@@ -510,7 +523,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
   auto batch_row = [&](int b) { return q0 + (int64_t)b * 4 * QB; };
   u32x4 qs[NS][NL];
   auto load = [&](int b, u32x4 (&q)[NL]) {
-    const TileRows tr = tile_rows(batch_row(b < NBATCH ? b : NBATCH - 1), a.n, QB);
+    const TileRows tr = tile_rows(batch_row(b < NBATCH ? b : NBATCH - 1), n, QB);
     const uint16_t* qt = Q + tr.first * D;
 #pragma unroll
     for (int i = 0; i < NL; ++i) q[i] = ld16_row(qt, i * RPI + prow, tr.last, D, pblk * 8);  // rows >= n are never stored
@@ -590,13 +603,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     u32x4 v[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) v[i] = ld16(&Ts[sofs(i * RPI + prow, pblk)]);
-    if (r0 + QB <= a.n) {  // uniform: only the last tile of a head can be partial
+    if (r0 + QB <= n) {  // uniform: only the last tile of a head can be partial
 #pragma unroll
       for (int i = 0; i < NL; ++i) st16(ot + (uint32_t)(((i * RPI + prow) * D + pblk * 8) * 2), v[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        if ((int64_t)(i * RPI + prow) < a.n - r0)  // rows >= n are not stored
+        if ((int64_t)(i * RPI + prow) < n - r0)  // rows >= n are not stored
           st16(ot + (uint32_t)(((i * RPI + prow) * D + pblk * 8) * 2), v[i]);
     }
   };
@@ -614,8 +627,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
 // fp32 output: same orientation with the fp32 MFMA (one k value per lane).  A lane loads 16
 // bytes of its query row, a[16m + 4g .. +3]; k-step 4m+e uses a = 16m + 4g + e on both
 // operands.  The normaliser phi(q).z is a plain fp32 dot product.
-template <int D>
-__global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
+template <int D, class TB>
+__global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
   constexpr int LD = D + 4;
   constexpr int NC = D / 16;
   constexpr int64_t QT = nc_queries(D, 0);  // queries per workgroup
@@ -627,6 +640,9 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t tiles = (a.n + QT - 1) / QT;
   const int64_t bh = blockIdx.x / tiles;
+  const HeadSpan sp = head_span(tb, a.n, bh);
+  if ((blockIdx.x % tiles) * QT >= sp.n) return;  // a tile past a shorter sequence's end
+  const int64_t n = sp.n;
   const int64_t q0 = (blockIdx.x % tiles) * QT + wave * QPW;
   constexpr int NKV4 = D * D / 1024;
   f32x4 kv4[NKV4];
@@ -643,8 +659,8 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
   if (tid < D) zs[tid] = zv;
   __syncthreads();
 
-  const float* Q = reinterpret_cast<const float*>(a.q) + bh * a.n * D;
-  float* O = reinterpret_cast<float*>(a.out) + bh * a.n * D;
+  const float* Q = reinterpret_cast<const float*>(a.q) + sp.row0 * D;
+  float* O = reinterpret_cast<float*>(a.out) + sp.row0 * D;
   for (int blk = 0; blk < QPW / 16; ++blk) {
     const int64_t row = q0 + blk * 16 + l16;
     f32x4 acc[NC];
@@ -653,7 +669,7 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
     float dpart = 0.f;
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) {
-      f32x4 qv = row < a.n ? *reinterpret_cast<const f32x4*>(Q + row * D + m * 16 + g * 4) : zero4();
+      f32x4 qv = row < n ? *reinterpret_cast<const f32x4*>(Q + row * D + m * 16 + g * 4) : zero4();
       float qf[4] = {phi(qv.x), phi(qv.y), phi(qv.z), phi(qv.w)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) dpart += qf[e] * zs[m * 16 + g * 4 + e];
@@ -667,7 +683,7 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
       }
     }
     float den = sum_over_groups(dpart);
-    if (row < a.n) {
+    if (row < n) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         f32x4 o = {acc[c][0] / den, acc[c][1] / den, acc[c][2] / den, acc[c][3] / den};
@@ -678,20 +694,28 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a) {
 }
 
 // ----------------------------------------------------------------------------- launchers
-template <int D>
-static hipError_t launch_kv_state_t(const KvStateArgs& a, int dtype, hipStream_t s) {
+template <int D, class TB>
+static void launch_kv_state_tb(const KvStateArgs& a, int dtype, hipStream_t s, const TB& tb) {
   const int64_t blocks = a.groups * a.slices;
   if (dtype == 1 && D == 64)
-    hipLaunchKernelGGL(kv_state_bf16_waves<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kv_state_bf16_waves<64, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
   else if (dtype == 1)
-    hipLaunchKernelGGL(kv_state_bf16<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kv_state_bf16<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
   else
-    hipLaunchKernelGGL(kv_state_f32<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kv_state_f32<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
+}
+
+template <int D>
+static hipError_t launch_kv_state_t(const KvStateArgs& a, int dtype, hipStream_t s, const SeqTable* tab) {
+  if (tab)
+    launch_kv_state_tb<D>(a, dtype, s, *tab);
+  else
+    launch_kv_state_tb<D>(a, dtype, s, NoTable{});
   return hipGetLastError();
 }
 
-hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s) {
-  return d == 64 ? launch_kv_state_t<64>(a, dtype, s) : launch_kv_state_t<128>(a, dtype, s);
+hipError_t launch_kv_state(const KvStateArgs& a, int d, int dtype, hipStream_t s, const SeqTable* tab) {
+  return d == 64 ? launch_kv_state_t<64>(a, dtype, s, tab) : launch_kv_state_t<128>(a, dtype, s, tab);
 }
 
 template <int D>
@@ -705,19 +729,27 @@ hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s) {
   return d == 64 ? launch_state_reduce_t<64>(a, s) : launch_state_reduce_t<128>(a, s);
 }
 
-template <int D>
-static hipError_t launch_nc_out_t(const NcOutArgs& a, int dtype, hipStream_t s) {
+template <int D, class TB>
+static void launch_nc_out_tb(const NcOutArgs& a, int dtype, hipStream_t s, const TB& tb) {
   const int64_t qt = nc_queries(D, dtype);
   const int64_t blocks = a.bh * ((a.n + qt - 1) / qt);
   if (dtype == 1)
-    hipLaunchKernelGGL(nc_out_bf16<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((nc_out_bf16<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
   else
-    hipLaunchKernelGGL(nc_out_f32<D>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((nc_out_f32<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
+}
+
+template <int D>
+static hipError_t launch_nc_out_t(const NcOutArgs& a, int dtype, hipStream_t s, const SeqTable* tab) {
+  if (tab)
+    launch_nc_out_tb<D>(a, dtype, s, *tab);
+  else
+    launch_nc_out_tb<D>(a, dtype, s, NoTable{});
   return hipGetLastError();
 }
 
-hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s) {
-  return d == 64 ? launch_nc_out_t<64>(a, dtype, s) : launch_nc_out_t<128>(a, dtype, s);
+hipError_t launch_nc_out(const NcOutArgs& a, int d, int dtype, hipStream_t s, const SeqTable* tab) {
+  return d == 64 ? launch_nc_out_t<64>(a, dtype, s, tab) : launch_nc_out_t<128>(a, dtype, s, tab);
 }
 
 }  // namespace la

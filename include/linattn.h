@@ -161,6 +161,33 @@ int la_causal_segments(const void* q, const void* k, const void* v, void* out,
                        int64_t chunk, int dtype, int64_t seg_len, void* stream);
 
 /*
+ * Variable-length batches: nseq sequences of n_s tokens each, every one laid out as the fixed
+ * layout's [H][n_s][d] block, the blocks packed back to back (sequence s starts at element
+ * H * cu_seqlens[s] * d).  cu_seqlens is a HOST array of nseq + 1 offsets in tokens:
+ * cu_seqlens[0] = 0, nondecreasing, n_s = cu_seqlens[s + 1] - cu_seqlens[s] (0 allowed);
+ * nseq <= 256 (LA_ERR_UNSUPPORTED above).  The library reads it during the call only.  Each
+ * sequence's result is that of the fixed-length call on it alone (up to rounding: the work is
+ * cut into slices and segments planned for the longest sequence).  q, k, v and out are
+ * [sum_s H n_s d] elements; other arguments and the workspace rules as for the fixed-length
+ * calls, with the workspace sizes below.  Bad offsets (not starting at 0, decreasing) give
+ * LA_ERR_SHAPE, a NULL cu_seqlens LA_ERR_NULL.
+ */
+size_t la_noncausal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
+                                           int64_t d, int dtype);
+
+int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, void* out,
+                                const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
+                                int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t la_causal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
+                                        int64_t d, int64_t chunk, int dtype);
+
+int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* out,
+                             const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
+                             int64_t chunk, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * One recurrent decode step for B*H independent heads, in place on the state
  * ("The recurrent view"; the fixed-size state of Active recall A5):
  *     S += phi(k) v^T ;  z += phi(k) ;  out = phi(q)^T S / phi(q)^T z
@@ -173,6 +200,16 @@ int la_causal_segments(const void* q, const void* k, const void* v, void* out,
  */
 int la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
                    int64_t B, int64_t H, int64_t d, int dtype, void* stream);
+
+/*
+ * la_decode_step for the sequences whose flag is set: active is a DEVICE array of B bytes
+ * (nonzero = active), read by the kernel, so it may change from step to step without a host
+ * synchronisation.  For an inactive sequence the state (S, z) and out are left as they were.
+ * active must not be NULL (LA_ERR_NULL) nor overlap out, S or z.
+ */
+int la_decode_step_masked(const void* q, const void* k, const void* v, float* S, float* z,
+                          void* out, const uint8_t* active, int64_t B, int64_t H, int64_t d,
+                          int dtype, void* stream);
 
 #ifdef __cplusplus
 }

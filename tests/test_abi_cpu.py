@@ -133,6 +133,35 @@ def test_validation_causal_state():
     assert _cs(lib, chunk=96, Sn=S, zn=Z) == -4
 
 
+def _cu(vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def test_validation_varlen():
+    lib = _lib()
+    nc = lambda cu, nseq, H=2, d=64, dtype=1, ws=0x100000, wsb=1 << 30, q=0x1000: lib.la_forward_noncausal_varlen(
+        P(q), P(0x2000), P(0x3000), P(0x4000), cu, nseq, H, d, dtype, P(ws), wsb, None)
+    ca = lambda cu, nseq, chunk=64, H=2, d=64, dtype=1: lib.la_forward_causal_varlen(
+        P(0x1000), P(0x2000), P(0x3000), P(0x4000), cu, nseq, H, d, chunk, dtype, P(0x100000), 1 << 30, None)
+    assert nc(None, 2) == -1                                   # no offsets
+    assert nc(_cu([1, 5, 9]), 2) == -2                         # not starting at 0
+    assert nc(_cu([0, 5, 3]), 2) == -2                         # decreasing
+    assert nc(_cu(list(range(258))), 257) == -4                # more than 256 sequences
+    assert nc(_cu([0, 5, 9]), 2, d=96) == -4
+    assert nc(_cu([0, 0, 0]), 2, q=0) == 0                     # no tokens: nothing to do
+    assert nc(_cu([0, 5, 9]), 2, q=0) == -1
+    assert nc(_cu([0, 5, 9]), 2, ws=0) == -6
+    assert ca(_cu([0, 5, 9]), 2, chunk=96) == -4
+    assert ca(_cu([0, 5, 3]), 2) == -2
+    # workspace: planned for the longest sequence
+    cu = [0, 100, 100, 5000]
+    assert ea.la_noncausal_varlen_workspace_bytes(cu, 4, 64, 1) == ea.la_noncausal_workspace_bytes(3, 4, 4900, 64, 1)
+    assert ea.la_causal_varlen_workspace_bytes([0, 70000], 1, 128, 128, 1) == ea.la_causal_workspace_bytes(1, 1, 70000, 128, 128, 1)
+    # masked decode needs its flags
+    assert lib.la_decode_step_masked(P(0x1000), P(0x2000), P(0x3000), P(0x10000), P(0x20000), P(0x4000), None,
+                                     1, 1, 64, 1, None) == -1
+
+
 def test_validation_decode():
     lib = _lib()
     assert _dec(lib, dtype=5) == -3

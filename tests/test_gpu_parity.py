@@ -422,6 +422,90 @@ def test_causal_state_empty_sequence(ea):
     assert torch.count_nonzero(Sn) == 0 and torch.count_nonzero(zn) == 0
 
 
+# ----------------------------------------------------------------------------- variable-length batches
+def _packed(seed, lengths, H, d, dtype, scale):
+    """Per-sequence inputs [H, n_s, d] and their packed form [sum_s H n_s, d] (sequence blocks
+    back to back)."""
+    seqs = [random_inputs(seed + 17 * i, (H, n, d), dtype, scale) for i, n in enumerate(lengths)]
+    packed = [np.concatenate([s[j].reshape(-1, d) for s in seqs]) for j in range(3)]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return seqs, packed, cu
+
+
+VARLEN = [("noncausal", "bf16", 64, 0), ("noncausal", "bf16", 128, 0), ("noncausal", "f32", 64, 0),
+          ("causal", "bf16", 128, 128), ("causal", "bf16", 64, 64), ("causal", "bf16", 64, 128),
+          ("causal", "f32", 64, 64), ("causal", "f32", 128, 64)]
+
+
+@pytest.mark.parametrize("form,dtype,d,chunk", VARLEN)
+def test_varlen_equals_each_sequence_alone(ea, form, dtype, d, chunk):
+    # a ragged batch (empty, one-token, chunk-edge and several-segment sequences) gives each
+    # sequence the result of the fixed-length call on it alone, and the oracle's
+    import torch
+    H = 3
+    lengths = [300, 0, 1, chunk + 1 if chunk else 65, 2500, 64, 1000]
+    scale = 1.0 if dtype == "f32" else 1.0 / np.sqrt(d)
+    seqs, (pq, pk, pv), cu = _packed(90 + d + chunk, lengths, H, d, dtype, scale)
+    tq, tk, tv = to_dev(pq, dtype), to_dev(pk, dtype), to_dev(pv, dtype)
+    say("varlen", form, dtype, d, chunk)
+    if form == "noncausal":
+        out = ea.la_forward_noncausal_varlen(tq, tk, tv, cu, H)
+    else:
+        out = ea.la_forward_causal_varlen(tq, tk, tv, cu, H, chunk=chunk)
+    g = from_dev(out, dtype)
+    for i, (n, (q, k, v)) in enumerate(zip(lengths, seqs)):
+        if n == 0:
+            continue
+        gs = g[H * cu[i]:H * cu[i + 1]].reshape(H, n, d)
+        ref = oracle_forward(form, q[None], k[None], v[None], dtype)[0]
+        assert normwise_err(gs, ref) <= TOL[dtype], (i, n)
+        alone = run_forward(ea, form, q[None], k[None], v[None], dtype, chunk or 64)[0]
+        assert normwise_err(gs, alone) <= TOL[dtype], (i, n)
+
+
+def test_varlen_many_sequences_long(ea):
+    # many sequences of mixed lengths, several segments for the longest, 128-token chunks
+    H, d = 4, 128
+    rng = np.random.default_rng(3)
+    lengths = [int(x) for x in rng.integers(0, 6000, size=24)]
+    seqs, (pq, pk, pv), cu = _packed(95, lengths, H, d, "bf16", 1.0 / np.sqrt(d))
+    tq, tk, tv = to_dev(pq, "bf16"), to_dev(pk, "bf16"), to_dev(pv, "bf16")
+    say("varlen many sequences")
+    for form in ("noncausal", "causal"):
+        out = (ea.la_forward_noncausal_varlen(tq, tk, tv, cu, H) if form == "noncausal"
+               else ea.la_forward_causal_varlen(tq, tk, tv, cu, H, chunk=128))
+        g = from_dev(out, "bf16")
+        for i in (0, 7, 23, int(np.argmax(lengths))):
+            n = lengths[i]
+            if n == 0:
+                continue
+            q, k, v = seqs[i]
+            gs = g[H * cu[i]:H * cu[i + 1]].reshape(H, n, d)
+            assert normwise_err(gs, oracle_forward(form, q[None], k[None], v[None], "bf16")[0]) <= TOL_BF16
+
+
+def test_decode_masked_skips_inactive_sequences(ea):
+    # active sequences step exactly as la_decode_step; inactive ones keep state and out
+    import torch
+    B, H, d = 5, 3, 128
+    q, k, v = random_inputs(96, (B, H, d), "bf16", 1.0 / np.sqrt(d))
+    S0 = torch.randn(B, H, d, d, device="cuda") * 0.01
+    z0 = torch.rand(B, H, d, device="cuda") + 1.0
+    active = torch.tensor([1, 0, 1, 1, 0], dtype=torch.uint8, device="cuda")
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    say("decode masked")
+    S1, z1 = S0.clone(), z0.clone()
+    full = ea.la_decode_step(tq, tk, tv, S1, z1)
+    S2, z2 = S0.clone(), z0.clone()
+    out = torch.full_like(full, 7.0)
+    ea.la_decode_step_masked(tq, tk, tv, S2, z2, active, out=out)
+    torch.cuda.synchronize()
+    on = active.bool()
+    assert torch.equal(out[on], full[on]) and torch.equal(S2[on], S1[on]) and torch.equal(z2[on], z1[on])
+    off = ~on
+    assert torch.all(out[off] == 7.0) and torch.equal(S2[off], S0[off]) and torch.equal(z2[off], z0[off])
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
 def test_state_sums_vs_oracle(ea, dtype, d):
     import torch
