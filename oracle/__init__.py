@@ -16,6 +16,9 @@ matmuls, not shrinking them", the two evaluation orders of "Worked example: the
 reassociation trick, by hand", and the recurrence of "The recurrent view: attention as an
 RNN".  Every oracle function is pinned by tests in ``tests/test_oracle_pins.py``; none is
 parity-unpinned.
+
+The FAVOR+ feature map (positive random features) lives in ``oracle/favor.py`` (numpy,
+fp64), pinned by ``tests/test_favor_oracle_pins.py``.
 """
 from __future__ import annotations
 

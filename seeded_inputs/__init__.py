@@ -21,6 +21,12 @@ tables, n = 65,536 with d_head = 128 and 32 heads in the long-context Q&A):
   C4 causal     bf16  B=4 H=32 n=65536 d=128 chunk 128 seed 4
   C5 decode     bf16  256 sequences x H=32, d=128, state from 1024 prior tokens, 512 steps,
                 seed 5
+FAVOR+ feature map (random features m; q, k, v N(0,1), feature scale d^(-1/4)):
+  F3 non-causal bf16  B=8 H=16 n=16384 d=64  m=256            seed 6
+  F4 causal     bf16  B=4 H=32 n=65536 d=128 m=128  chunk 64  seed 7
+  F5 decode     bf16  256 x 32 heads, d=128, m=128, 1024 prior tokens, 512 steps, seed 8
+The projection of a FAVOR+ workload is drawn by ``projection`` (i.i.d. N(0,1) rows) from
+the workload seed.
 """
 from __future__ import annotations
 
@@ -32,6 +38,7 @@ import numpy as np
 
 TAG_Q, TAG_K, TAG_V = 0, 1, 2
 TAG_PRIOR_K, TAG_PRIOR_V = 3, 4
+TAG_PROJ, TAG_PROJ_LEN = 5, 6
 
 
 @dataclass(frozen=True)
@@ -47,6 +54,7 @@ class Workload:
     seed: int
     scaled: bool       # N(0,1)/sqrt(d) when True, N(0,1) otherwise
     prior: int = 0     # decode only: tokens folded into the initial state
+    m: int = 0         # FAVOR+ workloads: random features (0: phi = elu + 1)
 
 
 WORKLOADS = {
@@ -55,6 +63,10 @@ WORKLOADS = {
     "C3": Workload("C3", "noncausal", "bf16", 8, 16, 16384, 64, 0, 3, True),
     "C4": Workload("C4", "causal", "bf16", 4, 32, 65536, 128, 128, 4, True),
     "C5": Workload("C5", "decode", "bf16", 256, 32, 512, 128, 0, 5, True, prior=1024),
+    # the same shapes with FAVOR+ features: unit-variance q, k, feature scale d^(-1/4)
+    "F3": Workload("F3", "noncausal", "bf16", 8, 16, 16384, 64, 0, 6, False, m=256),
+    "F4": Workload("F4", "causal", "bf16", 4, 32, 65536, 128, 64, 7, False, m=128),
+    "F5": Workload("F5", "decode", "bf16", 256, 32, 512, 128, 0, 8, False, prior=1024, m=128),
 }
 
 
@@ -170,3 +182,18 @@ def random_inputs(seed: int, shape, dtype: str = "f32", scale: float = 1.0):
         x = g.standard_normal(shape, dtype=np.float32) * np.float32(scale)
         res.append(encode(x, dtype))
     return tuple(res)
+
+
+def projection(seed: int, m: int, d: int, dtype: str) -> np.ndarray:
+    """A FAVOR+ projection [m, d] with i.i.d. N(0, 1) entries, in storage type."""
+    x = _stream(seed, TAG_PROJ, 0, 0).standard_normal((m, d), dtype=np.float32)
+    return encode(x, dtype)
+
+
+def orf_draws(seed: int, m: int, d: int):
+    """The Gaussian numbers an orthogonal random projection is built from: ceil(m/d) blocks
+    [d, d] and as many [d, d] blocks of length vectors, float64 N(0, 1)."""
+    nb = -(-m // d)
+    g = _stream(seed, TAG_PROJ, 1, 0).standard_normal((nb, d, d))
+    ln = _stream(seed, TAG_PROJ_LEN, 1, 0).standard_normal((nb, d, d))
+    return g, ln
