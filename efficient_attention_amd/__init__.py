@@ -1,4 +1,5 @@
-"""Kernelized linear attention (phi = elu + 1) for AMD Instinct MI355X (gfx950).
+"""Kernelized linear attention (phi = elu + 1, or FAVOR+ random features) for AMD Instinct
+MI355X (gfx950).
 
 The computation lives in hand-written HIP kernels behind the C ABI of include/linattn.h
 (liblinattn.so, built in-tree by ``python -m efficient_attention_amd.build``).  This package
@@ -16,6 +17,9 @@ from ._binding import (  # noqa: F401
     la_causal_workspace_bytes,
     la_decode_step,
     la_decode_step_masked,
+    la_favor_decode_step,
+    la_favor_forward_noncausal,
+    la_favor_noncausal_workspace_bytes,
     la_forward_causal,
     la_forward_causal_state,
     la_forward_causal_varlen,

@@ -26,7 +26,8 @@ EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
            "la_causal_plan", "la_state_sums_workspace_bytes", "la_state_sums",
            "la_causal_segments", "la_decode_step", "la_forward_causal_state",
            "la_noncausal_varlen_workspace_bytes", "la_forward_noncausal_varlen",
-           "la_causal_varlen_workspace_bytes", "la_forward_causal_varlen", "la_decode_step_masked")
+           "la_causal_varlen_workspace_bytes", "la_forward_causal_varlen", "la_decode_step_masked",
+           "la_favor_noncausal_workspace_bytes", "la_favor_forward_noncausal", "la_favor_decode_step")
 
 _lib = None
 _lock = threading.Lock()
@@ -85,6 +86,13 @@ def load():
         lib.la_causal_varlen_workspace_bytes.restype = SZ
         lib.la_forward_causal_varlen.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]
         lib.la_forward_causal_varlen.restype = I
+        F = ctypes.c_float
+        lib.la_favor_noncausal_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+        lib.la_favor_noncausal_workspace_bytes.restype = SZ
+        lib.la_favor_forward_noncausal.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I, P, SZ, P]
+        lib.la_favor_forward_noncausal.restype = I
+        lib.la_favor_decode_step.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, P]
+        lib.la_favor_decode_step.restype = I
         _lib = lib
     return _lib
 
@@ -399,4 +407,59 @@ def la_decode_step_masked(q, k, v, S, z, active, out=None, stream=None):
                                       out.data_ptr(), active.data_ptr(), B, H, d, _dtype_code(q), sh)
     if st != LA_OK:
         raise LinAttnError(st, "la_decode_step_masked")
+    return out
+
+
+# ---------------------------------------------------------------- FAVOR+ feature map
+def _check_proj(w, q):
+    if not isinstance(w, torch.Tensor) or w.dim() != 2 or w.shape[1] != q.shape[-1]:
+        raise ValueError("w must be a [m, d] tensor with d = %d" % q.shape[-1])
+    if w.dtype != q.dtype or w.device != q.device or not w.is_contiguous():
+        raise ValueError("w must be contiguous, with the dtype and device of q")
+    return int(w.shape[0])
+
+
+def la_favor_noncausal_workspace_bytes(B: int, H: int, n: int, d: int, m: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().la_favor_noncausal_workspace_bytes(B, H, n, d, m, code))
+
+
+def la_favor_forward_noncausal(q, k, v, w, scale: float, out=None, ws=None, stream=None):
+    """Non-causal attention with FAVOR+ features phi(x) = exp(W x' - |x'|^2/2)/sqrt(m), x' =
+    scale x, over [B, H, n, d] tensors and the projection w [m, d]; returns out."""
+    _check_qkv(q, k, v, 4)
+    m = _check_proj(w, q)
+    out = _out_like(q, out)
+    B, H, n, d = q.shape
+    code = _dtype_code(q)
+    sh = _stream_handle(q.device, stream)
+    need = la_favor_noncausal_workspace_bytes(B, H, n, d, m, code)
+    if ws is None:
+        ws = workspace(need, q.device, sh)
+    st = load().la_favor_forward_noncausal(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(), out.data_ptr(), B, H, n, d, m,
+        float(scale), code, ws.data_ptr() if ws is not None else None,
+        ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_favor_forward_noncausal")
+    return out
+
+
+def la_favor_decode_step(q, k, v, w, S, z, c, scale: float, out=None, stream=None):
+    """One FAVOR+ decode step over [B, H, d] tensors; the state (S [B, H, m, d], z [B, H, m],
+    c [B, H], fp32; true state exp(c) (S, z)) is updated in place; returns out."""
+    _check_qkv(q, k, v, 3)
+    m = _check_proj(w, q)
+    B, H, d = q.shape
+    for name, t, shape in (("S", S, (B, H, m, d)), ("z", z, (B, H, m)), ("c", c, (B, H))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s" % (name, shape, q.device))
+    out = _out_like(q, out)
+    sh = _stream_handle(q.device, stream)
+    st = load().la_favor_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(),
+                                     S.data_ptr(), z.data_ptr(), c.data_ptr(), out.data_ptr(),
+                                     B, H, d, m, float(scale), _dtype_code(q), sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_favor_decode_step")
     return out

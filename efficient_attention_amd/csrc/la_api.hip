@@ -144,6 +144,36 @@ int make_varlen(const int64_t* cu, int64_t nseq, int64_t H, int64_t d, int dtype
   return LA_OK;
 }
 
+// ---- FAVOR+ (positive random features)
+int check_favor(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m, int dtype, int64_t* bh,
+                size_t* bytes) {
+  int st = check_shape(B, H, n, d, dtype, bh, bytes);
+  if (st != LA_OK) return st;
+  if (m < 0) return LA_ERR_SHAPE;
+  if (dtype != LA_DTYPE_BF16 || !la::favor_supported(d, m)) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+bool scale_ok(float scale) { return scale > 0.f && scale <= 3.0e38f; }  // positive and finite
+
+// Stage-1 plan of the FAVOR+ state sums: groups of group_len tokens, each over `slices`
+// workgroups (at most 64, the reduction's limit) of a multiple of the tile.
+StatePlan plan_favor_state(int64_t groups, int64_t group_len, int d, int m) {
+  StatePlan p;
+  p.groups = groups;
+  const int64_t tiles = cdiv(group_len, la::kFavorTile);
+  const int64_t slices = clamp64(cdiv(kTargetStateBlocks, groups), 1, tiles < 64 ? tiles : 64);
+  p.slice_len = cdiv(tiles, slices) * la::kFavorTile;
+  p.slices = cdiv(group_len, p.slice_len);
+  p.scratch_bytes = (size_t)groups * (size_t)p.slices * (size_t)la::favor_rec(d, m) * sizeof(float);
+  return p;
+}
+
+// Non-causal FAVOR+ workspace: the per-slice partial records, then one record per head.
+size_t favor_nc_ws_bytes(const StatePlan& p, int d, int m) {
+  return round256(p.scratch_bytes) + (size_t)p.groups * (size_t)la::favor_rec(d, m) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,6 +191,7 @@ const char* la_status_string(int status) {
     case LA_ERR_WORKSPACE: return "workspace missing or too small";
     case LA_ERR_ALIAS: return "output overlaps an input, the state or the workspace";
     case LA_ERR_HIP: return "HIP kernel launch failed";
+    case LA_ERR_VALUE: return "invalid scalar argument (scale must be positive and finite)";
     default: return "unknown status";
   }
 }
@@ -539,6 +570,115 @@ int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* 
     ca.seg_parts = p.slices;
   }
   if (la::launch_causal(ca, (int)d, (int)chunk, dtype, s, &vl.tab) != hipSuccess) return LA_ERR_HIP;
+  return LA_OK;
+}
+
+// ---------------------------------------------------------------- FAVOR+
+size_t la_favor_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
+                                          int dtype) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  if (check_favor(B, H, n, d, m, dtype, &bh, &bytes) != LA_OK || bh == 0 || n == 0) return 0;
+  return favor_nc_ws_bytes(plan_favor_state(bh, n, (int)d, (int)m), (int)d, (int)m);
+}
+
+int la_favor_forward_noncausal(const void* q, const void* k, const void* v, const void* w,
+                               void* out, int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
+                               float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_favor(B, H, n, d, m, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (!scale_ok(scale)) return LA_ERR_VALUE;
+  if (bh == 0 || n == 0) return LA_OK;
+  if (!q || !k || !v || !w || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(out))
+    return LA_ERR_ALIGN;
+  const StatePlan p = plan_favor_state(bh, n, (int)d, (int)m);
+  const size_t need = favor_nc_ws_bytes(p, (int)d, (int)m);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  const size_t wbytes = (size_t)(m * d) * 2;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, w, wbytes) ||
+      overlaps(out, bytes, workspace, need))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * cdiv(n, la::kFavorQueries))) return LA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* parts = reinterpret_cast<float*>(ws);
+  float* states = reinterpret_cast<float*>(ws + round256(p.scratch_bytes));
+  la::FavorStateArgs ka;
+  ka.k = k;
+  ka.v = v;
+  ka.w = w;
+  ka.partials = parts;
+  ka.n = n;
+  ka.group_len = n;
+  ka.groups_per_head = 1;
+  ka.groups = bh;
+  ka.slices = p.slices;
+  ka.slice_len = p.slice_len;
+  ka.scale = scale;
+  if (la::launch_favor_kv_state(ka, (int)d, (int)m, s) != hipSuccess) return LA_ERR_HIP;
+  la::FavorReduceArgs ra;
+  ra.partials = parts;
+  ra.state = states;
+  ra.groups = bh;
+  ra.slices = p.slices;
+  if (la::launch_favor_reduce(ra, (int)d, (int)m, s) != hipSuccess) return LA_ERR_HIP;
+  la::FavorOutArgs oa;
+  oa.q = q;
+  oa.w = w;
+  oa.out = out;
+  oa.state = states;
+  oa.n = n;
+  oa.bh = bh;
+  oa.scale = scale;
+  if (la::launch_favor_out(oa, (int)d, (int)m, s) != hipSuccess) return LA_ERR_HIP;
+  return LA_OK;
+}
+
+int la_favor_decode_step(const void* q, const void* k, const void* v, const void* w, float* S,
+                         float* z, float* c, void* out, int64_t B, int64_t H, int64_t d, int64_t m,
+                         float scale, int dtype, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_favor(B, H, 1, d, m, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (!scale_ok(scale)) return LA_ERR_VALUE;
+  if (bh == 0) return LA_OK;
+  if (!q || !k || !v || !w || !S || !z || !c || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(S) ||
+      !aligned16(out) || ((uintptr_t)z & 3u) || ((uintptr_t)c & 3u))
+    return LA_ERR_ALIGN;
+  if (!grid_ok(bh)) return LA_ERR_SHAPE;
+  const size_t sb = (size_t)bh * (size_t)(m * d) * sizeof(float);
+  const size_t zb = (size_t)bh * (size_t)m * sizeof(float), cb = (size_t)bh * sizeof(float);
+  const size_t wbytes = (size_t)(m * d) * 2;
+  const void* ins[4] = {q, k, v, w};
+  const size_t inb[4] = {bytes, bytes, bytes, wbytes};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(out, bytes, ins[i], inb[i]) || overlaps(S, sb, ins[i], inb[i]) ||
+        overlaps(z, zb, ins[i], inb[i]) || overlaps(c, cb, ins[i], inb[i]))
+      return LA_ERR_ALIAS;
+  if (overlaps(out, bytes, S, sb) || overlaps(out, bytes, z, zb) || overlaps(out, bytes, c, cb) ||
+      overlaps(S, sb, z, zb) || overlaps(S, sb, c, cb) || overlaps(z, zb, c, cb))
+    return LA_ERR_ALIAS;
+  la::FavorDecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.w = w;
+  a.S = S;
+  a.z = z;
+  a.c = c;
+  a.out = out;
+  a.bh = bh;
+  a.scale = scale;
+  if (la::launch_favor_decode(a, (int)d, (int)m, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return LA_ERR_HIP;
   return LA_OK;
 }
 

@@ -1,0 +1,580 @@
+// la_favor.hip -- linear attention with the FAVOR+ feature map on gfx950: non-causal form
+// (state sums, their reduction, the output) and the recurrent decode step.
+//
+// Feature map.  "Efficient Transformers: Linear Attention and Flash Attention" (section "Linear
+// attention: reordering the matmuls, not shrinking them") names FAVOR+ (Choromanski et al.,
+// "Rethinking Attention with Performers") as the non-negative feature map whose inner products
+// approximate the softmax kernel; its positive random features are
+//     phi(x) = exp(W x' - |x'|^2 / 2) / sqrt(m),   x' = scale * x,   W [m][d],
+// and the attention is that of eq. Attention_i with this phi: out_i = phi(q_i)^T S / phi(q_i)^T z
+// with S = sum_j phi(k_j) v_j^T (m x d) and z = sum_j phi(k_j).
+//
+// Ranges.  The exponents w.x' - |x'|^2/2 can lie far outside fp32's range of exp, so no phi is
+// ever formed on its own scale:
+//   * keys: a state is stored as (S, z) with a log-scale c (true state = exp(c) (S, z)); the
+//     features of a tile enter as exp(u - c) with c the running maximum of the exponents u, and
+//     when a tile raises the maximum the accumulated sums are multiplied by exp(c_old - c_new)
+//     first.  Partial states of different token ranges are brought to their common maximum
+//     before they are added.
+//   * queries: phi(q) multiplies numerator and denominator alike, so any positive factor per
+//     query cancels; the output kernels use exp(scale (w.q - max_i w_i.q)), every feature <= 1,
+//     which also drops the |q'|^2/2 and 1/sqrt(m) factors.
+// Both are exact rewritings of the same quotient (no term is dropped), not approximations.
+//
+// MFMA use.  The projection W x is a dense contraction over d and goes through
+// v_mfma_f32_16x16x32_bf16 with W and x as bf16 operands (both are bf16 inputs: exact) and fp32
+// accumulation; the features are rounded to bf16 as the operand of the next product, as phi(K)
+// is in the elu + 1 kernels.  The result layout of the projection is arranged to be the operand
+// layout of the next product (see la_common.h), so features never go through LDS.
+#include <math.h>
+
+#include <type_traits>
+
+#include "la_common.h"
+#include "la_kernels.h"
+
+namespace la {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// sum of squares of 8 bf16 values, in fp32, fixed order
+__device__ __forceinline__ float sumsq_bf16x8(u32x4 x) {
+  float a = bf_lo(x.x), b = bf_hi(x.x), c = bf_lo(x.y), d = bf_hi(x.y);
+  float e = bf_lo(x.z), f = bf_hi(x.z), g = bf_lo(x.w), h = bf_hi(x.w);
+  return ((a * a + b * b) + (c * c + d * d)) + ((e * e + f * f) + (g * g + h * h));
+}
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// V tiles [rows][D] in LDS, 16-byte pieces permuted per row so that the transposed operand
+// reads (ld_v_rows) hit distinct bank groups: row r's piece b sits at piece b ^ 2((r / (128/D)) %
+// (D/16)).
+template <int D>
+__device__ __forceinline__ int vofs(int r, int c) {
+  constexpr int VRL = 128 / D;
+  return r * D + ((((c >> 3) ^ (2 * ((r / VRL) % (D / 16))))) << 3) + (c & 7);
+}
+// 16x16x32 operand with k over 32 rows of a V tile starting at row0, column col0 + l16: k slot
+// 4h + e is row row0 + 16h + 4g + e (the row order of an MFMA result, two 16-row tiles)
+template <int D>
+__device__ __forceinline__ u32x4 ld_v_rows(const uint16_t* Vt, int row0, int col0, int l16, int g) {
+  const uint16_t* p0 = Vt + vofs<D>(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3));
+  const u32x2 lo = ld_tr16(p0), hi = ld_tr16(p0 + 16 * D);
+  u32x4 r;
+  r.x = lo.x;
+  r.y = lo.y;
+  r.z = hi.x;
+  r.w = hi.y;
+  return r;
+}
+
+// ================================================================ stage 1: state sums
+// One workgroup (4 waves) sums the features of one token slice: S_p = sum_j phi(k_j) v_j^T,
+// z_p = sum_j phi(k_j), with log-scale c_p.  The slice streams through LDS in tiles of 32
+// tokens (double-buffered, one barrier per tile); wave w owns features [w M/4, (w+1) M/4):
+//   U = K_tile W_w^T on MFMA (A = token rows of K from LDS, B = this wave's rows of W, held in
+//       registers for the whole slice) -> lane holds u for feature l16 of each of its tiles and
+//       tokens 4g + r, 16 + 4g + r;
+//   u = scale U - (scale^2 |k|^2 / 2 + ln(M) / 2) per token; the wave's running maximum c_w;
+//   S_w += exp(u - c_w)^T V_tile and z_w += exp(u - c_w)^T 1 on MFMA, the exp values packed to
+//       bf16 as the A operand in the result's own layout, V read transposed from LDS in the
+//       same token order.
+// At the end the four waves' blocks are brought to the workgroup maximum and written.
+template <int D, int M>
+__global__ __launch_bounds__(256) void favor_kv_state(FavorStateArgs a) {
+  constexpr int T = kFavorTile;
+  constexpr int LDK = D + 16;
+  constexpr int KA = D / 32;        // k-steps of the projection
+  constexpr int DC = D / 16;        // value-column tiles
+  constexpr int FW = M / 4;         // features per wave
+  constexpr int FT = FW / 16;       // feature tiles per wave
+  constexpr int PPR = D / 8;        // 16-byte pieces per row
+  constexpr int RP = T * PPR / 256; // pieces per thread and tensor
+  constexpr int64_t REC = favor_rec(D, M);
+  static_assert(FT >= 1 && RP >= 1, "shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][T * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][T * D];
+  __shared__ __attribute__((aligned(16))) float kt[2][T];
+  __shared__ float cw_sh[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t grp = blockIdx.x / a.slices, sl = blockIdx.x % a.slices;
+  const int64_t bh = grp / a.groups_per_head, gi = grp % a.groups_per_head;
+  const int64_t gs = gi * a.group_len;
+  const int64_t ge = gs + a.group_len < a.n ? gs + a.group_len : a.n;
+  const int64_t t0 = gs + sl * a.slice_len;
+  const int64_t t1 = t0 + a.slice_len < ge ? t0 + a.slice_len : ge;
+  float* rec = a.partials + (int64_t)blockIdx.x * REC;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + bh * a.n * D;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + bh * a.n * D;
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w);
+
+  if (t0 >= t1) {  // an empty slice: the empty state
+    for (int64_t e = tid; e < (int64_t)M * D + M; e += 256) rec[e] = 0.f;
+    if (tid == 0) rec[(int64_t)M * D + M] = kNegInf;
+    return;
+  }
+
+  const float s = a.scale;
+  const float kconst = 0.5f * logf((float)M);  // ln(sqrt(M))
+  const float hs2 = 0.5f * s * s;
+
+  // this wave's rows of W as B operands: column = feature, k = d
+  u32x4 wr[FT][KA];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) wr[ft][ks] = ld16(W + (int64_t)(wave * FW + ft * 16 + l16) * D + ks * 32 + g * 8);
+
+  auto prow = [&](int p) { return tid / PPR + p * (256 / PPR); };
+  const int pcol = (tid % PPR) * 8;
+  u32x4 kr[RP], vr[RP];
+  auto load = [&](int64_t tt) {
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+      kr[p] = ld16_clamp(K, tt + prow(p), t1, D, pcol);
+      vr[p] = ld16_clamp(V, tt + prow(p), t1, D, pcol);
+    }
+  };
+  // tile to LDS; rows past the slice end get a zero V row and an exponent offset of +inf (so
+  // u = -inf and exp(u - c) = 0)
+  auto store = [&](int b, int64_t tt) {
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+      const int row = prow(p);
+      const bool ok = tt + row < t1;
+      st16(&Ks[b][row * LDK + pcol], kr[p]);
+      st16(&Vs[b][vofs<D>(row, pcol)], keep_if(vr[p], ok));
+      float ss = sumsq_bf16x8(kr[p]);
+#pragma unroll
+      for (int off = 1; off < PPR; off <<= 1) ss += __shfl_xor(ss, off);
+      if (tid % PPR == 0) kt[b][row] = ok ? hs2 * ss + kconst : __builtin_huge_valf();
+    }
+  };
+
+  f32x4 acc[FT][DC], accz[FT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    accz[ft] = zero4();
+#pragma unroll
+    for (int ct = 0; ct < DC; ++ct) acc[ft][ct] = zero4();
+  }
+  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
+  u32x4 ones;                          // B operand with a column of ones (column 0)
+  ones.x = ones.y = ones.z = ones.w = (l16 == 0) ? one2 : 0u;
+  float cw = kNegInf;
+
+  load(t0);
+  store(0, t0);
+  __syncthreads();
+  int b = 0;
+  for (int64_t tt = t0; tt < t1; tt += T, b ^= 1) {
+    load(tt + T);  // next tile (clamped rows past the end; stored but never counted)
+    u32x4 ka0[KA], ka1[KA];
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) {
+      ka0[ks] = ld16(&Ks[b][l16 * LDK + ks * 32 + g * 8]);
+      ka1[ks] = ld16(&Ks[b][(16 + l16) * LDK + ks * 32 + g * 8]);
+    }
+    const f32x4 kt0 = *reinterpret_cast<const f32x4*>(&kt[b][4 * g]);
+    const f32x4 kt1 = *reinterpret_cast<const f32x4*>(&kt[b][16 + 4 * g]);
+    f32x4 u0[FT], u1[FT];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      u0[ft] = zero4();
+      u1[ft] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KA; ++ks) {
+        u0[ft] = mfma_bf16(ka0[ks], wr[ft][ks], u0[ft]);
+        u1[ft] = mfma_bf16(ka1[ks], wr[ft][ks], u1[ft]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u0[ft][r] = s * u0[ft][r] - kt0[r];
+        u1[ft][r] = s * u1[ft][r] - kt1[r];
+        tmax = fmaxf(tmax, fmaxf(u0[ft][r], u1[ft][r]));
+      }
+    }
+    tmax = wave_max(tmax);
+    if (tmax > cw) {  // wave-uniform: rescale what this wave has summed to the new maximum
+      const float al = fexp(cw - tmax);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        accz[ft] *= al;
+#pragma unroll
+        for (int ct = 0; ct < DC; ++ct) acc[ft][ct] *= al;
+      }
+      cw = tmax;
+    }
+    u32x4 bv[DC];
+#pragma unroll
+    for (int ct = 0; ct < DC; ++ct) bv[ct] = ld_v_rows<D>(Vs[b], 0, ct * 16, l16, g);
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      u32x4 af;
+      af.x = pack_bf16(fexp(u0[ft][0] - cw), fexp(u0[ft][1] - cw));
+      af.y = pack_bf16(fexp(u0[ft][2] - cw), fexp(u0[ft][3] - cw));
+      af.z = pack_bf16(fexp(u1[ft][0] - cw), fexp(u1[ft][1] - cw));
+      af.w = pack_bf16(fexp(u1[ft][2] - cw), fexp(u1[ft][3] - cw));
+      accz[ft] = mfma_bf16(af, ones, accz[ft]);
+#pragma unroll
+      for (int ct = 0; ct < DC; ++ct) acc[ft][ct] = mfma_bf16(af, bv[ct], acc[ft][ct]);
+    }
+    store(b ^ 1, tt + T);
+    __syncthreads();
+  }
+
+  // common scale of the four waves' blocks
+  if (lane == 0) cw_sh[wave] = cw;
+  __syncthreads();
+  const float cmax = fmaxf(fmaxf(cw_sh[0], cw_sh[1]), fmaxf(cw_sh[2], cw_sh[3]));
+  const float be = cw == kNegInf ? 0.f : fexp(cw - cmax);
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const int f0 = wave * FW + ft * 16 + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < DC; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rec[(int64_t)(f0 + r) * D + ct * 16 + l16] = acc[ft][ct][r] * be;
+    if (l16 == 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rec[(int64_t)M * D + f0 + r] = accz[ft][r] * be;
+  }
+  if (tid == 0) rec[(int64_t)M * D + M] = cmax;
+}
+
+// ================================================================ stage 2: one state per group
+// state = sum_p exp(c_p - c) (S_p, z_p) with c = max_p c_p, slices added in order.  Eight
+// workgroups per group, each over an eighth of the record.
+template <int D, int M>
+__global__ __launch_bounds__(256) void favor_reduce(FavorReduceArgs a) {
+  constexpr int64_t REC = favor_rec(D, M);
+  constexpr int64_t BODY = (int64_t)M * D + M;  // multiple of 8
+  constexpr int64_t PART = BODY / 8;
+  constexpr int kMaxSlices = 64;
+  __shared__ float fac[kMaxSlices];
+  const int64_t grp = blockIdx.x / 8, part = blockIdx.x % 8;
+  const float* P = a.partials + grp * a.slices * REC;
+  float c = kNegInf;
+  for (int64_t p = 0; p < a.slices; ++p) c = fmaxf(c, P[p * REC + BODY]);
+  if (threadIdx.x < a.slices) {
+    const float cp = P[threadIdx.x * REC + BODY];
+    fac[threadIdx.x] = cp == kNegInf ? 0.f : fexp(cp - c);
+  }
+  __syncthreads();
+  float* out = a.state + grp * REC;
+  for (int64_t e = part * PART + threadIdx.x; e < (part + 1) * PART; e += 256) {
+    float acc = 0.f;
+    for (int64_t p = 0; p < a.slices; ++p) acc += fac[p] * P[p * REC + e];
+    out[e] = acc;
+  }
+  if (part == 0 && threadIdx.x == 0) out[BODY] = c;
+}
+
+// ================================================================ non-causal output
+// One workgroup (8 waves) per kFavorQueries queries of a head; a wave takes 16-query tiles.
+// LDS: the head's state transposed, St[c][f] = bf16(S[f][c]); a normaliser tile Zr with rows
+// bf16(z) and bf16(z - bf16(z)) (rows 2..15 zero); W [M][D].  Per tile, outputs transposed:
+//   U^T = W Q^T (A = rows of W, B = the lane's own query row from global memory): lane holds
+//       features 16 ft + 4g + r of query l16;
+//   f = exp(scale (U - max_f U)) packed to bf16 in the result layout, which is the B operand
+//       of the next product with k slot 4h + e = feature 32 j + 16 h + 4 g + e;
+//   out^T = St f (A = rows of St read in that feature order), den = Zr f; out = out^T / den.
+template <int D, int M>
+__global__ __launch_bounds__(512) void favor_out(FavorOutArgs a) {
+  constexpr int NT = 512;
+  constexpr int QT = (int)kFavorQueries;
+  constexpr int LDT = M + 8;        // St / Zr row stride: 4 (mod 64) dwords
+  constexpr int LDW = D + 16;
+  constexpr int KA = D / 32;
+  constexpr int DC = D / 16;
+  constexpr int MT = M / 16;        // feature tiles
+  constexpr int MJ = M / 32;        // k-steps over features
+  constexpr int64_t REC = favor_rec(D, M);
+
+  __shared__ __attribute__((aligned(16))) uint16_t St[D * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[M * LDW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  // all tiles of a head on one XCD (workgroups go to the 8 XCDs round-robin), so that its L2
+  // serves the head's state to every tile
+  const int64_t tiles = (a.n + QT - 1) / QT;
+  int64_t bh, tile;
+  if (a.bh % 8 == 0) {
+    const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+    bh = (j / tiles) * 8 + x;
+    tile = j % tiles;
+  } else {
+    bh = blockIdx.x / tiles;
+    tile = blockIdx.x % tiles;
+  }
+  const float* st = a.state + bh * REC;
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w);
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
+  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
+
+  // St[c][f], f in pairs: thread e covers (f = 2 (e / D), c = e % D)
+  for (int e = tid; e < M * D / 2; e += NT) {
+    const int f = 2 * (e / D), c = e % D;
+    *reinterpret_cast<uint32_t*>(&St[c * LDT + f]) = pack_bf16(st[f * D + c], st[(f + 1) * D + c]);
+  }
+  for (int e = tid; e < 16 * M; e += NT) {
+    const int row = e / M, f = e % M;
+    uint16_t val = 0;
+    if (row < 2) {
+      const float z = st[M * D + f];
+      const __bf16 hi = (__bf16)z;
+      val = row == 0 ? __builtin_bit_cast(uint16_t, hi) : __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
+    }
+    Zr[row * LDT + f] = val;
+  }
+  for (int e = tid; e < M * D / 8; e += NT) {
+    const int f = e / (D / 8), c = (e % (D / 8)) * 8;
+    st16(&Ws[f * LDW + c], ld16(W + f * D + c));
+  }
+  __syncthreads();
+
+  const float s = a.scale;
+  const int64_t qbase = tile * QT;
+  for (int qt = wave; qt < QT / 16; qt += NT / 64) {
+    const int64_t q0 = qbase + qt * 16;
+    if (q0 >= a.n) break;
+    u32x4 qb[KA];
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) qb[ks] = ld16_clamp(Q, q0 + l16, a.n, D, ks * 32 + g * 8);
+    f32x4 u[MT];
+    float mq = kNegInf;
+#pragma unroll
+    for (int ft = 0; ft < MT; ++ft) {
+      u[ft] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KA; ++ks) u[ft] = mfma_bf16(ld16(&Ws[(ft * 16 + l16) * LDW + ks * 32 + g * 8]), qb[ks], u[ft]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mq = fmaxf(mq, u[ft][r]);
+    }
+    mq = fmaxf(mq, __shfl_xor(mq, 16));
+    mq = fmaxf(mq, __shfl_xor(mq, 32));
+    u32x4 fq[MJ];
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+      fq[j].x = pack_bf16(fexp(s * (u[2 * j][0] - mq)), fexp(s * (u[2 * j][1] - mq)));
+      fq[j].y = pack_bf16(fexp(s * (u[2 * j][2] - mq)), fexp(s * (u[2 * j][3] - mq)));
+      fq[j].z = pack_bf16(fexp(s * (u[2 * j + 1][0] - mq)), fexp(s * (u[2 * j + 1][1] - mq)));
+      fq[j].w = pack_bf16(fexp(s * (u[2 * j + 1][2] - mq)), fexp(s * (u[2 * j + 1][3] - mq)));
+    }
+    f32x4 acco[DC];
+    f32x4 accd = zero4();
+#pragma unroll
+    for (int ct = 0; ct < DC; ++ct) acco[ct] = zero4();
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+#pragma unroll
+      for (int ct = 0; ct < DC; ++ct) {
+        const uint16_t* p = &St[(ct * 16 + l16) * LDT + 32 * j + 4 * g];
+        const u32x2 lo = ld8(p), hi = ld8(p + 16);
+        u32x4 as;
+        as.x = lo.x;
+        as.y = lo.y;
+        as.z = hi.x;
+        as.w = hi.y;
+        acco[ct] = mfma_bf16(as, fq[j], acco[ct]);
+      }
+      const uint16_t* p = &Zr[l16 * LDT + 32 * j + 4 * g];
+      const u32x2 lo = ld8(p), hi = ld8(p + 16);
+      u32x4 az;
+      az.x = lo.x;
+      az.y = lo.y;
+      az.z = hi.x;
+      az.w = hi.y;
+      accd = mfma_bf16(az, fq[j], accd);
+    }
+    const float den = __shfl(accd[0] + accd[1], l16);
+    const float inv = 1.0f / den;
+    // lane rows g and g ^ 1 swap halves of a column-tile pair (v_permlane16_swap) so that a lane
+    // holds 8 consecutive columns of one query: one 16-byte store
+    const int64_t row = q0 + l16;
+#pragma unroll
+    for (int ct = 0; ct < DC; ct += 2) {
+      const uint32_t ax = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
+      const uint32_t ay = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
+      const uint32_t bx = pack_bf16(acco[ct + 1][0] * inv, acco[ct + 1][1] * inv);
+      const uint32_t by = pack_bf16(acco[ct + 1][2] * inv, acco[ct + 1][3] * inv);
+      const auto sx = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
+      u32x4 o;
+      o.x = sx[0];
+      o.y = sy[0];
+      o.z = sx[1];
+      o.w = sy[1];
+      if (row < a.n) st16(O + row * D + (ct + (g & 1)) * 16 + 8 * (g >> 1), o);
+    }
+  }
+}
+
+// ================================================================ decode step
+// One workgroup per head, in place on (S, z, c):
+//   u_f = scale w_f.k - scale^2 |k|^2/2 - ln(M)/2,  c' = max(c, max_f u_f),  a = exp(c - c'),
+//   S' = a S + exp(u - c') v^T,  z' = a z + exp(u - c'),
+//   out = f^T S' / f^T z' with f = exp(scale (w.q - max_f w_f.q)).
+// The projections are fp32 dot products of the bf16 rows of W (read through L2; W is shared by
+// all heads) with k and q; the state update is a read-modify-write stream over S: each thread
+// owns 4 adjacent columns and M / RG rows, loads them all first, and keeps a running column
+// sum of f_a S'[a][c].  Sums are combined through LDS in a fixed order (bitwise reproducible).
+template <int D, int M>
+__global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
+  constexpr int CG = D / 4;         // column groups of 4
+  constexpr int RG = 256 / CG;      // row groups
+  constexpr int RPT = M / RG;       // rows per thread
+  __shared__ float qs[D], ks[D], vs[D];
+  __shared__ float fk[M], fq[M];
+  __shared__ float red[RG][D];
+  __shared__ float wk[4], wmk[4], wmq[4], wd[4];  // per-wave partials (one array per reduction)
+
+  const int64_t h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cg = tid % CG, rg = tid / CG;
+  float* S = a.S + h * M * D;
+
+  f32x4 sv[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) sv[r] = *reinterpret_cast<const f32x4*>(S + (int64_t)(rg + RG * r) * D + cg * 4);
+
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + h * D;
+  const uint16_t* k = reinterpret_cast<const uint16_t*>(a.k) + h * D;
+  const uint16_t* v = reinterpret_cast<const uint16_t*>(a.v) + h * D;
+  float kk = 0.f;
+  if (tid < D) {
+    qs[tid] = __uint_as_float((uint32_t)q[tid] << 16);
+    const float kv = __uint_as_float((uint32_t)k[tid] << 16);
+    ks[tid] = kv;
+    vs[tid] = __uint_as_float((uint32_t)v[tid] << 16);
+    kk = kv * kv;
+  }
+  // |k|^2: wave sums in lane order, then the waves in order
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) kk += __shfl_xor(kk, off);
+  if (lane == 0) wk[wave] = kk;
+  __syncthreads();
+  const float knorm = (wk[0] + wk[1]) + (wk[2] + wk[3]);
+  const float s = a.scale;
+  float uk = kNegInf, uq = kNegInf;
+  if (tid < M) {
+    const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.w) + (int64_t)tid * D;
+    float dk = 0.f, dq = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < D; c0 += 8) {
+      const u32x4 w8 = ld16(wrow + c0);
+      const float wv[8] = {bf_lo(w8.x), bf_hi(w8.x), bf_lo(w8.y), bf_hi(w8.y),
+                           bf_lo(w8.z), bf_hi(w8.z), bf_lo(w8.w), bf_hi(w8.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dk += wv[e] * ks[c0 + e];
+        dq += wv[e] * qs[c0 + e];
+      }
+    }
+    uk = s * dk - (0.5f * s * s * knorm + 0.5f * logf((float)M));
+    uq = dq;
+  }
+  const float mk = wave_max(uk), mq = wave_max(uq);
+  if (lane == 0) {
+    wmk[wave] = mk;
+    wmq[wave] = mq;
+  }
+  __syncthreads();
+  const float c_old = a.c[h];
+  const float umax = fmaxf(fmaxf(wmk[0], wmk[1]), fmaxf(wmk[2], wmk[3]));
+  const float qmax = fmaxf(fmaxf(wmq[0], wmq[1]), fmaxf(wmq[2], wmq[3]));
+  const float c_new = fmaxf(c_old, umax);
+  const float al = c_old == kNegInf ? 0.f : fexp(c_old - c_new);
+  float dpart = 0.f;
+  if (tid < M) {
+    const float ek = fexp(uk - c_new);
+    const float eq = fexp(s * (uq - qmax));
+    fk[tid] = ek;
+    fq[tid] = eq;
+    const float znew = al * a.z[h * M + tid] + ek;
+    a.z[h * M + tid] = znew;
+    dpart = eq * znew;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dpart += __shfl_xor(dpart, off);
+  if (lane == 0) wd[wave] = dpart;
+  __syncthreads();  // fk, fq and wd written; every thread has read c
+  if (tid == 0) a.c[h] = c_new;
+
+  const f32x4 v4 = *reinterpret_cast<const f32x4*>(&vs[cg * 4]);
+  f32x4 num = zero4();
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int row = rg + RG * r;
+    const float ka = fk[row], qa = fq[row];
+    sv[r] = sv[r] * al + ka * v4;
+    *reinterpret_cast<f32x4*>(S + (int64_t)row * D + cg * 4) = sv[r];
+    num += qa * sv[r];
+  }
+  *reinterpret_cast<f32x4*>(&red[rg][cg * 4]) = num;
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc += red[r][tid];
+    const float den = (wd[0] + wd[1]) + (wd[2] + wd[3]);
+    reinterpret_cast<__bf16*>(a.out)[h * D + tid] = (__bf16)(acc / den);
+  }
+}
+
+// ================================================================ launchers
+template <class F>
+static hipError_t favor_dispatch(int d, int m, F&& f) {
+  if (d == 64 && m == 64) f(std::integral_constant<int, 64>{}, std::integral_constant<int, 64>{});
+  else if (d == 64 && m == 128) f(std::integral_constant<int, 64>{}, std::integral_constant<int, 128>{});
+  else if (d == 64 && m == 256) f(std::integral_constant<int, 64>{}, std::integral_constant<int, 256>{});
+  else if (d == 128 && m == 64) f(std::integral_constant<int, 128>{}, std::integral_constant<int, 64>{});
+  else if (d == 128 && m == 128) f(std::integral_constant<int, 128>{}, std::integral_constant<int, 128>{});
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_favor_kv_state(const FavorStateArgs& a, int d, int m, hipStream_t s) {
+  return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
+    hipLaunchKernelGGL((favor_kv_state<decltype(Dc)::value, decltype(Mc)::value>),
+                       dim3((unsigned)(a.groups * a.slices)), dim3(256), 0, s, a);
+  });
+}
+
+hipError_t launch_favor_reduce(const FavorReduceArgs& a, int d, int m, hipStream_t s) {
+  return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
+    hipLaunchKernelGGL((favor_reduce<decltype(Dc)::value, decltype(Mc)::value>),
+                       dim3((unsigned)(a.groups * 8)), dim3(256), 0, s, a);
+  });
+}
+
+hipError_t launch_favor_out(const FavorOutArgs& a, int d, int m, hipStream_t s) {
+  const int64_t blocks = a.bh * ((a.n + kFavorQueries - 1) / kFavorQueries);
+  return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
+    hipLaunchKernelGGL((favor_out<decltype(Dc)::value, decltype(Mc)::value>), dim3((unsigned)blocks),
+                       dim3(512), 0, s, a);
+  });
+}
+
+hipError_t launch_favor_decode(const FavorDecodeArgs& a, int d, int m, hipStream_t s) {
+  return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
+    hipLaunchKernelGGL((favor_decode<decltype(Dc)::value, decltype(Mc)::value>), dim3((unsigned)a.bh),
+                       dim3(256), 0, s, a);
+  });
+}
+
+}  // namespace la

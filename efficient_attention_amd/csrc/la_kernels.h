@@ -93,6 +93,68 @@ hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
 // sn, zn = s0, z0 (zeros where s0, z0 are null) for every head: the final state of an empty sequence.
 hipError_t launch_state_copy(const CausalArgs& a, int d, hipStream_t s);
 
+// ---- FAVOR+ feature map (positive random features; la_favor.hip, la_favor_causal.hip)
+// phi(x) = exp(W x' - |x'|^2/2) / sqrt(m), x' = scale * x, W [m][d] bf16.  A state (S [m][d],
+// z [m]) is kept with a log-scale c: the true state is exp(c) * (S, z), so that the stored
+// values stay within fp32 range whatever the exponents; c = -inf with S = z = 0 is the empty
+// state.  State record of the internal partials: S, z, c, then 3 unused floats.
+constexpr int64_t favor_rec(int d, int m) { return (int64_t)m * d + m + 4; }
+// (d, m) pairs with kernels: m * d <= 16384, m a multiple of 64
+constexpr bool favor_supported(int64_t d, int64_t m) {
+  return (d == 64 && (m == 64 || m == 128 || m == 256)) || (d == 128 && (m == 64 || m == 128));
+}
+constexpr int kFavorTile = 32;        // favor_kv_state: tokens per tile
+constexpr int64_t kFavorQueries = 2048;  // favor_out: queries per workgroup
+
+struct FavorStateArgs {
+  const void* k;
+  const void* v;
+  const void* w;
+  float* partials;      // [groups][slices][favor_rec]
+  int64_t n;            // tokens per head
+  int64_t group_len;    // tokens per group (the last group of a head may be shorter)
+  int64_t groups_per_head;
+  int64_t groups;
+  int64_t slices;       // workgroups per group
+  int64_t slice_len;    // tokens per workgroup (multiple of kFavorTile)
+  float scale;
+};
+
+struct FavorReduceArgs {
+  const float* partials;  // [groups][slices][favor_rec]
+  float* state;           // [groups][favor_rec]
+  int64_t groups;
+  int64_t slices;
+};
+
+struct FavorOutArgs {
+  const void* q;
+  const void* w;
+  void* out;
+  const float* state;     // [bh][favor_rec]
+  int64_t n;
+  int64_t bh;
+  float scale;
+};
+
+struct FavorDecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* w;
+  float* S;               // [bh][m][d]
+  float* z;               // [bh][m]
+  float* c;               // [bh]
+  void* out;
+  int64_t bh;
+  float scale;
+};
+
+hipError_t launch_favor_kv_state(const FavorStateArgs& a, int d, int m, hipStream_t s);
+hipError_t launch_favor_reduce(const FavorReduceArgs& a, int d, int m, hipStream_t s);
+hipError_t launch_favor_out(const FavorOutArgs& a, int d, int m, hipStream_t s);
+hipError_t launch_favor_decode(const FavorDecodeArgs& a, int d, int m, hipStream_t s);
+
 // Queries per workgroup of the non-causal output kernel: 4 waves x 512, or 4 waves x 1024 for
 // bf16 with d = 128, whose workgroups fit only two per compute unit (LDS): 128 heads x 16K
 // queries are then one round of workgroups.

@@ -57,7 +57,8 @@ enum {
   LA_ERR_ALIGN = -5,       /* a base pointer is not 16-byte aligned                      */
   LA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes size  */
   LA_ERR_ALIAS = -7,       /* out overlaps an input (or the state)                       */
-  LA_ERR_HIP = -8          /* a kernel launch failed                                     */
+  LA_ERR_HIP = -8,         /* a kernel launch failed                                     */
+  LA_ERR_VALUE = -9        /* a scalar argument out of range (FAVOR+ scale)              */
 };
 
 /* ABI version of the loaded library (LA_ABI_VERSION at build time). */
@@ -210,6 +211,61 @@ int la_decode_step(const void* q, const void* k, const void* v, float* S, float*
 int la_decode_step_masked(const void* q, const void* k, const void* v, float* S, float* z,
                           void* out, const uint8_t* active, int64_t B, int64_t H, int64_t d,
                           int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * FAVOR+ feature map.  "Efficient Transformers: Linear Attention and Flash Attention" (section
+ * "Linear attention: reordering the matmuls, not shrinking them") names FAVOR+ (Choromanski et
+ * al., "Rethinking Attention with Performers") as the non-negative random-feature alternative to
+ * elu + 1 whose inner products approximate the softmax kernel exp(x . y).  Its positive random
+ * features are used here:
+ *     phi(x) = exp(W x' - |x'|^2 / 2) / sqrt(m),   x' = scale * x,
+ * with W the [m][d] projection (rows are Gaussian directions; the caller draws it, i.i.d. or in
+ * orthogonal blocks, and may redraw it between calls).  phi(q) . phi(k) then estimates
+ * exp(scale^2 q . k); scale = d^(-1/4) gives the kernel of softmax attention.  The attention is
+ * eq. Attention_i with this phi (out_i = phi(q_i)^T S / phi(q_i)^T z, S = sum_j phi(k_j) v_j^T
+ * [m][d], z = sum_j phi(k_j) [m]), over all keys or over j <= i.
+ *
+ * Supported: bf16 only (q, k, v, W, out; fp32 is LA_ERR_UNSUPPORTED), d = 64 with m in
+ * {64, 128, 256}, d = 128 with m in {64, 128} (m * d <= 16384); other (d, m) pairs return
+ * LA_ERR_UNSUPPORTED.  scale must be positive and finite (LA_ERR_VALUE).  W is read only, 16-byte
+ * aligned, and shared by all heads.
+ *
+ * State with a log-scale.  The exponents of phi leave fp32's range for large inputs, so a state
+ * handed across the ABI is (S [m][d], z [m], c) with the true state exp(c) * (S, z).  The empty
+ * state is S = 0, z = 0, c = -infinity.  The kernels keep every stored value within range by
+ * moving the scale into c (exact rewriting, nothing is dropped).
+ * ------------------------------------------------------------------------------------- */
+
+/* Workspace bytes of la_favor_forward_noncausal for this shape (0 for an empty or invalid one). */
+size_t la_favor_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
+                                          int dtype);
+
+/*
+ * Non-causal FAVOR+ attention: out_i = phi(q_i)^T S / phi(q_i)^T z over all n keys of the head.
+ *   q, k, v, out : [B][H][n][d] bf16; out must not overlap q, k, v, w or the workspace
+ *   w            : [m][d] bf16 projection
+ *   workspace    : at least la_favor_noncausal_workspace_bytes bytes, 16-byte aligned, owned by
+ *                  the caller; its contents on entry do not matter
+ */
+int la_favor_forward_noncausal(const void* q, const void* k, const void* v, const void* w,
+                               void* out, int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
+                               float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * One FAVOR+ decode step for B*H heads, in place on the state ("The recurrent view"):
+ *     S += phi(k) v^T ;  z += phi(k) ;  out = phi(q)^T S / phi(q)^T z   (update first)
+ * with the state kept as exp(c) * (S, z) (c moves to the larger exponent when a key needs it).
+ *   q, k, v, out : [B][H][d] bf16
+ *   w            : [m][d] bf16
+ *   S [B][H][m][d], z [B][H][m], c [B][H] : fp32, read and written in place; S 16-byte aligned,
+ *                  z and c 4-byte aligned; start from the empty state (zeros, c = -infinity) or
+ *                  from a state written by la_favor_forward_causal
+ * No two of out, S, z, c may overlap, nor any of them q, k, v or w (LA_ERR_ALIAS).
+ */
+int la_favor_decode_step(const void* q, const void* k, const void* v, const void* w, float* S,
+                         float* z, float* c, void* out, int64_t B, int64_t H, int64_t d, int64_t m,
+                         float scale, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

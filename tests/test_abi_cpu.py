@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert ea.la_abi_version() == _header_constant("LA_ABI_VERSION")
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = ea.la_status_string(code)
         assert isinstance(s, str) and s
     assert ea.la_status_string(-1000) == "unknown status"
@@ -205,3 +205,46 @@ def test_causal_plan_and_stage_validation():
     assert cs(sums=0) == -1                                   # several segments need sums
     assert cs(out=0x80000) == -7                              # out overlaps sums
     assert cs(n=0, q=0) == 0
+
+
+def _fnc(lib, q=0x1000, k=0x2000, v=0x3000, w=0x5000, out=0x4000, B=1, H=1, n=8, d=64, m=128,
+         scale=0.35, dtype=1, ws=0x100000, wsb=1 << 30):
+    return lib.la_favor_forward_noncausal(P(q), P(k), P(v), P(w), P(out), B, H, n, d, m, scale, dtype,
+                                          P(ws), wsb, None)
+
+
+def _fdec(lib, q=0x1000, k=0x2000, v=0x3000, w=0x5000, S=0x10000, z=0x80000, c=0x90000, out=0x4000,
+          B=1, H=1, d=64, m=128, scale=0.35, dtype=1):
+    return lib.la_favor_decode_step(P(q), P(k), P(v), P(w), P(S), P(z), P(c), P(out), B, H, d, m, scale,
+                                    dtype, None)
+
+
+def test_validation_favor():
+    lib = _lib()
+    assert _fnc(lib, dtype=0) == -4                           # fp32: not supported for FAVOR+
+    assert _fnc(lib, dtype=9) == -3
+    assert _fnc(lib, d=128, m=256) == -4                       # m * d above 16384
+    assert _fnc(lib, m=96) == -4
+    assert _fnc(lib, m=-1) == -2
+    assert _fnc(lib, scale=0.0) == -9
+    assert _fnc(lib, scale=float("inf")) == -9
+    assert _fnc(lib, scale=float("nan")) == -9
+    assert _fnc(lib, n=0, q=0, w=0) == 0                      # empty: no pointers needed
+    assert _fnc(lib, w=0) == -1
+    assert _fnc(lib, w=0x5008) == -5
+    assert _fnc(lib, ws=0) == -6
+    assert _fnc(lib, out=0x5000) == -7                         # out over the projection
+    assert _fnc(lib, out=0x100000 + 256) == -7                 # out inside the workspace
+    assert ea.la_favor_noncausal_workspace_bytes(1, 1, 8, 64, 128, 1) > 0
+    assert ea.la_favor_noncausal_workspace_bytes(1, 1, 8, 64, 128, 0) == 0
+    # one per-head record (S, z, c) at least
+    assert ea.la_favor_noncausal_workspace_bytes(8, 16, 16384, 64, 256, 1) >= 128 * (256 * 64 + 256 + 4) * 4
+    assert _fdec(lib, m=512) == -4
+    assert _fdec(lib, scale=-1.0) == -9
+    assert _fdec(lib, B=0, q=0) == 0
+    assert _fdec(lib, c=0) == -1
+    assert _fdec(lib, S=0x10004) == -5
+    assert _fdec(lib, z=0x80002) == -5                         # z needs 4-byte alignment only
+    assert _fdec(lib, out=0x10000) == -7                       # out over S
+    assert _fdec(lib, c=0x10000 + 64) == -7                    # c inside S
+    assert _fdec(lib, z=0x5000) == -7                          # z over the projection
