@@ -17,7 +17,9 @@ from ._binding import (  # noqa: F401
     la_causal_workspace_bytes,
     la_decode_step,
     la_decode_step_masked,
+    la_favor_causal_workspace_bytes,
     la_favor_decode_step,
+    la_favor_forward_causal,
     la_favor_forward_noncausal,
     la_favor_noncausal_workspace_bytes,
     la_forward_causal,

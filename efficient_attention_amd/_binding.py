@@ -27,7 +27,8 @@ EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
            "la_causal_segments", "la_decode_step", "la_forward_causal_state",
            "la_noncausal_varlen_workspace_bytes", "la_forward_noncausal_varlen",
            "la_causal_varlen_workspace_bytes", "la_forward_causal_varlen", "la_decode_step_masked",
-           "la_favor_noncausal_workspace_bytes", "la_favor_forward_noncausal", "la_favor_decode_step")
+           "la_favor_noncausal_workspace_bytes", "la_favor_forward_noncausal", "la_favor_decode_step",
+           "la_favor_causal_workspace_bytes", "la_favor_forward_causal")
 
 _lib = None
 _lock = threading.Lock()
@@ -93,6 +94,11 @@ def load():
         lib.la_favor_forward_noncausal.restype = I
         lib.la_favor_decode_step.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, P]
         lib.la_favor_decode_step.restype = I
+        lib.la_favor_causal_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64, I]
+        lib.la_favor_causal_workspace_bytes.restype = SZ
+        lib.la_favor_forward_causal.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I,
+                                                P, SZ, P]
+        lib.la_favor_forward_causal.restype = I
         _lib = lib
     return _lib
 
@@ -462,4 +468,46 @@ def la_favor_decode_step(q, k, v, w, S, z, c, scale: float, out=None, stream=Non
                                      B, H, d, m, float(scale), _dtype_code(q), sh)
     if st != LA_OK:
         raise LinAttnError(st, "la_favor_decode_step")
+    return out
+
+
+def la_favor_causal_workspace_bytes(B: int, H: int, n: int, d: int, m: int, chunk: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(load().la_favor_causal_workspace_bytes(B, H, n, d, m, chunk, code))
+
+
+def la_favor_forward_causal(q, k, v, w, scale: float, chunk: int = 64, out=None, final_state: bool = False,
+                            Sn=None, zn=None, cn=None, ws=None, stream=None):
+    """Causal attention with FAVOR+ features over [B, H, n, d] tensors.  Returns out, or with
+    final_state (out, Sn, zn, cn): the state after the last token as exp(cn) (Sn, zn)."""
+    _check_qkv(q, k, v, 4)
+    m = _check_proj(w, q)
+    B, H, n, d = q.shape
+    if final_state:
+        if Sn is None:
+            Sn = torch.empty((B, H, m, d), dtype=torch.float32, device=q.device)
+        if zn is None:
+            zn = torch.empty((B, H, m), dtype=torch.float32, device=q.device)
+        if cn is None:
+            cn = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        for name, t, shape in (("Sn", Sn, (B, H, m, d)), ("zn", zn, (B, H, m)), ("cn", cn, (B, H))):
+            if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() \
+                    or t.device != q.device:
+                raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s" % (name, shape, q.device))
+    else:
+        Sn = zn = cn = None
+    out = _out_like(q, out)
+    code = _dtype_code(q)
+    sh = _stream_handle(q.device, stream)
+    need = la_favor_causal_workspace_bytes(B, H, n, d, m, chunk, code)
+    if ws is None:
+        ws = workspace(need, q.device, sh)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = load().la_favor_forward_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                        ptr(Sn), ptr(zn), ptr(cn), B, H, n, d, m, chunk, float(scale), code,
+                                        ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, sh)
+    if st != LA_OK:
+        raise LinAttnError(st, "la_favor_forward_causal")
+    if final_state:
+        return out, Sn, zn, cn
     return out

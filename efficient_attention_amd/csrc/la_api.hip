@@ -174,6 +174,25 @@ size_t favor_nc_ws_bytes(const StatePlan& p, int d, int m) {
   return round256(p.scratch_bytes) + (size_t)p.groups * (size_t)la::favor_rec(d, m) * sizeof(float);
 }
 
+// Causal FAVOR+ plan: segments per head as for elu + 1 (chunk 64); the leading segments' state
+// sums need the workspace.
+struct FavorCausalPlan {
+  int64_t seg_len = 0, segs = 0;
+  StatePlan st;
+  size_t ws = 0;
+};
+
+FavorCausalPlan plan_favor_causal(int64_t bh, int64_t n, int d, int m) {
+  FavorCausalPlan p;
+  p.seg_len = causal_seg_len(bh, n, la::kFavorChunk);
+  p.segs = cdiv(n, p.seg_len);
+  if (p.segs > 1) {
+    p.st = plan_favor_state(bh * (p.segs - 1), p.seg_len, d, m);
+    p.ws = p.st.scratch_bytes;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -679,6 +698,104 @@ int la_favor_decode_step(const void* q, const void* k, const void* v, const void
   a.scale = scale;
   if (la::launch_favor_decode(a, (int)d, (int)m, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return LA_ERR_HIP;
+  return LA_OK;
+}
+
+size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
+                                       int64_t chunk, int dtype) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  if (check_favor(B, H, n, d, m, dtype, &bh, &bytes) != LA_OK || bh == 0 || n == 0) return 0;
+  if (chunk != la::kFavorChunk) return 0;
+  return plan_favor_causal(bh, n, (int)d, (int)m).ws;
+}
+
+int la_favor_forward_causal(const void* q, const void* k, const void* v, const void* w, void* out,
+                            float* Sn, float* zn, float* cn, int64_t B, int64_t H, int64_t n,
+                            int64_t d, int64_t m, int64_t chunk, float scale, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  int st = check_favor(B, H, n, d, m, dtype, &bh, &bytes);
+  if (st != LA_OK) return st;
+  if (chunk != la::kFavorChunk) return LA_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return LA_ERR_VALUE;
+  const bool fin = Sn || zn || cn;
+  if (fin && !(Sn && zn && cn)) return LA_ERR_NULL;
+  if (bh == 0) return LA_OK;
+  const size_t sb = (size_t)bh * (size_t)(m * d) * sizeof(float);
+  const size_t zb = (size_t)bh * (size_t)m * sizeof(float), cb = (size_t)bh * sizeof(float);
+  if (fin) {
+    if (!aligned16(Sn) || ((uintptr_t)zn & 3u) || ((uintptr_t)cn & 3u)) return LA_ERR_ALIGN;
+    if (overlaps(Sn, sb, zn, zb) || overlaps(Sn, sb, cn, cb) || overlaps(zn, zb, cn, cb)) return LA_ERR_ALIAS;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  la::FavorCausalArgs ca;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.w = w;
+  ca.out = out;
+  ca.seg_state = nullptr;
+  ca.seg_parts = 1;
+  ca.sn = Sn;
+  ca.zn = zn;
+  ca.cn = cn;
+  ca.n = n;
+  ca.bh = bh;
+  ca.segs = 1;
+  ca.seg_len = 0;
+  ca.scale = scale;
+  if (n == 0) {  // no tokens: the final state is the empty state
+    if (!fin) return LA_OK;
+    if (!grid_ok(bh)) return LA_ERR_SHAPE;
+    if (la::launch_favor_empty_state(ca, (int)d, (int)m, s) != hipSuccess) return LA_ERR_HIP;
+    return LA_OK;
+  }
+  if (!q || !k || !v || !w || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(out))
+    return LA_ERR_ALIGN;
+  const FavorCausalPlan p = plan_favor_causal(bh, n, (int)d, (int)m);
+  if (p.ws > 0) {
+    if (!workspace || workspace_bytes < p.ws) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_ALIGN;
+  }
+  const size_t wbytes = (size_t)(m * d) * 2;
+  const void* ins[4] = {q, k, v, w};
+  const size_t inb[4] = {bytes, bytes, bytes, wbytes};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(out, bytes, ins[i], inb[i])) return LA_ERR_ALIAS;
+    if (fin && (overlaps(Sn, sb, ins[i], inb[i]) || overlaps(zn, zb, ins[i], inb[i]) ||
+                overlaps(cn, cb, ins[i], inb[i])))
+      return LA_ERR_ALIAS;
+  }
+  if (overlaps(out, bytes, workspace, p.ws)) return LA_ERR_ALIAS;
+  if (fin && (overlaps(out, bytes, Sn, sb) || overlaps(out, bytes, zn, zb) || overlaps(out, bytes, cn, cb) ||
+              overlaps(Sn, sb, workspace, p.ws) || overlaps(zn, zb, workspace, p.ws) ||
+              overlaps(cn, cb, workspace, p.ws)))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(bh * p.segs) || (p.segs > 1 && !grid_ok(p.st.groups * p.st.slices))) return LA_ERR_SHAPE;
+  ca.segs = p.segs;
+  ca.seg_len = p.seg_len;
+  if (p.segs > 1) {
+    float* parts = reinterpret_cast<float*>(workspace);
+    la::FavorStateArgs ka;
+    ka.k = k;
+    ka.v = v;
+    ka.w = w;
+    ka.partials = parts;
+    ka.n = n;
+    ka.group_len = p.seg_len;
+    ka.groups_per_head = p.segs - 1;
+    ka.groups = p.st.groups;
+    ka.slices = p.st.slices;
+    ka.slice_len = p.st.slice_len;
+    ka.scale = scale;
+    if (la::launch_favor_kv_state(ka, (int)d, (int)m, s) != hipSuccess) return LA_ERR_HIP;
+    ca.seg_state = parts;
+    ca.seg_parts = p.st.slices;
+  }
+  if (la::launch_favor_causal(ca, (int)d, (int)m, s) != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
 }
 

@@ -536,6 +536,456 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
   }
 }
 
+// ================================================================ causal, chunked
+// One workgroup (8 waves) walks one segment of one head in chunks of C = 64 tokens, like the
+// elu + 1 chunked kernel (la_causal.hip): for the queries of a chunk
+//   num = f(Q) S_prev + tril(f(Q) phi(K_c)^T) V_c,  den = f(Q) z_prev + tril(...) 1,
+// then S += phi(K_c)^T V_c, z += phi(K_c)^T 1, with f(Q) the per-query-shifted features (the shift
+// cancels in num / den).  Scales: the state is kept on a log-scale c that moves up to the
+// largest key exponent seen so far (what is kept is multiplied by exp(c_old - c_new) when it
+// does); the chunk's key features are stored on their own token's scale m_j (largest exponent of
+// key j); and query i is evaluated on the scale P_i = max(c of the state it reads, m_j for the
+// chunk's keys j <= i), the largest exponent among the keys it attends to: every weight is then
+// at most 1 and the largest one is not below fp32's range, however far apart the exponents of
+// different tokens are.  So A_ij enters as (f(q_i) . phi~(k_j)) exp(m_j - P_i), the carried state
+// as exp(c_prev - P_i) S, and the state update as phi~(K)^T (exp(m_j - c) V).
+//
+// Feature order.  Features are stored in "operand order": stored feature q = 32 j + 8 g + 4 h + r
+// is feature p = 32 j + 16 h + 4 g + r.  An MFMA result lane (g, r) of feature tiles 2j and
+// 2j + 1 then writes 4 consecutive stored features, and the 8 k-slots a lane of group g gives a
+// 16x16x32 operand over features are 8 consecutive stored features (one 16-byte LDS read).  The
+// relabelling is the same in every tensor that carries a feature index (phi(K) tile, state, z,
+// query features), so the products are unchanged; the state is converted back to feature order
+// where it crosses the kernel's boundary.
+//
+// LDS (bf16 unless noted): Kf[C][M+16] phi(K_c) token-major; Vs[2][C][D] V of this chunk and the
+// next; St[D][M+16] the state transposed, St[c][q] = S[q][c]; Zr[16][M+16] rows bf16(z) and
+// bf16(z - bf16(z)); Ws[M][D+16] the projection.  Work per wave: query tile it (waves w and 7-w
+// share tile it = min(w, 7-w) and split the value columns); the same token tile and half of the
+// features for the next chunk's key projection; a block of the fp32 state accumulators (feature
+// tiles NAW (w % 4).., column tiles NCW (w / 4)..; waves 0..3 also keep z).
+__device__ __forceinline__ int favor_p_of_q(int q) {
+  return (q & ~31) + 16 * ((q >> 2) & 1) + 4 * ((q >> 3) & 3) + (q & 3);
+}
+
+template <int D, int M>
+__global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
+  constexpr int C = kFavorChunk;
+  constexpr int NT = 512;
+  constexpr int LDF = M + 16;      // 8 (mod 64) dwords
+  constexpr int LDW = D + 16;
+  constexpr int KA = D / 32;
+  constexpr int MT = M / 16;       // feature tiles
+  constexpr int MJ = M / 32;       // k-steps over features
+  constexpr int NI = C / 16;       // token tiles per chunk (4)
+  constexpr int NC = D / 16;       // value-column tiles
+  constexpr int NAW = MT / 4;      // state feature tiles per wave
+  constexpr int NCW = NC / 2;      // state column tiles per wave
+  constexpr int OCT = NC / 2;      // output column tiles per wave
+  constexpr int HF = MT / 2;       // key-projection feature tiles per wave
+  constexpr int KJ = C / 32;       // k-steps over the tokens of a chunk
+  constexpr int PPR = D / 8;
+  constexpr int RPV = C * PPR / NT;
+  constexpr int64_t REC = favor_rec(D, M);
+  static_assert(NAW >= 1 && RPV >= 1 && OCT % 2 == 0 && NI == 4, "shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Kf[C * LDF];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C * D];
+  __shared__ __attribute__((aligned(16))) uint16_t St[D * LDF];
+  __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDF];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[M * LDW];
+  __shared__ float wmax[8];
+  __shared__ __attribute__((aligned(16))) float tm[2][C];   // per-token maxima of the two feature halves
+  __shared__ __attribute__((aligned(16))) float mk[C];      // m_j of this chunk's keys
+  __shared__ float pm[C];                                    // P_i of this chunk's queries
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
+  const int64_t t0 = seg * a.seg_len;
+  if (t0 >= a.n) return;
+  const int64_t t1 = t0 + a.seg_len < a.n ? t0 + a.seg_len : a.n;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + bh * a.n * D;
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + bh * a.n * D;
+  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w);
+
+  const int it = wave < 4 ? wave : 7 - wave;  // query tile, and token tile of the key projection
+  const int oc0 = wave < 4 ? 0 : OCT;          // first output column tile
+  const int hf0 = wave < 4 ? 0 : HF;           // first key-projection feature tile
+  const int sa0 = NAW * (wave & 3), sc0 = NCW * (wave >> 2);
+  const bool zown = wave < 4;
+  const float s = a.scale;
+  const float kconst = 0.5f * logf((float)M);
+  const float hs2 = 0.5f * s * s;
+
+  for (int e = tid; e < M * D / 8; e += NT) {
+    const int f = e / (D / 8), c = (e % (D / 8)) * 8;
+    st16(&Ws[f * LDW + c], ld16(W + f * D + c));
+  }
+
+  // ---- initial state: the leading segments' partial sums, brought to their largest log-scale
+  f32x4 accS[NAW][NCW], accz[NAW];
+#pragma unroll
+  for (int i = 0; i < NAW; ++i) {
+    accz[i] = zero4();
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) accS[i][j] = zero4();
+  }
+  float c_cur = kNegInf;
+  const int64_t nparts = seg * a.seg_parts;
+  const float* parts = a.seg_state ? a.seg_state + bh * (a.segs - 1) * a.seg_parts * REC : nullptr;
+  for (int64_t p = 0; p < nparts; ++p) c_cur = fmaxf(c_cur, parts[p * REC + (int64_t)M * D + M]);
+  for (int64_t p = 0; p < nparts; ++p) {
+    const float* rp = parts + p * REC;
+    const float cp = rp[(int64_t)M * D + M];
+    const float fac = cp == kNegInf ? 0.f : fexp(cp - c_cur);
+#pragma unroll
+    for (int i = 0; i < NAW; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pf = favor_p_of_q((sa0 + i) * 16 + 4 * g + r);
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) accS[i][j][r] += fac * rp[(int64_t)pf * D + (sc0 + j) * 16 + l16];
+        if (zown && l16 == 0) accz[i][r] += fac * rp[(int64_t)M * D + pf];
+      }
+    }
+  }
+  auto write_state = [&]() {
+#pragma unroll
+    for (int i = 0; i < NAW; ++i)
+#pragma unroll
+      for (int j = 0; j < NCW; ++j) {
+        u32x2 w2;
+        w2.x = pack_bf16(accS[i][j][0], accS[i][j][1]);
+        w2.y = pack_bf16(accS[i][j][2], accS[i][j][3]);
+        *reinterpret_cast<u32x2*>(&St[((sc0 + j) * 16 + l16) * LDF + (sa0 + i) * 16 + g * 4]) = w2;
+      }
+    if (zown && l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < NAW; ++i) {
+        u32x2 hi2, lo2;
+        float hi[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hi[r] = (float)(__bf16)accz[i][r];
+        hi2.x = pack_bf16(hi[0], hi[1]);
+        hi2.y = pack_bf16(hi[2], hi[3]);
+        lo2.x = pack_bf16(accz[i][0] - hi[0], accz[i][1] - hi[1]);
+        lo2.y = pack_bf16(accz[i][2] - hi[2], accz[i][3] - hi[3]);
+        *reinterpret_cast<u32x2*>(&Zr[(sa0 + i) * 16 + g * 4]) = hi2;
+        *reinterpret_cast<u32x2*>(&Zr[LDF + (sa0 + i) * 16 + g * 4]) = lo2;
+      }
+    }
+  };
+  for (int e = tid; e < 14 * LDF; e += NT) Zr[2 * LDF + e] = 0;  // rows 2..15 stay zero
+
+  const uint32_t one2 = 0x3F803F80u;
+  u32x4 ones;
+  ones.x = ones.y = ones.z = ones.w = (l16 == 0) ? one2 : 0u;
+
+  // ---- per-chunk row loads: the wave's key and query rows as MFMA operands (lane l16 = token,
+  // k = 32 ks + 8 g), and 16-byte pieces of the V tile
+  u32x4 kb[KA], qr[KA], vv[RPV];
+  auto prow = [&](int p) { return tid / PPR + p * (NT / PPR); };
+  const int pcol = (tid % PPR) * 8;
+  auto load_kv = [&](int64_t c0) {
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) kb[ks] = ld16_clamp(K, c0 + it * 16 + l16, t1, D, ks * 32 + g * 8);
+#pragma unroll
+    for (int p = 0; p < RPV; ++p) vv[p] = ld16_clamp(V, c0 + prow(p), t1, D, pcol);
+  };
+  auto load_q = [&](int64_t c0) {
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) qr[ks] = ld16_clamp(Q, c0 + it * 16 + l16, t1, D, ks * 32 + g * 8);
+  };
+  auto store_v = [&](uint16_t* Vt, int64_t c0) {
+#pragma unroll
+    for (int p = 0; p < RPV; ++p) st16(&Vt[vofs<D>(prow(p), pcol)], keep_if(vv[p], c0 + prow(p) < t1));
+  };
+  // key projection of the loaded rows: u[ft][r] = exponent of feature 16 (hf0 + ft) + 4 g + r of
+  // token l16 (-inf past the segment end); returns the wave's maximum
+  f32x4 uk[HF];
+  auto key_exponents = [&](int64_t c0) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) ss += sumsq_bf16x8(kb[ks]);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const bool ok = c0 + it * 16 + l16 < t1;
+    const float off = ok ? hs2 * ss + kconst : __builtin_huge_valf();
+    float mx = kNegInf;
+#pragma unroll
+    for (int ft = 0; ft < HF; ++ft) {
+      uk[ft] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KA; ++ks)
+        uk[ft] = mfma_bf16(ld16(&Ws[((hf0 + ft) * 16 + l16) * LDW + ks * 32 + g * 8]), kb[ks], uk[ft]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uk[ft][r] = s * uk[ft][r] - off;
+        mx = fmaxf(mx, uk[ft][r]);
+      }
+    }
+    // this half's maximum for token l16 (lanes l16, l16 + 16, ...), and the wave's maximum
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) tm[wave < 4 ? 0 : 1][it * 16 + l16] = mx;
+    return wave_max(mx);
+  };
+  // phi(K) of the projected rows on their token's scale, into Kf (operand order); a token past
+  // the end (all exponents -inf) gets zero features
+  auto store_kf = [&]() {
+    const int t = it * 16 + l16;
+    const float mt = fmaxf(tm[0][t], tm[1][t]);
+    const float sh = mt == kNegInf ? 0.f : mt;
+#pragma unroll
+    for (int ft = 0; ft < HF; ++ft) {
+      const int f = hf0 + ft;
+      u32x2 w2;
+      w2.x = pack_bf16(fexp(uk[ft][0] - sh), fexp(uk[ft][1] - sh));
+      w2.y = pack_bf16(fexp(uk[ft][2] - sh), fexp(uk[ft][3] - sh));
+      *reinterpret_cast<u32x2*>(&Kf[t * LDF + 32 * (f >> 1) + 8 * g + 4 * (f & 1)]) = w2;
+    }
+  };
+  // m_j of the chunk and P_i = max(c_state, m_0..m_i), by wave 0 (prefix maximum over lanes)
+  auto scan_maxima = [&](float c_state) {
+    if (wave == 0) {
+      float x = fmaxf(tm[0][lane], tm[1][lane]);
+      mk[lane] = x;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x = fmaxf(x, y);
+      }
+      pm[lane] = fmaxf(x, c_state);
+    }
+  };
+
+  // ---- first chunk
+  load_kv(t0);
+  load_q(t0);
+  __syncthreads();  // Ws ready
+  {
+    const float m0 = key_exponents(t0);
+    if (lane == 0) wmax[wave] = m0;
+  }
+  store_v(Vs[0], t0);
+  __syncthreads();
+  float c_next = c_cur;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
+  float al = c_cur == kNegInf ? 0.f : fexp(c_cur - c_next);
+  store_kf();
+  scan_maxima(c_cur);
+  write_state();  // the initial state, on scale c_cur
+  float c_prev = c_cur;  // scale of the state in St
+  c_cur = c_next;        // scale of the state after this chunk
+
+  int buf = 0;
+  for (int64_t c0 = t0; c0 < t1; c0 += C, buf ^= 1) {
+    __syncthreads();  // Kf, Vs[buf], St, Zr of this chunk ready
+    const uint16_t* Vc = Vs[buf];
+    __builtin_amdgcn_sched_barrier(0);
+    load_kv(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // query features of this chunk's tile: U^T = W Q^T, f = exp(scale (U - max_f U))
+    u32x4 fq[MJ];
+    {
+      f32x4 uq[MT];
+      float mq = kNegInf;
+#pragma unroll
+      for (int ft = 0; ft < MT; ++ft) {
+        uq[ft] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KA; ++ks)
+          uq[ft] = mfma_bf16(ld16(&Ws[(ft * 16 + l16) * LDW + ks * 32 + g * 8]), qr[ks], uq[ft]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mq = fmaxf(mq, uq[ft][r]);
+      }
+      mq = fmaxf(mq, __shfl_xor(mq, 16));
+      mq = fmaxf(mq, __shfl_xor(mq, 32));
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        fq[j].x = pack_bf16(fexp(s * (uq[2 * j][0] - mq)), fexp(s * (uq[2 * j][1] - mq)));
+        fq[j].y = pack_bf16(fexp(s * (uq[2 * j][2] - mq)), fexp(s * (uq[2 * j][3] - mq)));
+        fq[j].z = pack_bf16(fexp(s * (uq[2 * j + 1][0] - mq)), fexp(s * (uq[2 * j + 1][1] - mq)));
+        fq[j].w = pack_bf16(fexp(s * (uq[2 * j + 1][2] - mq)), fexp(s * (uq[2 * j + 1][3] - mq)));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (i) state: rescale to this chunk's log-scale, then S += phi~(K_c)^T (e V_c), z += phi~(K_c)^T e
+    // with e_j = exp(m_j - c) for the tokens of the operands' k slots
+#pragma unroll
+    for (int i = 0; i < NAW; ++i) {
+      accz[i] *= al;
+#pragma unroll
+      for (int j = 0; j < NCW; ++j) accS[i][j] *= al;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KJ; ++ks) {
+      const f32x4 m_lo = *reinterpret_cast<const f32x4*>(&mk[ks * 32 + 4 * g]);
+      const f32x4 m_hi = *reinterpret_cast<const f32x4*>(&mk[ks * 32 + 16 + 4 * g]);
+      float e8[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e8[r] = fexp(m_lo[r] - c_cur);
+        e8[4 + r] = fexp(m_hi[r] - c_cur);
+      }
+      u32x4 bz;  // column 0: the factors; other columns zero
+      bz.x = pack_bf16(e8[0], e8[1]);
+      bz.y = pack_bf16(e8[2], e8[3]);
+      bz.z = pack_bf16(e8[4], e8[5]);
+      bz.w = pack_bf16(e8[6], e8[7]);
+      bz = keep_if(bz, zown && l16 == 0);
+      u32x4 bv[NCW];
+#pragma unroll
+      for (int j = 0; j < NCW; ++j) {
+        const u32x4 raw = ld_v_rows<D>(Vc, ks * 32, (sc0 + j) * 16, l16, g);
+        bv[j].x = pack_bf16(bf_lo(raw.x) * e8[0], bf_hi(raw.x) * e8[1]);
+        bv[j].y = pack_bf16(bf_lo(raw.y) * e8[2], bf_hi(raw.y) * e8[3]);
+        bv[j].z = pack_bf16(bf_lo(raw.z) * e8[4], bf_hi(raw.z) * e8[5]);
+        bv[j].w = pack_bf16(bf_lo(raw.w) * e8[6], bf_hi(raw.w) * e8[7]);
+      }
+#pragma unroll
+      for (int i = 0; i < NAW; ++i) {
+        const u32x4 ak = ld_rows_operand(Kf, LDF, ks * 32, (sa0 + i) * 16, l16, g);
+        accz[i] = mfma_bf16(ak, bz, accz[i]);
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_bf16(ak, bv[j], accS[i][j]);
+      }
+    }
+
+    // (ii) earlier chunks: S^T f and [z_hi; z_lo] f on the previous scale, then rescaled
+    f32x4 acco[OCT];
+    f32x4 accd = zero4();
+#pragma unroll
+    for (int ct = 0; ct < OCT; ++ct) acco[ct] = zero4();
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+#pragma unroll
+      for (int ct = 0; ct < OCT; ++ct)
+        acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], acco[ct]);
+      accd = mfma_bf16(ld16(&Zr[l16 * LDF + 32 * j + 8 * g]), fq[j], accd);
+    }
+    const float pq = pm[it * 16 + l16];  // P_i of this lane's query
+    {
+      const float sc = fexp(c_prev - pq);
+#pragma unroll
+      for (int ct = 0; ct < OCT; ++ct) acco[ct] *= sc;
+      accd *= sc;
+    }
+
+    // (iii) this chunk: A^T = phi(K_c) f^T masked to key <= query, then V^T A^T and ones A^T
+    auto a_tiles = [&](int m, f32x4& a0, f32x4& a1) {
+      a0 = zero4();
+      a1 = zero4();
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        a0 = mfma_bf16(ld16(&Kf[(2 * m * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], a0);
+        a1 = mfma_bf16(ld16(&Kf[((2 * m + 1) * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], a1);
+      }
+    };
+    auto pack_a = [&](int m, f32x4 a0, f32x4 a1) {
+      const f32x4 m0 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 4 * g]);
+      const f32x4 m1 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 16 + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        a0[r] *= fexp(m0[r] - pq);
+        a1[r] *= fexp(m1[r] - pq);
+        if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
+        if (2 * m + 1 > it || (2 * m + 1 == it && g * 4 + r > l16)) a1[r] = 0.f;
+      }
+      u32x4 af;
+      af.x = pack_bf16(a0[0], a0[1]);
+      af.y = pack_bf16(a0[2], a0[3]);
+      af.z = pack_bf16(a1[0], a1[1]);
+      af.w = pack_bf16(a1[2], a1[3]);
+      return af;
+    };
+    auto av_step = [&](int m, u32x4 af) {
+#pragma unroll
+      for (int ct = 0; ct < OCT; ++ct) acco[ct] = mfma_bf16(ld_v_rows<D>(Vc, m * 32, (oc0 + ct) * 16, l16, g), af, acco[ct]);
+      accd = mfma_bf16(ones, af, accd);
+    };
+    {
+      f32x4 a0, a1;
+      a_tiles(0, a0, a1);
+      if (it >= 2) {
+        const u32x4 af = pack_a(0, a0, a1);
+        a_tiles(1, a0, a1);
+        av_step(0, af);
+        av_step(1, pack_a(1, a0, a1));
+      } else {
+        av_step(0, pack_a(0, a0, a1));
+      }
+    }
+
+    const float den = __shfl(accd[0] + accd[1], l16);
+    const float inv = 1.0f / den;
+    const int64_t row = c0 + it * 16 + l16;
+#pragma unroll
+    for (int ct = 0; ct < OCT; ct += 2) {
+      const uint32_t ax = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
+      const uint32_t ay = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
+      const uint32_t bx = pack_bf16(acco[ct + 1][0] * inv, acco[ct + 1][1] * inv);
+      const uint32_t by = pack_bf16(acco[ct + 1][2] * inv, acco[ct + 1][3] * inv);
+      const auto sx = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
+      u32x4 o;
+      o.x = sx[0];
+      o.y = sy[0];
+      o.z = sx[1];
+      o.w = sy[1];
+      if (row < t1) st16(O + row * D + (oc0 + ct + (g & 1)) * 16 + 8 * (g >> 1), o);
+    }
+
+    // next chunk: key exponents and their maximum, V to the idle buffer
+    {
+      const float mn = key_exponents(c0 + C);
+      if (lane == 0) wmax[wave] = mn;
+    }
+    store_v(Vs[buf ^ 1], c0 + C);
+    __syncthreads();  // every wave is done with Kf, St, Zr of this chunk; the maxima are in
+    c_next = c_cur;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
+    al = fexp(c_cur - c_next);
+    store_kf();
+    scan_maxima(c_cur);
+    write_state();  // the state after this chunk, on scale c_cur
+    c_prev = c_cur;
+    c_cur = c_next;
+  }
+
+  // the state after the last token (scale c_cur), in feature order, from the last segment
+  if (a.sn && seg == (a.n - 1) / a.seg_len) {
+    float* sn = a.sn + bh * M * D;
+#pragma unroll
+    for (int i = 0; i < NAW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pf = favor_p_of_q((sa0 + i) * 16 + 4 * g + r);
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) sn[(int64_t)pf * D + (sc0 + j) * 16 + l16] = accS[i][j][r];
+        if (zown && l16 == 0) a.zn[bh * M + pf] = accz[i][r];
+      }
+    if (tid == 0) a.cn[bh] = c_cur;
+  }
+}
+
+template <int D, int M>
+__global__ __launch_bounds__(256) void favor_empty_state(FavorCausalArgs a) {
+  const int64_t h = blockIdx.x;
+  for (int e = threadIdx.x; e < M * D; e += 256) a.sn[h * M * D + e] = 0.f;
+  for (int e = threadIdx.x; e < M; e += 256) a.zn[h * M + e] = 0.f;
+  if (threadIdx.x == 0) a.cn[h] = kNegInf;
+}
+
 // ================================================================ launchers
 template <class F>
 static hipError_t favor_dispatch(int d, int m, F&& f) {
@@ -573,6 +1023,24 @@ hipError_t launch_favor_out(const FavorOutArgs& a, int d, int m, hipStream_t s) 
 hipError_t launch_favor_decode(const FavorDecodeArgs& a, int d, int m, hipStream_t s) {
   return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
     hipLaunchKernelGGL((favor_decode<decltype(Dc)::value, decltype(Mc)::value>), dim3((unsigned)a.bh),
+                       dim3(256), 0, s, a);
+  });
+}
+
+}  // namespace la
+
+namespace la {
+
+hipError_t launch_favor_causal(const FavorCausalArgs& a, int d, int m, hipStream_t s) {
+  return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
+    hipLaunchKernelGGL((favor_causal<decltype(Dc)::value, decltype(Mc)::value>),
+                       dim3((unsigned)(a.bh * a.segs)), dim3(512), 0, s, a);
+  });
+}
+
+hipError_t launch_favor_empty_state(const FavorCausalArgs& a, int d, int m, hipStream_t s) {
+  return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
+    hipLaunchKernelGGL((favor_empty_state<decltype(Dc)::value, decltype(Mc)::value>), dim3((unsigned)a.bh),
                        dim3(256), 0, s, a);
   });
 }

@@ -150,10 +150,32 @@ struct FavorDecodeArgs {
   float scale;
 };
 
+struct FavorCausalArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* w;
+  void* out;
+  const float* seg_state;  // [bh][segs-1][seg_parts][favor_rec]: the leading segments' sums (or null)
+  int64_t seg_parts;
+  float* sn;               // [bh][m][d], [bh][m], [bh]: the state after token n-1 with its
+  float* zn;               //   log-scale (all null: not written)
+  float* cn;
+  int64_t n;
+  int64_t bh;
+  int64_t segs;            // segments per head
+  int64_t seg_len;         // tokens per segment (multiple of kFavorChunk)
+  float scale;
+};
+constexpr int kFavorChunk = 64;  // favor_causal: tokens per chunk
+
 hipError_t launch_favor_kv_state(const FavorStateArgs& a, int d, int m, hipStream_t s);
 hipError_t launch_favor_reduce(const FavorReduceArgs& a, int d, int m, hipStream_t s);
 hipError_t launch_favor_out(const FavorOutArgs& a, int d, int m, hipStream_t s);
 hipError_t launch_favor_decode(const FavorDecodeArgs& a, int d, int m, hipStream_t s);
+hipError_t launch_favor_causal(const FavorCausalArgs& a, int d, int m, hipStream_t s);
+// sn, zn, cn = the empty state (zeros, c = -inf) for every head
+hipError_t launch_favor_empty_state(const FavorCausalArgs& a, int d, int m, hipStream_t s);
 
 // Queries per workgroup of the non-causal output kernel: 4 waves x 512, or 4 waves x 1024 for
 // bf16 with d = 128, whose workgroups fit only two per compute unit (LDS): 128 heads x 16K

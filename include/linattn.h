@@ -252,6 +252,27 @@ int la_favor_forward_noncausal(const void* q, const void* k, const void* v, cons
                                float scale, int dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Workspace bytes of la_favor_forward_causal (0: none needed, or an invalid shape). */
+size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
+                                       int64_t chunk, int dtype);
+
+/*
+ * Causal FAVOR+ attention (j <= i), chunked ("The recurrent view": the prefix sums S_i, z_i split
+ * at each chunk start into the carried state and the masked pairwise part inside the chunk).
+ *   q, k, v, out : [B][H][n][d] bf16; w : [m][d] bf16
+ *   chunk        : 64 (the only chunk of this form; others LA_ERR_UNSUPPORTED)
+ *   Sn, zn, cn   : all NULL, or all given: receive the state after token n-1 as
+ *                  exp(cn) * (Sn [B][H][m][d], zn [B][H][m]) fp32 (Sn 16-byte aligned, zn and cn
+ *                  4-byte aligned), the input of la_favor_decode_step; for n = 0 the empty state
+ *                  is written and q, k, v, w, out are not read.  Giving only some is LA_ERR_NULL.
+ *   workspace    : la_favor_causal_workspace_bytes bytes (may be NULL when that is 0)
+ * No output (out, Sn, zn, cn) may overlap another output, an input or the workspace.
+ */
+int la_favor_forward_causal(const void* q, const void* k, const void* v, const void* w, void* out,
+                            float* Sn, float* zn, float* cn, int64_t B, int64_t H, int64_t n,
+                            int64_t d, int64_t m, int64_t chunk, float scale, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * One FAVOR+ decode step for B*H heads, in place on the state ("The recurrent view"):
  *     S += phi(k) v^T ;  z += phi(k) ;  out = phi(q)^T S / phi(q)^T z   (update first)

@@ -248,3 +248,32 @@ def test_validation_favor():
     assert _fdec(lib, out=0x10000) == -7                       # out over S
     assert _fdec(lib, c=0x10000 + 64) == -7                    # c inside S
     assert _fdec(lib, z=0x5000) == -7                          # z over the projection
+
+
+def _fca(lib, q=0x1000, k=0x2000, v=0x3000, w=0x5000, out=0x4000, Sn=0, zn=0, cn=0, B=1, H=1, n=8, d=64,
+         m=128, chunk=64, scale=0.35, dtype=1, ws=0x100000, wsb=1 << 30):
+    return lib.la_favor_forward_causal(P(q), P(k), P(v), P(w), P(out), P(Sn or None), P(zn or None),
+                                       P(cn or None), B, H, n, d, m, chunk, scale, dtype, P(ws), wsb, None)
+
+
+def test_validation_favor_causal():
+    lib = _lib()
+    S, Z, C = 0x200000, 0x300000, 0x380000
+    assert _fca(lib, chunk=128) == -4                          # chunk 64 only
+    assert _fca(lib, dtype=0) == -4
+    assert _fca(lib, d=128, m=256) == -4
+    assert _fca(lib, scale=0.0) == -9
+    assert _fca(lib, Sn=S) == -1                               # zn, cn missing
+    assert _fca(lib, Sn=S, zn=Z) == -1
+    assert _fca(lib, Sn=S + 4, zn=Z, cn=C) == -5
+    assert _fca(lib, Sn=S, zn=Z + 2, cn=C) == -5
+    assert _fca(lib, Sn=S, zn=S + 64, cn=C) == -7              # zn inside Sn
+    assert _fca(lib, Sn=S, zn=Z, cn=C, out=Z) == -7            # out over zn
+    assert _fca(lib, Sn=S, zn=Z, cn=C, k=C) == -7              # cn over an input
+    assert _fca(lib, w=0) == -1
+    assert _fca(lib, out=0x5000) == -7                         # out over the projection
+    assert _fca(lib, B=0, Sn=S, zn=Z, cn=C) == 0               # no heads
+    assert _fca(lib, n=4096, ws=0) == -6                       # one head: segments need sums
+    assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 128, 64, 1) > 0
+    assert ea.la_favor_causal_workspace_bytes(64, 8, 4096, 64, 128, 64, 1) == 0  # one segment per head
+    assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 128, 128, 1) == 0  # invalid chunk

@@ -174,3 +174,105 @@ def test_favor_decode_is_bitwise_reproducible(ea):
         res.append((o, S.cpu().numpy(), z.cpu().numpy(), c.cpu().numpy()))
     for a, b in zip(res[0], res[1]):
         assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- causal
+CA_CASES = [
+    # B, H, n, d, m, projection
+    (1, 2, 1000, 64, 256, "iid"),     # 16 segments per head: leading-segment sums on every cut
+    (2, 3, 333, 64, 128, "orf"),
+    (1, 1, 31, 64, 64, "iid"),        # less than one chunk
+    (1, 1, 1, 128, 128, "orf"),       # one token
+    (1, 2, 2500, 128, 64, "iid"),
+    (2, 1, 777, 128, 128, "orf"),
+    (2, 4, 4096, 64, 256, "iid"),
+    (64, 4, 200, 128, 128, "iid"),    # one segment per head
+]
+
+
+def _causal_ref(Q, K, V, Wd, scale):
+    if Q.shape[-2] <= 2048:
+        return favor.quadratic(Q, K, V, Wd, scale, causal=True)
+    return favor.causal_recurrent(Q, K, V, Wd, scale)
+
+
+@pytest.mark.parametrize("B,H,n,d,m,kind", CA_CASES)
+def test_favor_causal_vs_oracle(ea, B, H, n, d, m, kind):
+    q, k, v = _inputs(600 + n + d + m, (B, H, n, d))
+    w = _proj(700 + m + d, m, d, kind)
+    scale = d ** -0.25
+    say("favor causal", B, H, n, d, m, kind)
+    out = from_dev(ea.la_favor_forward_causal(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                              to_dev(w, "bf16"), scale), "bf16")
+    ref = _causal_ref(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16"), scale)
+    err = normwise_err(out, ref)
+    say("  err", err)
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("amp,scale", [(4.0, 64 ** -0.25), (3.0, 1.0)])
+def test_favor_causal_exponents_beyond_fp32(ea, amp, scale):
+    B, H, n, d, m = 1, 2, 700, 64, 128
+    q, k, v = _inputs(41, (B, H, n, d), amp)
+    w = _proj(42, m, d, "iid")
+    say("favor causal large exponents", amp, scale)
+    out = from_dev(ea.la_favor_forward_causal(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                              to_dev(w, "bf16"), scale), "bf16")
+    ref = favor.quadratic(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16"), scale, causal=True)
+    assert np.all(np.isfinite(ref))
+    err = normwise_err(out, ref)
+    say("  err", err)
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("n,d,m", [(1000, 64, 256), (777, 128, 128), (64, 64, 64)])
+def test_favor_causal_final_state_then_decode(ea, n, d, m):
+    """Prefill with the final state, hand it to the decode step: outputs and the state after the
+    decode steps follow the recurrence over all n + steps tokens."""
+    torch = pytest.importorskip("torch")
+    B, H, steps = 2, 2, 8
+    q, k, v = _inputs(800 + n, (B, H, n + steps, d))
+    w = _proj(801 + m, m, d, "orf")
+    scale = d ** -0.25
+    tw = to_dev(w, "bf16")
+    pre = lambda x: to_dev(np.ascontiguousarray(x[:, :, :n]), "bf16")
+    say("favor causal final state", n, d, m)
+    out, S, z, c = ea.la_favor_forward_causal(pre(q), pre(k), pre(v), tw, scale, final_state=True)
+    Q, K, V, Wd = f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16")
+    ref, Sref, zref = favor.causal_recurrent(Q, K, V, Wd, scale, return_state=True)
+    _, Spre, zpre = favor.causal_recurrent(Q[:, :, :n], K[:, :, :n], V[:, :, :n], Wd, scale, return_state=True)
+    assert normwise_err(from_dev(out, "bf16"), ref[:, :, :n]) <= TOL_BF16
+    St, zt = _true_state(torch, S, z, c)
+    assert normwise_err(St, Spre) <= TOL_BF16
+    assert normwise_err(zt, zpre, head_axes_last=1) <= TOL_BF16
+    outs = _decode_run(ea, torch, q[:, :, n:], k[:, :, n:], v[:, :, n:], w, scale, S, z, c)
+    for i in range(steps):
+        assert normwise_err(outs[..., i, :], ref[:, :, n + i], head_axes_last=1) <= TOL_BF16, i
+    St, zt = _true_state(torch, S, z, c)
+    assert normwise_err(St, Sref) <= TOL_BF16
+
+
+def test_favor_causal_empty_sequence_state(ea):
+    torch = pytest.importorskip("torch")
+    B, H, d, m = 2, 3, 64, 128
+    q = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    w = to_dev(_proj(900, m, d, "iid"), "bf16")
+    Sn = torch.full((B, H, m, d), 7.0, dtype=torch.float32, device="cuda")
+    zn = torch.full((B, H, m), 7.0, dtype=torch.float32, device="cuda")
+    cn = torch.zeros((B, H), dtype=torch.float32, device="cuda")
+    say("favor causal empty")
+    ea.la_favor_forward_causal(q, q, q, w, 0.3, final_state=True, Sn=Sn, zn=zn, cn=cn)
+    torch.cuda.synchronize()
+    assert float(Sn.abs().max()) == 0.0 and float(zn.abs().max()) == 0.0
+    assert bool(torch.isinf(cn).all()) and float(cn.max()) < 0
+
+
+def test_favor_causal_last_row_equals_noncausal(ea):
+    B, H, n, d, m = 2, 2, 1500, 64, 256
+    q, k, v = _inputs(910, (B, H, n, d))
+    w = _proj(911, m, d, "iid")
+    tq, tk, tv, tw = (to_dev(x, "bf16") for x in (q, k, v, w))
+    say("favor causal vs noncausal last row")
+    oc = from_dev(ea.la_favor_forward_causal(tq, tk, tv, tw, 0.35), "bf16")
+    on = from_dev(ea.la_favor_forward_noncausal(tq, tk, tv, tw, 0.35), "bf16")
+    assert normwise_err(oc[:, :, -1:], on[:, :, -1:]) <= TOL_BF16
