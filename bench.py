@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
     python bench.py --grid      # the metric's grid of shapes, each forward alone (see run_grid)
+    python bench.py --favor     # the FAVOR+ feature map on the same shapes (see run_favor)
 
 One step = the whole hot path over one batch of each synthetic workload:
   * non-causal forward, bf16, B=8 H=16 n=16384 d=64 (feature map, split-n KV/z sums, output);
@@ -32,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA peak of MI355X
 METRIC = "tokens/sec + HBM GB/s (% peak), linear-attn fwd n=16K/64K, d=64/128, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "causal_bf16_d128_c128_traffic.txt")
 ROOFLINE_SOURCES = ["efficient_attention_amd/csrc/la_causal.hip", "efficient_attention_amd/csrc/la_common.h"]
@@ -194,6 +196,103 @@ def run_grid():
                       "grid": points}), flush=True)
 
 
+def favor_flops(form, n_tokens, d, m, chunk=64):
+    """Algorithmic MFMA work of the FAVOR+ forms per call (2 flops per multiply-add):
+    non-causal per head-token: key and query projections (2 * 2md), state update (2md + 2m),
+    output (2md + 2m); causal adds the masked pairwise part of a chunk on average (C/2 keys per
+    query: C m for the weights, C d for their product with V); decode per head: two projections,
+    the state update and the output (8md)."""
+    if form == "noncausal":
+        return n_tokens * (8 * m * d + 4 * m)
+    if form == "causal":
+        return n_tokens * (8 * m * d + 4 * m + chunk * m + chunk * d)
+    return n_tokens * 8 * m * d
+
+
+def run_favor():
+    """The FAVOR+ feature map on the same shapes as the elu + 1 workloads (seeded_inputs F3, F4,
+    F5): non-causal B=8 H=16 n=16384 d=64 m=256, causal B=4 H=32 n=65536 d=128 m=128 chunk 64,
+    one decode step for 256 x 32 heads d=128 m=128 from the state of 1024 prior tokens (written by
+    the causal forward).  q, k, v ~ N(0, 1) drawn on the device (seeded), projection i.i.d.
+    N(0, 1) from seeded_inputs, feature scale d^(-1/4).  Each call timed alone after a
+    cache-evicting read (median of 5), against its algorithmic HBM bytes and MFMA flops."""
+    import torch
+
+    import efficient_attention_amd as ea
+    from seeded_inputs import WORKLOADS, projection
+
+    dev = torch.device("cuda:0")
+    flush = torch.ones(1 << 28, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        times = []
+        for _ in range(5):
+            flush.sum()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    def draw(shape, tag):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(zlib.crc32(repr(("favor",) + tuple(shape) + (tag,)).encode()))
+        return torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
+
+    def wdev(w):
+        return torch.from_numpy(projection(w.seed, w.m, w.d, "bf16").view(np.int16)).view(torch.bfloat16).to(dev)
+
+    res = []
+
+    def report(name, w, ms, nbytes, flops, extra=None):
+        r = {"workload": name, "form": w.form, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "m": w.m,
+             "isolated_ms": ms, "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+             "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12,
+             "pct_bf16_mfma_peak": 100 * flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+             "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+             "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) else "mfma"}
+        if extra:
+            r.update(extra)
+        res.append(r)
+        print("[bench] favor %s" % json.dumps(r), file=sys.stderr, flush=True)
+
+    F3, F4, F5 = WORKLOADS["F3"], WORKLOADS["F4"], WORKLOADS["F5"]
+    for w in (F3, F4):
+        q, k, v = (draw((w.B, w.H, w.n, w.d), t) for t in range(3))
+        W = wdev(w)
+        out = torch.empty_like(q)
+        scale = w.d ** -0.25
+        if w.form == "noncausal":
+            ms = timed(lambda: ea.la_favor_forward_noncausal(q, k, v, W, scale, out=out))
+        else:
+            ms = timed(lambda: ea.la_favor_forward_causal(q, k, v, W, scale, chunk=w.chunk, out=out))
+        report(w.name, w, ms, algorithmic_bytes(w.B, w.H, w.n, w.d, 2),
+               favor_flops(w.form, w.B * w.H * w.n, w.d, w.m, w.chunk))
+        del q, k, v, out
+    # decode: state of 1024 prior tokens from the causal forward, then one step
+    w = F5
+    pq, pk, pv = (draw((w.B, w.H, w.prior, w.d), 10 + t) for t in range(3))
+    W = wdev(w)
+    scale = w.d ** -0.25
+    _, S, z, c = ea.la_favor_forward_causal(pq, pk, pv, W, scale, final_state=True)
+    del pq, pk, pv
+    q, k, v = (draw((w.B, w.H, w.d), 20 + t) for t in range(3))
+    out = torch.empty_like(q)
+    S0, z0, c0 = S.clone(), z.clone(), c.clone()
+    ms = timed(lambda: ea.la_favor_decode_step(q, k, v, W, S, z, c, scale, out=out))
+    BH = w.B * w.H
+    report(w.name, w, ms, BH * (2 * (w.m * w.d + w.m + 1) * 4 + 4 * w.d * 2), favor_flops("decode", BH, w.d, w.m),
+           {"note": "state [m][d] + z [m] + c fp32 read and written per head, q k v out bf16"})
+    print(json.dumps({"metric": METRIC, "mode": "favor", "n_gpus": 1,
+                      "data": "synthetic (seeded N(0,1) bf16 q/k/v on device, i.i.d. N(0,1) projection)",
+                      "favor": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +303,8 @@ def main():
                     help="also run one plain device copy of 2 GiB (reference for HBM counters)")
     ap.add_argument("--grid", action="store_true",
                     help="time every forward of the metric's shape grid instead of the step")
+    ap.add_argument("--favor", action="store_true",
+                    help="time the FAVOR+ feature map's forms on the same shapes instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -212,6 +313,9 @@ def main():
 
     if args.grid:
         run_grid()
+        return
+    if args.favor:
+        run_favor()
         return
 
     import torch

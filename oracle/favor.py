@@ -97,6 +97,21 @@ def quadratic(q, k, v, W, scale, causal):
     return (A @ _f64(v)) / A.sum(axis=-1, keepdims=True)
 
 
+def rows(q, k, v, W, scale, row_idx, causal):
+    """Selected output rows of ONE head ([n, d] inputs) by the definition: out_i = sum_j w_ij v_j /
+    sum_j w_ij, w_ij = phi(q_i) . phi(k_j), over all j (or j <= i when causal)."""
+    fk = features(k, W, scale)
+    v = _f64(v)
+    idx = np.asarray(row_idx, dtype=np.int64)
+    fq = features(_f64(q)[idx], W, scale)
+    out = np.empty((idx.size, v.shape[-1]))
+    for r, i in enumerate(idx):
+        end = int(i) + 1 if causal else fk.shape[0]
+        wts = fk[:end] @ fq[r]
+        out[r] = (wts @ v[:end]) / wts.sum()
+    return out
+
+
 def decode_step(q, k, v, S, z, W, scale):
     """One step of the recurrence per head, update first: S + phi(k) v^T, z + phi(k), then
     out = phi(q)^T S / phi(q)^T z.  q, k, v [..., d]; S [..., m, d]; z [..., m].  Returns

@@ -230,3 +230,13 @@ def test_decode_step_updates_before_reading():
     fk = favor.features(k, W, 1.0)
     np.testing.assert_allclose(S, np.outer(fk, v), rtol=1e-15)
     np.testing.assert_allclose(z, fk, rtol=1e-15)
+
+
+def test_rows_equal_the_full_forms():
+    W = projection(80, 32, 8, "f32").astype(np.float64)
+    q, k, v = (_gauss(s, (57, 8)) for s in (81, 82, 83))
+    idx = [0, 1, 17, 56]
+    np.testing.assert_allclose(favor.rows(q, k, v, W, 0.6, idx, causal=True),
+                               favor.quadratic(q, k, v, W, 0.6, causal=True)[idx], rtol=1e-12)
+    np.testing.assert_allclose(favor.rows(q, k, v, W, 0.6, idx, causal=False),
+                               favor.noncausal(q, k, v, W, 0.6)[idx], rtol=1e-12)

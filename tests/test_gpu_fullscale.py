@@ -210,3 +210,99 @@ def test_grid_point_full_size(ea, form, dtype, n, d):
             say("grid", form, dtype, n, d, "oracle head")
             whole = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
             assert normwise_err(G, whole) <= tol
+
+
+
+# ----------------------------------------------------------------------------- FAVOR+
+def _favor_forward(ea, name):
+    from oracle import favor
+    from seeded_inputs import projection
+    w = WORKLOADS[name]
+    say(name, "generating inputs", w)
+    q, k, v = forward_inputs(w)
+    wp = projection(w.seed, w.m, w.d, "bf16")
+    scale = w.d ** -0.25
+    tq, tk, tv, tw = (to_dev(x, "bf16") for x in (q, k, v, wp))
+    say(name, "GPU run")
+    if w.form == "noncausal":
+        out = ea.la_favor_forward_noncausal(tq, tk, tv, tw, scale)
+    else:
+        out = ea.la_favor_forward_causal(tq, tk, tv, tw, scale, chunk=w.chunk)
+    del tq, tk, tv
+    g = from_dev(out, "bf16")
+    assert np.all(np.isfinite(g))
+    Wd = f64(wp, "bf16")
+    causal = w.form == "causal"
+    # one whole head
+    b, h = w.B - 1, w.H - 1
+    say(name, "oracle head", b, h)
+    Q, K, V = (f64(x[b, h], "bf16") for x in (q, k, v))
+    ref = favor.causal_recurrent(Q, K, V, Wd, scale) if causal else favor.noncausal(Q, K, V, Wd, scale)
+    e = normwise_err(g[b, h], ref)
+    print("%s head (%d,%d) normwise err %.3e" % (name, b, h, e))
+    assert e <= TOL_BF16
+    # sampled rows of other heads, by the definition
+    rng = np.random.default_rng(8)
+    seg_len = ea.la_causal_plan(w.B, w.H, w.n, w.d, 64, 1) if causal else w.n
+    extra = [0, 1, w.n - 1, seg_len - 1, seg_len, seg_len + 1, 63, 64]
+    for _ in range(4):
+        b, h = int(rng.integers(0, w.B)), int(rng.integers(0, w.H))
+        rows = _sample_rows(w.n, extra, rng)
+        say(name, "oracle rows", b, h, len(rows))
+        Q, K, V = (f64(x[b, h], "bf16") for x in (q, k, v))
+        ref = favor.rows(Q, K, V, Wd, scale, rows, causal)
+        e = normwise_err(g[b, h][rows][None], ref[None])
+        assert e <= TOL_BF16, (b, h, e)
+
+
+def test_f3_favor_noncausal_full(ea):
+    _favor_forward(ea, "F3")
+
+
+def test_f4_favor_causal_full(ea):
+    _favor_forward(ea, "F4")
+
+
+def test_f5_favor_decode_full(ea):
+    """Prefill 1024 tokens per head with the causal forward (final state), then 6 decode steps
+    for all 8192 heads; sampled heads' outputs and states against the fp64 recurrence."""
+    import torch
+    from oracle import favor
+    from seeded_inputs import projection
+    w = WORKLOADS["F5"]
+    steps = 6
+    say("F5 generating inputs")
+    pk, pv, dq, dk, dv = decode_inputs(w, steps=steps)
+    rng = np.random.default_rng(9)
+    wp = projection(w.seed, w.m, w.d, "bf16")
+    scale = w.d ** -0.25
+    tw = to_dev(wp, "bf16")
+    tpk, tpv = to_dev(pk, "bf16"), to_dev(pv, "bf16")
+    say("F5 prefill")  # (the prefill's outputs are not used: its keys stand in for its queries)
+    _, S, z, c = ea.la_favor_forward_causal(tpk, tpk, tpv, tw, scale, final_state=True)
+    del tpk, tpv
+    outs = []
+    for i in range(steps):
+        o = ea.la_favor_decode_step(to_dev(np.ascontiguousarray(dq[:, :, i]), "bf16"),
+                                    to_dev(np.ascontiguousarray(dk[:, :, i]), "bf16"),
+                                    to_dev(np.ascontiguousarray(dv[:, :, i]), "bf16"), tw, S, z, c, scale)
+        outs.append(from_dev(o, "bf16"))
+    g = np.stack(outs, axis=2)
+    assert np.all(np.isfinite(g))
+    Wd = f64(wp, "bf16")
+    cs = c.cpu().numpy().astype(np.float64)
+    Ss = S.cpu().numpy()
+    zs = z.cpu().numpy()
+    heads = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(0, w.B)), int(rng.integers(0, w.H))) for _ in range(14)]
+    for (b, h) in heads:
+        K = np.concatenate([f64(pk[b, h], "bf16"), f64(dk[b, h], "bf16")])
+        V = np.concatenate([f64(pv[b, h], "bf16"), f64(dv[b, h], "bf16")])
+        Qd = f64(dq[b, h], "bf16")
+        S0, z0 = favor.state(K[: w.prior], V[: w.prior], Wd, scale)
+        ref, Sref, zref = favor.causal_recurrent(Qd, K[w.prior:], V[w.prior:], Wd, scale, s0=S0, z0=z0,
+                                                 return_state=True)
+        assert normwise_err(g[b, h], ref) <= TOL_BF16, (b, h)
+        St = Ss[b, h].astype(np.float64) * np.exp(cs[b, h])
+        zt = zs[b, h].astype(np.float64) * np.exp(cs[b, h])
+        assert normwise_err(St, Sref) <= TOL_BF16, (b, h)
+        assert normwise_err(zt[None], zref[None]) <= TOL_BF16, (b, h)
