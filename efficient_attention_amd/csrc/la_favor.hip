@@ -76,35 +76,48 @@ __device__ __forceinline__ u32x4 ld_v_rows(const uint16_t* Vt, int row0, int col
   return r;
 }
 
+// Feature relabelling used where features meet MFMA operands over the feature index: stored
+// feature q = 32 j + 8 g + 4 h + r is feature p = 32 j + 16 h + 4 g + r.  An MFMA result lane
+// (g, r) of feature tiles 2j and 2j + 1 holds the 4 + 4 features that are 8 consecutive stored
+// ones, and a 16x16x32 operand over features takes 8 consecutive stored features per lane group
+// (one 16-byte LDS read).
+__device__ __forceinline__ int favor_p_of_q(int q) {
+  return (q & ~31) + 16 * ((q >> 2) & 1) + 4 * ((q >> 3) & 3) + (q & 3);
+}
+
 // ================================================================ stage 1: state sums
-// One workgroup (4 waves) sums the features of one token slice: S_p = sum_j phi(k_j) v_j^T,
-// z_p = sum_j phi(k_j), with log-scale c_p.  The slice streams through LDS in tiles of 32
-// tokens (double-buffered, one barrier per tile); wave w owns features [w M/4, (w+1) M/4):
+// One workgroup (NW = 8 waves, or 4 when M = 64) sums the features of one token slice:
+// S_p = sum_j phi(k_j) v_j^T, z_p = sum_j phi(k_j), with log-scale c_p.  The slice streams
+// through LDS in tiles of 64 tokens (double-buffered, one barrier per tile); wave w owns the
+// 16 FT features from w M / NW:
 //   U = K_tile W_w^T on MFMA (A = token rows of K from LDS, B = this wave's rows of W, held in
-//       registers for the whole slice) -> lane holds u for feature l16 of each of its tiles and
-//       tokens 4g + r, 16 + 4g + r;
+//       registers for the whole slice) -> lane holds u for feature l16 of each of its feature
+//       tiles and tokens 16 tt + 4 g + r of the four token tiles tt;
 //   u = scale U - (scale^2 |k|^2 / 2 + ln(M) / 2) per token; the wave's running maximum c_w;
 //   S_w += exp(u - c_w)^T V_tile and z_w += exp(u - c_w)^T 1 on MFMA, the exp values packed to
-//       bf16 as the A operand in the result's own layout, V read transposed from LDS in the
-//       same token order.
-// At the end the four waves' blocks are brought to the workgroup maximum and written.
+//       bf16 as the A operand in the result's own layout (token tiles 2s, 2s + 1 form k-step s),
+//       V read transposed from LDS in the same token order.
+// At the end the waves' blocks are brought to the workgroup maximum and written.
 template <int D, int M>
-__global__ __launch_bounds__(256) void favor_kv_state(FavorStateArgs a) {
+__global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStateArgs a) {
+  constexpr int NW = M >= 128 ? 8 : 4;
+  constexpr int NT = 64 * NW;
   constexpr int T = kFavorTile;
+  constexpr int TT = T / 16;        // token tiles per tile
   constexpr int LDK = D + 16;
   constexpr int KA = D / 32;        // k-steps of the projection
   constexpr int DC = D / 16;        // value-column tiles
-  constexpr int FW = M / 4;         // features per wave
+  constexpr int FW = M / NW;        // features per wave
   constexpr int FT = FW / 16;       // feature tiles per wave
   constexpr int PPR = D / 8;        // 16-byte pieces per row
-  constexpr int RP = T * PPR / 256; // pieces per thread and tensor
+  constexpr int RP = T * PPR / NT;  // pieces per thread and tensor
   constexpr int64_t REC = favor_rec(D, M);
-  static_assert(FT >= 1 && RP >= 1, "shape");
+  static_assert(FT >= 1 && RP >= 1 && TT % 2 == 0, "shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][T * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][T * D];
   __shared__ __attribute__((aligned(16))) float kt[2][T];
-  __shared__ float cw_sh[4];
+  __shared__ float cw_sh[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(256) void favor_kv_state(FavorStateArgs a) {
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w);
 
   if (t0 >= t1) {  // an empty slice: the empty state
-    for (int64_t e = tid; e < (int64_t)M * D + M; e += 256) rec[e] = 0.f;
+    for (int64_t e = tid; e < (int64_t)M * D + M; e += NT) rec[e] = 0.f;
     if (tid == 0) rec[(int64_t)M * D + M] = kNegInf;
     return;
   }
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(256) void favor_kv_state(FavorStateArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KA; ++ks) wr[ft][ks] = ld16(W + (int64_t)(wave * FW + ft * 16 + l16) * D + ks * 32 + g * 8);
 
-  auto prow = [&](int p) { return tid / PPR + p * (256 / PPR); };
+  auto prow = [&](int p) { return tid / PPR + p * (NT / PPR); };
   const int pcol = (tid % PPR) * 8;
   u32x4 kr[RP], vr[RP];
   auto load = [&](int64_t tt) {
@@ -180,30 +193,24 @@ __global__ __launch_bounds__(256) void favor_kv_state(FavorStateArgs a) {
   int b = 0;
   for (int64_t tt = t0; tt < t1; tt += T, b ^= 1) {
     load(tt + T);  // next tile (clamped rows past the end; stored but never counted)
-    u32x4 ka0[KA], ka1[KA];
-#pragma unroll
-    for (int ks = 0; ks < KA; ++ks) {
-      ka0[ks] = ld16(&Ks[b][l16 * LDK + ks * 32 + g * 8]);
-      ka1[ks] = ld16(&Ks[b][(16 + l16) * LDK + ks * 32 + g * 8]);
-    }
-    const f32x4 kt0 = *reinterpret_cast<const f32x4*>(&kt[b][4 * g]);
-    const f32x4 kt1 = *reinterpret_cast<const f32x4*>(&kt[b][16 + 4 * g]);
-    f32x4 u0[FT], u1[FT];
+    f32x4 u[FT][TT];
     float tmax = kNegInf;
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      u0[ft] = zero4();
-      u1[ft] = zero4();
+    for (int ti = 0; ti < TT; ++ti) {
+      u32x4 ka[KA];
 #pragma unroll
-      for (int ks = 0; ks < KA; ++ks) {
-        u0[ft] = mfma_bf16(ka0[ks], wr[ft][ks], u0[ft]);
-        u1[ft] = mfma_bf16(ka1[ks], wr[ft][ks], u1[ft]);
-      }
+      for (int ks = 0; ks < KA; ++ks) ka[ks] = ld16(&Ks[b][(ti * 16 + l16) * LDK + ks * 32 + g * 8]);
+      const f32x4 ktv = *reinterpret_cast<const f32x4*>(&kt[b][ti * 16 + 4 * g]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u0[ft][r] = s * u0[ft][r] - kt0[r];
-        u1[ft][r] = s * u1[ft][r] - kt1[r];
-        tmax = fmaxf(tmax, fmaxf(u0[ft][r], u1[ft][r]));
+      for (int ft = 0; ft < FT; ++ft) {
+        u[ft][ti] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KA; ++ks) u[ft][ti] = mfma_bf16(ka[ks], wr[ft][ks], u[ft][ti]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u[ft][ti][r] = s * u[ft][ti][r] - ktv[r];
+          tmax = fmaxf(tmax, u[ft][ti][r]);
+        }
       }
     }
     tmax = wave_max(tmax);
@@ -217,28 +224,34 @@ __global__ __launch_bounds__(256) void favor_kv_state(FavorStateArgs a) {
       }
       cw = tmax;
     }
-    u32x4 bv[DC];
 #pragma unroll
-    for (int ct = 0; ct < DC; ++ct) bv[ct] = ld_v_rows<D>(Vs[b], 0, ct * 16, l16, g);
+    for (int st = 0; st < TT / 2; ++st) {
+      u32x4 bv[DC];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      u32x4 af;
-      af.x = pack_bf16(fexp(u0[ft][0] - cw), fexp(u0[ft][1] - cw));
-      af.y = pack_bf16(fexp(u0[ft][2] - cw), fexp(u0[ft][3] - cw));
-      af.z = pack_bf16(fexp(u1[ft][0] - cw), fexp(u1[ft][1] - cw));
-      af.w = pack_bf16(fexp(u1[ft][2] - cw), fexp(u1[ft][3] - cw));
-      accz[ft] = mfma_bf16(af, ones, accz[ft]);
+      for (int ct = 0; ct < DC; ++ct) bv[ct] = ld_v_rows<D>(Vs[b], st * 32, ct * 16, l16, g);
 #pragma unroll
-      for (int ct = 0; ct < DC; ++ct) acc[ft][ct] = mfma_bf16(af, bv[ct], acc[ft][ct]);
+      for (int ft = 0; ft < FT; ++ft) {
+        const f32x4 u0 = u[ft][2 * st], u1 = u[ft][2 * st + 1];
+        u32x4 af;
+        af.x = pack_bf16(fexp(u0[0] - cw), fexp(u0[1] - cw));
+        af.y = pack_bf16(fexp(u0[2] - cw), fexp(u0[3] - cw));
+        af.z = pack_bf16(fexp(u1[0] - cw), fexp(u1[1] - cw));
+        af.w = pack_bf16(fexp(u1[2] - cw), fexp(u1[3] - cw));
+        accz[ft] = mfma_bf16(af, ones, accz[ft]);
+#pragma unroll
+        for (int ct = 0; ct < DC; ++ct) acc[ft][ct] = mfma_bf16(af, bv[ct], acc[ft][ct]);
+      }
     }
     store(b ^ 1, tt + T);
     __syncthreads();
   }
 
-  // common scale of the four waves' blocks
+  // common scale of the waves' blocks
   if (lane == 0) cw_sh[wave] = cw;
   __syncthreads();
-  const float cmax = fmaxf(fmaxf(cw_sh[0], cw_sh[1]), fmaxf(cw_sh[2], cw_sh[3]));
+  float cmax = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) cmax = fmaxf(cmax, cw_sh[w]);
   const float be = cw == kNegInf ? 0.f : fexp(cw - cmax);
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
@@ -283,19 +296,21 @@ __global__ __launch_bounds__(256) void favor_reduce(FavorReduceArgs a) {
 }
 
 // ================================================================ non-causal output
-// One workgroup (8 waves) per kFavorQueries queries of a head; a wave takes 16-query tiles.
-// LDS: the head's state transposed, St[c][f] = bf16(S[f][c]); a normaliser tile Zr with rows
-// bf16(z) and bf16(z - bf16(z)) (rows 2..15 zero); W [M][D].  Per tile, outputs transposed:
+// One workgroup (8 waves) per kFavorQueries queries of a head; a wave takes 16-query tiles, the
+// query rows of its next tile in flight while it computes the current one.  LDS, features in
+// operand order (favor_p_of_q): the head's state transposed, St[c][q] = bf16(S[p(q)][c]); a
+// normaliser tile Zr with rows bf16(z) and bf16(z - bf16(z)) (rows 2..15 zero); W [M][D].  Per
+// tile, outputs transposed:
 //   U^T = W Q^T (A = rows of W, B = the lane's own query row from global memory): lane holds
 //       features 16 ft + 4g + r of query l16;
-//   f = exp(scale (U - max_f U)) packed to bf16 in the result layout, which is the B operand
-//       of the next product with k slot 4h + e = feature 32 j + 16 h + 4 g + e;
-//   out^T = St f (A = rows of St read in that feature order), den = Zr f; out = out^T / den.
+//   f = exp(scale (U - max_f U)) packed to bf16 in the result layout: the B operand of the next
+//       product, k slot e of lane group g = stored feature 32 j + 8 g + e;
+//   out^T = St f (A = 16-byte rows of St), den = Zr f; out = out^T / den.
 template <int D, int M>
 __global__ __launch_bounds__(512) void favor_out(FavorOutArgs a) {
   constexpr int NT = 512;
   constexpr int QT = (int)kFavorQueries;
-  constexpr int LDT = M + 8;        // St / Zr row stride: 4 (mod 64) dwords
+  constexpr int LDT = M + 16;       // St / Zr row stride: 8 (mod 64) dwords
   constexpr int LDW = D + 16;
   constexpr int KA = D / 32;
   constexpr int DC = D / 16;
@@ -325,102 +340,144 @@ __global__ __launch_bounds__(512) void favor_out(FavorOutArgs a) {
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w);
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + bh * a.n * D;
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
+  const int64_t qbase = tile * QT;
 
-  // St[c][f], f in pairs: thread e covers (f = 2 (e / D), c = e % D)
-  for (int e = tid; e < M * D / 2; e += NT) {
-    const int f = 2 * (e / D), c = e % D;
-    *reinterpret_cast<uint32_t*>(&St[c * LDT + f]) = pack_bf16(st[f * D + c], st[(f + 1) * D + c]);
+  // the first pass's query rows (tiles qt and qt + 8), before the set-up
+  u32x4 qb[KA], qb1[KA];
+  int qt = wave;
+#pragma unroll
+  for (int ks = 0; ks < KA; ++ks) {
+    qb[ks] = ld16_clamp(Q, qbase + qt * 16 + l16, a.n, D, ks * 32 + g * 8);
+    qb1[ks] = ld16_clamp(Q, qbase + (qt + NT / 64) * 16 + l16, a.n, D, ks * 32 + g * 8);
   }
-  for (int e = tid; e < 16 * M; e += NT) {
-    const int row = e / M, f = e % M;
-    uint16_t val = 0;
-    if (row < 2) {
-      const float z = st[M * D + f];
-      const __bf16 hi = (__bf16)z;
-      val = row == 0 ? __builtin_bit_cast(uint16_t, hi) : __builtin_bit_cast(uint16_t, (__bf16)(z - (float)hi));
-    }
-    Zr[row * LDT + f] = val;
+
+  // St[c][q], stored features in pairs (q even: p(q + 1) = p(q) + 1); Zr; W.  Every load of the
+  // set-up is issued before the first store, so the L2 latency is paid once.
+  constexpr int SP = M * D / 2 / NT;   // feature pairs per thread
+  constexpr int WP = M * D / 8 / NT;   // 16-byte pieces of W per thread
+  float sv[SP][2];
+  u32x4 wv[WP];
+#pragma unroll
+  for (int i = 0; i < SP; ++i) {
+    const int e = tid + i * NT;
+    const int pf = favor_p_of_q(2 * (e / D)), c = e % D;
+    sv[i][0] = st[pf * D + c];
+    sv[i][1] = st[(pf + 1) * D + c];
   }
-  for (int e = tid; e < M * D / 8; e += NT) {
-    const int f = e / (D / 8), c = (e % (D / 8)) * 8;
-    st16(&Ws[f * LDW + c], ld16(W + f * D + c));
+  const float zq = tid < M ? st[M * D + favor_p_of_q(tid)] : 0.f;
+#pragma unroll
+  for (int i = 0; i < WP; ++i) {
+    const int e = tid + i * NT;
+    wv[i] = ld16(W + (e / (D / 8)) * D + (e % (D / 8)) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < SP; ++i) {
+    const int e = tid + i * NT;
+    *reinterpret_cast<uint32_t*>(&St[(e % D) * LDT + 2 * (e / D)]) = pack_bf16(sv[i][0], sv[i][1]);
+  }
+  for (int e = tid; e < 16 * M; e += NT) Zr[(e / M) * LDT + e % M] = 0;
+#pragma unroll
+  for (int i = 0; i < WP; ++i) {
+    const int e = tid + i * NT;
+    st16(&Ws[(e / (D / 8)) * LDW + (e % (D / 8)) * 8], wv[i]);
+  }
+  __syncthreads();  // Zr cleared before its first two rows are written
+  if (tid < M) {
+    const __bf16 hi = (__bf16)zq;
+    Zr[tid] = __builtin_bit_cast(uint16_t, hi);
+    Zr[LDT + tid] = __builtin_bit_cast(uint16_t, (__bf16)(zq - (float)hi));
   }
   __syncthreads();
 
   const float s = a.scale;
-  const int64_t qbase = tile * QT;
-  for (int qt = wave; qt < QT / 16; qt += NT / 64) {
+  // two 16-query tiles per pass (tiles qt and qt + 8 of the workgroup's 128), so that each
+  // 16-byte LDS read of W, St and Zr feeds two MFMAs
+  for (; qt < QT / 16; qt += 2 * (NT / 64)) {
     const int64_t q0 = qbase + qt * 16;
     if (q0 >= a.n) break;
-    u32x4 qb[KA];
-#pragma unroll
-    for (int ks = 0; ks < KA; ++ks) qb[ks] = ld16_clamp(Q, q0 + l16, a.n, D, ks * 32 + g * 8);
-    f32x4 u[MT];
-    float mq = kNegInf;
+    const int64_t q1 = q0 + (NT / 64) * 16;
+    f32x4 u0[MT], u1[MT];
+    float m0 = kNegInf, m1 = kNegInf;
 #pragma unroll
     for (int ft = 0; ft < MT; ++ft) {
-      u[ft] = zero4();
+      u0[ft] = zero4();
+      u1[ft] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KA; ++ks) u[ft] = mfma_bf16(ld16(&Ws[(ft * 16 + l16) * LDW + ks * 32 + g * 8]), qb[ks], u[ft]);
+      for (int ks = 0; ks < KA; ++ks) {
+        const u32x4 wa = ld16(&Ws[(ft * 16 + l16) * LDW + ks * 32 + g * 8]);
+        u0[ft] = mfma_bf16(wa, qb[ks], u0[ft]);
+        u1[ft] = mfma_bf16(wa, qb1[ks], u1[ft]);
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mq = fmaxf(mq, u[ft][r]);
+      for (int r = 0; r < 4; ++r) {
+        m0 = fmaxf(m0, u0[ft][r]);
+        m1 = fmaxf(m1, u1[ft][r]);
+      }
     }
-    mq = fmaxf(mq, __shfl_xor(mq, 16));
-    mq = fmaxf(mq, __shfl_xor(mq, 32));
-    u32x4 fq[MJ];
+    // the next pass's rows in flight during this one
+    const int64_t qn0 = q0 + 2 * (NT / 64) * 16;
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) {
+      qb[ks] = ld16_clamp(Q, qn0 + l16, a.n, D, ks * 32 + g * 8);
+      qb1[ks] = ld16_clamp(Q, qn0 + (NT / 64) * 16 + l16, a.n, D, ks * 32 + g * 8);
+    }
+    m0 = fmaxf(m0, __shfl_xor(m0, 16));
+    m0 = fmaxf(m0, __shfl_xor(m0, 32));
+    m1 = fmaxf(m1, __shfl_xor(m1, 16));
+    m1 = fmaxf(m1, __shfl_xor(m1, 32));
+    u32x4 f0[MJ], f1[MJ];
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
-      fq[j].x = pack_bf16(fexp(s * (u[2 * j][0] - mq)), fexp(s * (u[2 * j][1] - mq)));
-      fq[j].y = pack_bf16(fexp(s * (u[2 * j][2] - mq)), fexp(s * (u[2 * j][3] - mq)));
-      fq[j].z = pack_bf16(fexp(s * (u[2 * j + 1][0] - mq)), fexp(s * (u[2 * j + 1][1] - mq)));
-      fq[j].w = pack_bf16(fexp(s * (u[2 * j + 1][2] - mq)), fexp(s * (u[2 * j + 1][3] - mq)));
+      f0[j].x = pack_bf16(fexp(s * (u0[2 * j][0] - m0)), fexp(s * (u0[2 * j][1] - m0)));
+      f0[j].y = pack_bf16(fexp(s * (u0[2 * j][2] - m0)), fexp(s * (u0[2 * j][3] - m0)));
+      f0[j].z = pack_bf16(fexp(s * (u0[2 * j + 1][0] - m0)), fexp(s * (u0[2 * j + 1][1] - m0)));
+      f0[j].w = pack_bf16(fexp(s * (u0[2 * j + 1][2] - m0)), fexp(s * (u0[2 * j + 1][3] - m0)));
+      f1[j].x = pack_bf16(fexp(s * (u1[2 * j][0] - m1)), fexp(s * (u1[2 * j][1] - m1)));
+      f1[j].y = pack_bf16(fexp(s * (u1[2 * j][2] - m1)), fexp(s * (u1[2 * j][3] - m1)));
+      f1[j].z = pack_bf16(fexp(s * (u1[2 * j + 1][0] - m1)), fexp(s * (u1[2 * j + 1][1] - m1)));
+      f1[j].w = pack_bf16(fexp(s * (u1[2 * j + 1][2] - m1)), fexp(s * (u1[2 * j + 1][3] - m1)));
     }
-    f32x4 acco[DC];
-    f32x4 accd = zero4();
+    f32x4 o0[DC], o1[DC];
+    f32x4 d0 = zero4(), d1 = zero4();
 #pragma unroll
-    for (int ct = 0; ct < DC; ++ct) acco[ct] = zero4();
+    for (int ct = 0; ct < DC; ++ct) {
+      o0[ct] = zero4();
+      o1[ct] = zero4();
+    }
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
 #pragma unroll
       for (int ct = 0; ct < DC; ++ct) {
-        const uint16_t* p = &St[(ct * 16 + l16) * LDT + 32 * j + 4 * g];
-        const u32x2 lo = ld8(p), hi = ld8(p + 16);
-        u32x4 as;
-        as.x = lo.x;
-        as.y = lo.y;
-        as.z = hi.x;
-        as.w = hi.y;
-        acco[ct] = mfma_bf16(as, fq[j], acco[ct]);
+        const u32x4 sa = ld16(&St[(ct * 16 + l16) * LDT + 32 * j + 8 * g]);
+        o0[ct] = mfma_bf16(sa, f0[j], o0[ct]);
+        o1[ct] = mfma_bf16(sa, f1[j], o1[ct]);
       }
-      const uint16_t* p = &Zr[l16 * LDT + 32 * j + 4 * g];
-      const u32x2 lo = ld8(p), hi = ld8(p + 16);
-      u32x4 az;
-      az.x = lo.x;
-      az.y = lo.y;
-      az.z = hi.x;
-      az.w = hi.y;
-      accd = mfma_bf16(az, fq[j], accd);
+      const u32x4 za = ld16(&Zr[l16 * LDT + 32 * j + 8 * g]);
+      d0 = mfma_bf16(za, f0[j], d0);
+      d1 = mfma_bf16(za, f1[j], d1);
     }
-    const float den = __shfl(accd[0] + accd[1], l16);
-    const float inv = 1.0f / den;
     // lane rows g and g ^ 1 swap halves of a column-tile pair (v_permlane16_swap) so that a lane
     // holds 8 consecutive columns of one query: one 16-byte store
-    const int64_t row = q0 + l16;
+    auto store_tile = [&](const f32x4 (&acco)[DC], f32x4 accd, int64_t row) {
+      const float inv = 1.0f / __shfl(accd[0] + accd[1], l16);
 #pragma unroll
-    for (int ct = 0; ct < DC; ct += 2) {
-      const uint32_t ax = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
-      const uint32_t ay = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
-      const uint32_t bx = pack_bf16(acco[ct + 1][0] * inv, acco[ct + 1][1] * inv);
-      const uint32_t by = pack_bf16(acco[ct + 1][2] * inv, acco[ct + 1][3] * inv);
-      const auto sx = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
-      const auto sy = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
-      u32x4 o;
-      o.x = sx[0];
-      o.y = sy[0];
-      o.z = sx[1];
-      o.w = sy[1];
-      if (row < a.n) st16(O + row * D + (ct + (g & 1)) * 16 + 8 * (g >> 1), o);
-    }
+      for (int ct = 0; ct < DC; ct += 2) {
+        const uint32_t ax = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
+        const uint32_t ay = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
+        const uint32_t bx = pack_bf16(acco[ct + 1][0] * inv, acco[ct + 1][1] * inv);
+        const uint32_t by = pack_bf16(acco[ct + 1][2] * inv, acco[ct + 1][3] * inv);
+        const auto sx = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
+        const auto sy = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
+        u32x4 o;
+        o.x = sx[0];
+        o.y = sy[0];
+        o.z = sx[1];
+        o.w = sy[1];
+        if (row < a.n) st16(O + row * D + (ct + (g & 1)) * 16 + 8 * (g >> 1), o);
+      }
+    };
+    store_tile(o0, d0, q0 + l16);
+    store_tile(o1, d1, q1 + l16);
   }
 }
 
@@ -564,10 +621,6 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 // share tile it = min(w, 7-w) and split the value columns); the same token tile and half of the
 // features for the next chunk's key projection; a block of the fp32 state accumulators (feature
 // tiles NAW (w % 4).., column tiles NCW (w / 4)..; waves 0..3 also keep z).
-__device__ __forceinline__ int favor_p_of_q(int q) {
-  return (q & ~31) + 16 * ((q >> 2) & 1) + 4 * ((q >> 3) & 3) + (q & 3);
-}
-
 template <int D, int M>
 __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   constexpr int C = kFavorChunk;
@@ -597,7 +650,6 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   __shared__ float wmax[8];
   __shared__ __attribute__((aligned(16))) float tm[2][C];   // per-token maxima of the two feature halves
   __shared__ __attribute__((aligned(16))) float mk[C];      // m_j of this chunk's keys
-  __shared__ float pm[C];                                    // P_i of this chunk's queries
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -748,18 +800,21 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       *reinterpret_cast<u32x2*>(&Kf[t * LDF + 32 * (f >> 1) + 8 * g + 4 * (f & 1)]) = w2;
     }
   };
-  // m_j of the chunk and P_i = max(c_state, m_0..m_i), by wave 0 (prefix maximum over lanes)
-  auto scan_maxima = [&](float c_state) {
-    if (wave == 0) {
-      float x = fmaxf(tm[0][lane], tm[1][lane]);
-      mk[lane] = x;
+  // m_j of the chunk's tokens (into mk, by waves 0..3, one per token tile) and P_i of this
+  // lane's query: max(c_state, the maxima of the earlier token tiles (per wave, from wmax:
+  // tile t belongs to waves t and 7 - t), the prefix maximum within its own tile)
+  auto chunk_maxima = [&](float c_state) {
+    const int t = it * 16 + l16;
+    float x = fmaxf(tm[0][t], tm[1][t]);
+    if (wave < 4 && g == 0) mk[t] = x;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x = fmaxf(x, y);
-      }
-      pm[lane] = fmaxf(x, c_state);
+    for (int off = 1; off < 16; off <<= 1) {
+      const float y = __shfl_up(x, off, 16);
+      if (l16 >= off) x = fmaxf(x, y);
     }
+    float base = c_state;
+    for (int tp = 0; tp < it; ++tp) base = fmaxf(base, fmaxf(wmax[tp], wmax[7 - tp]));
+    return fmaxf(base, x);
   };
 
   // ---- first chunk
@@ -777,7 +832,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
   float al = c_cur == kNegInf ? 0.f : fexp(c_cur - c_next);
   store_kf();
-  scan_maxima(c_cur);
+  float pq = chunk_maxima(c_cur);  // P_i of this lane's query in the coming chunk
   write_state();  // the initial state, on scale c_cur
   float c_prev = c_cur;  // scale of the state in St
   c_cur = c_next;        // scale of the state after this chunk
@@ -872,7 +927,6 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
         acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[l16 * LDF + 32 * j + 8 * g]), fq[j], accd);
     }
-    const float pq = pm[it * 16 + l16];  // P_i of this lane's query
     {
       const float sc = fexp(c_prev - pq);
 #pragma unroll
@@ -956,7 +1010,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
     al = fexp(c_cur - c_next);
     store_kf();
-    scan_maxima(c_cur);
+    pq = chunk_maxima(c_cur);
     write_state();  // the state after this chunk, on scale c_cur
     c_prev = c_cur;
     c_cur = c_next;
@@ -1001,7 +1055,7 @@ static hipError_t favor_dispatch(int d, int m, F&& f) {
 hipError_t launch_favor_kv_state(const FavorStateArgs& a, int d, int m, hipStream_t s) {
   return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
     hipLaunchKernelGGL((favor_kv_state<decltype(Dc)::value, decltype(Mc)::value>),
-                       dim3((unsigned)(a.groups * a.slices)), dim3(256), 0, s, a);
+                       dim3((unsigned)(a.groups * a.slices)), dim3(decltype(Mc)::value >= 128 ? 512 : 256), 0, s, a);
   });
 }
 

@@ -103,7 +103,7 @@ constexpr int64_t favor_rec(int d, int m) { return (int64_t)m * d + m + 4; }
 constexpr bool favor_supported(int64_t d, int64_t m) {
   return (d == 64 && (m == 64 || m == 128 || m == 256)) || (d == 128 && (m == 64 || m == 128));
 }
-constexpr int kFavorTile = 32;        // favor_kv_state: tokens per tile
+constexpr int kFavorTile = 64;        // favor_kv_state: tokens per tile
 constexpr int64_t kFavorQueries = 2048;  // favor_out: queries per workgroup
 
 struct FavorStateArgs {
