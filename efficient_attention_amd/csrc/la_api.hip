@@ -182,9 +182,9 @@ struct FavorCausalPlan {
   size_t ws = 0;
 };
 
-FavorCausalPlan plan_favor_causal(int64_t bh, int64_t n, int d, int m) {
+FavorCausalPlan plan_favor_causal(int64_t bh, int64_t n, int d, int m, int64_t chunk) {
   FavorCausalPlan p;
-  p.seg_len = causal_seg_len(bh, n, la::kFavorChunk);
+  p.seg_len = causal_seg_len(bh, n, chunk);
   p.segs = cdiv(n, p.seg_len);
   if (p.segs > 1) {
     p.st = plan_favor_state(bh * (p.segs - 1), p.seg_len, d, m);
@@ -706,8 +706,8 @@ size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t 
   int64_t bh = 0;
   size_t bytes = 0;
   if (check_favor(B, H, n, d, m, dtype, &bh, &bytes) != LA_OK || bh == 0 || n == 0) return 0;
-  if (chunk != la::kFavorChunk) return 0;
-  return plan_favor_causal(bh, n, (int)d, (int)m).ws;
+  if (!la::favor_chunk_ok(d, m, chunk)) return 0;
+  return plan_favor_causal(bh, n, (int)d, (int)m, chunk).ws;
 }
 
 int la_favor_forward_causal(const void* q, const void* k, const void* v, const void* w, void* out,
@@ -718,7 +718,7 @@ int la_favor_forward_causal(const void* q, const void* k, const void* v, const v
   size_t bytes = 0;
   int st = check_favor(B, H, n, d, m, dtype, &bh, &bytes);
   if (st != LA_OK) return st;
-  if (chunk != la::kFavorChunk) return LA_ERR_UNSUPPORTED;
+  if (!la::favor_chunk_ok(d, m, chunk)) return LA_ERR_UNSUPPORTED;
   if (!scale_ok(scale)) return LA_ERR_VALUE;
   const bool fin = Sn || zn || cn;
   if (fin && !(Sn && zn && cn)) return LA_ERR_NULL;
@@ -755,7 +755,7 @@ int la_favor_forward_causal(const void* q, const void* k, const void* v, const v
   if (!q || !k || !v || !w || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(out))
     return LA_ERR_ALIGN;
-  const FavorCausalPlan p = plan_favor_causal(bh, n, (int)d, (int)m);
+  const FavorCausalPlan p = plan_favor_causal(bh, n, (int)d, (int)m, chunk);
   if (p.ws > 0) {
     if (!workspace || workspace_bytes < p.ws) return LA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return LA_ERR_ALIGN;
@@ -795,7 +795,7 @@ int la_favor_forward_causal(const void* q, const void* k, const void* v, const v
     ca.seg_state = parts;
     ca.seg_parts = p.st.slices;
   }
-  if (la::launch_favor_causal(ca, (int)d, (int)m, s) != hipSuccess) return LA_ERR_HIP;
+  if (la::launch_favor_causal(ca, (int)d, (int)m, (int)chunk, s) != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
 }
 

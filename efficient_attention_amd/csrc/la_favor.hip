@@ -38,6 +38,10 @@ namespace la {
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// exp(a (u - m)) as one FMA and the base-2 exponential: al2 = a log2(e), ml2 = m a log2(e)
+__device__ __forceinline__ float fexp_shift(float u, float al2, float ml2) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(u, al2, -ml2));
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -297,8 +301,10 @@ __global__ __launch_bounds__(256) void favor_reduce(FavorReduceArgs a) {
 
 // ================================================================ non-causal output
 // One workgroup (8 waves) per kFavorQueries queries of a head; a wave takes 16-query tiles, the
-// query rows of its next tile in flight while it computes the current one.  LDS, features in
-// operand order (favor_p_of_q): the head's state transposed, St[c][q] = bf16(S[p(q)][c]); a
+// next tile's query rows in flight while it computes the current one.  LDS (72 KB or less, so
+// two workgroups share a compute unit), features in operand order (favor_p_of_q), every row's
+// 16-byte pieces XOR-permuted by the row index (swz) so that 16 rows read at one column are
+// conflict-free without padding: the head's state transposed, St[c][q] = bf16(S[p(q)][c]); a
 // normaliser tile Zr with rows bf16(z) and bf16(z - bf16(z)) (rows 2..15 zero); W [M][D].  Per
 // tile, outputs transposed:
 //   U^T = W Q^T (A = rows of W, B = the lane's own query row from global memory): lane holds
@@ -306,21 +312,25 @@ __global__ __launch_bounds__(256) void favor_reduce(FavorReduceArgs a) {
 //   f = exp(scale (U - max_f U)) packed to bf16 in the result layout: the B operand of the next
 //       product, k slot e of lane group g = stored feature 32 j + 8 g + e;
 //   out^T = St f (A = 16-byte rows of St), den = Zr f; out = out^T / den.
+template <int LEN>
+__device__ __forceinline__ int swz(int row, int col) {  // element (row, col) of a [.][LEN] tile
+  return row * LEN + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+}
+
 template <int D, int M>
-__global__ __launch_bounds__(512) void favor_out(FavorOutArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void favor_out(FavorOutArgs a) {
   constexpr int NT = 512;
   constexpr int QT = (int)kFavorQueries;
-  constexpr int LDT = M + 16;       // St / Zr row stride: 8 (mod 64) dwords
-  constexpr int LDW = D + 16;
   constexpr int KA = D / 32;
   constexpr int DC = D / 16;
   constexpr int MT = M / 16;        // feature tiles
   constexpr int MJ = M / 32;        // k-steps over features
   constexpr int64_t REC = favor_rec(D, M);
+  static_assert(D / 8 >= 8 && M / 8 >= 8, "the row permutation needs 8 pieces per row");
 
-  __shared__ __attribute__((aligned(16))) uint16_t St[D * LDT];
-  __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[M * LDW];
+  __shared__ __attribute__((aligned(16))) uint16_t St[D * M];
+  __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * M];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[M * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -342,14 +352,11 @@ __global__ __launch_bounds__(512) void favor_out(FavorOutArgs a) {
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
   const int64_t qbase = tile * QT;
 
-  // the first pass's query rows (tiles qt and qt + 8), before the set-up
-  u32x4 qb[KA], qb1[KA];
+  // the first tile's query rows, before the set-up
+  u32x4 qb[KA];
   int qt = wave;
 #pragma unroll
-  for (int ks = 0; ks < KA; ++ks) {
-    qb[ks] = ld16_clamp(Q, qbase + qt * 16 + l16, a.n, D, ks * 32 + g * 8);
-    qb1[ks] = ld16_clamp(Q, qbase + (qt + NT / 64) * 16 + l16, a.n, D, ks * 32 + g * 8);
-  }
+  for (int ks = 0; ks < KA; ++ks) qb[ks] = ld16_clamp(Q, qbase + qt * 16 + l16, a.n, D, ks * 32 + g * 8);
 
   // St[c][q], stored features in pairs (q even: p(q + 1) = p(q) + 1); Zr; W.  Every load of the
   // set-up is issued before the first store, so the L2 latency is paid once.
@@ -373,111 +380,84 @@ __global__ __launch_bounds__(512) void favor_out(FavorOutArgs a) {
 #pragma unroll
   for (int i = 0; i < SP; ++i) {
     const int e = tid + i * NT;
-    *reinterpret_cast<uint32_t*>(&St[(e % D) * LDT + 2 * (e / D)]) = pack_bf16(sv[i][0], sv[i][1]);
+    *reinterpret_cast<uint32_t*>(&St[swz<M>(e % D, 2 * (e / D))]) = pack_bf16(sv[i][0], sv[i][1]);
   }
-  for (int e = tid; e < 16 * M; e += NT) Zr[(e / M) * LDT + e % M] = 0;
+  for (int e = tid; e < 16 * M; e += NT) Zr[e] = 0;
 #pragma unroll
   for (int i = 0; i < WP; ++i) {
     const int e = tid + i * NT;
-    st16(&Ws[(e / (D / 8)) * LDW + (e % (D / 8)) * 8], wv[i]);
+    st16(&Ws[swz<D>(e / (D / 8), (e % (D / 8)) * 8)], wv[i]);
   }
   __syncthreads();  // Zr cleared before its first two rows are written
   if (tid < M) {
     const __bf16 hi = (__bf16)zq;
-    Zr[tid] = __builtin_bit_cast(uint16_t, hi);
-    Zr[LDT + tid] = __builtin_bit_cast(uint16_t, (__bf16)(zq - (float)hi));
+    Zr[swz<M>(0, tid)] = __builtin_bit_cast(uint16_t, hi);
+    Zr[swz<M>(1, tid)] = __builtin_bit_cast(uint16_t, (__bf16)(zq - (float)hi));
   }
   __syncthreads();
 
   const float s = a.scale;
-  // two 16-query tiles per pass (tiles qt and qt + 8 of the workgroup's 128), so that each
-  // 16-byte LDS read of W, St and Zr feeds two MFMAs
-  for (; qt < QT / 16; qt += 2 * (NT / 64)) {
+  const float sl2 = s * kLog2e;
+  for (; qt < QT / 16; qt += NT / 64) {
     const int64_t q0 = qbase + qt * 16;
     if (q0 >= a.n) break;
-    const int64_t q1 = q0 + (NT / 64) * 16;
-    f32x4 u0[MT], u1[MT];
-    float m0 = kNegInf, m1 = kNegInf;
+    u32x4 qn[KA];  // next tile's rows (clamped; unused past the end)
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) qn[ks] = ld16_clamp(Q, q0 + (NT / 64) * 16 + l16, a.n, D, ks * 32 + g * 8);
+    f32x4 u[MT];
+    float mq = kNegInf;
 #pragma unroll
     for (int ft = 0; ft < MT; ++ft) {
-      u0[ft] = zero4();
-      u1[ft] = zero4();
+      u[ft] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KA; ++ks) {
-        const u32x4 wa = ld16(&Ws[(ft * 16 + l16) * LDW + ks * 32 + g * 8]);
-        u0[ft] = mfma_bf16(wa, qb[ks], u0[ft]);
-        u1[ft] = mfma_bf16(wa, qb1[ks], u1[ft]);
-      }
+      for (int ks = 0; ks < KA; ++ks) u[ft] = mfma_bf16(ld16(&Ws[swz<D>(ft * 16 + l16, ks * 32 + g * 8)]), qb[ks], u[ft]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        m0 = fmaxf(m0, u0[ft][r]);
-        m1 = fmaxf(m1, u1[ft][r]);
-      }
+      for (int r = 0; r < 4; ++r) mq = fmaxf(mq, u[ft][r]);
     }
-    // the next pass's rows in flight during this one
-    const int64_t qn0 = q0 + 2 * (NT / 64) * 16;
-#pragma unroll
-    for (int ks = 0; ks < KA; ++ks) {
-      qb[ks] = ld16_clamp(Q, qn0 + l16, a.n, D, ks * 32 + g * 8);
-      qb1[ks] = ld16_clamp(Q, qn0 + (NT / 64) * 16 + l16, a.n, D, ks * 32 + g * 8);
-    }
-    m0 = fmaxf(m0, __shfl_xor(m0, 16));
-    m0 = fmaxf(m0, __shfl_xor(m0, 32));
-    m1 = fmaxf(m1, __shfl_xor(m1, 16));
-    m1 = fmaxf(m1, __shfl_xor(m1, 32));
-    u32x4 f0[MJ], f1[MJ];
+    mq = fmaxf(mq, __shfl_xor(mq, 16));
+    mq = fmaxf(mq, __shfl_xor(mq, 32));
+    const float mq_l2 = mq * sl2;
+    u32x4 fq[MJ];
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
-      f0[j].x = pack_bf16(fexp(s * (u0[2 * j][0] - m0)), fexp(s * (u0[2 * j][1] - m0)));
-      f0[j].y = pack_bf16(fexp(s * (u0[2 * j][2] - m0)), fexp(s * (u0[2 * j][3] - m0)));
-      f0[j].z = pack_bf16(fexp(s * (u0[2 * j + 1][0] - m0)), fexp(s * (u0[2 * j + 1][1] - m0)));
-      f0[j].w = pack_bf16(fexp(s * (u0[2 * j + 1][2] - m0)), fexp(s * (u0[2 * j + 1][3] - m0)));
-      f1[j].x = pack_bf16(fexp(s * (u1[2 * j][0] - m1)), fexp(s * (u1[2 * j][1] - m1)));
-      f1[j].y = pack_bf16(fexp(s * (u1[2 * j][2] - m1)), fexp(s * (u1[2 * j][3] - m1)));
-      f1[j].z = pack_bf16(fexp(s * (u1[2 * j + 1][0] - m1)), fexp(s * (u1[2 * j + 1][1] - m1)));
-      f1[j].w = pack_bf16(fexp(s * (u1[2 * j + 1][2] - m1)), fexp(s * (u1[2 * j + 1][3] - m1)));
+      fq[j].x = pack_bf16(fexp_shift(u[2 * j][0], sl2, mq_l2), fexp_shift(u[2 * j][1], sl2, mq_l2));
+      fq[j].y = pack_bf16(fexp_shift(u[2 * j][2], sl2, mq_l2), fexp_shift(u[2 * j][3], sl2, mq_l2));
+      fq[j].z = pack_bf16(fexp_shift(u[2 * j + 1][0], sl2, mq_l2), fexp_shift(u[2 * j + 1][1], sl2, mq_l2));
+      fq[j].w = pack_bf16(fexp_shift(u[2 * j + 1][2], sl2, mq_l2), fexp_shift(u[2 * j + 1][3], sl2, mq_l2));
     }
-    f32x4 o0[DC], o1[DC];
-    f32x4 d0 = zero4(), d1 = zero4();
+    f32x4 acco[DC];
+    f32x4 accd = zero4();
 #pragma unroll
-    for (int ct = 0; ct < DC; ++ct) {
-      o0[ct] = zero4();
-      o1[ct] = zero4();
-    }
+    for (int ct = 0; ct < DC; ++ct) acco[ct] = zero4();
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
 #pragma unroll
-      for (int ct = 0; ct < DC; ++ct) {
-        const u32x4 sa = ld16(&St[(ct * 16 + l16) * LDT + 32 * j + 8 * g]);
-        o0[ct] = mfma_bf16(sa, f0[j], o0[ct]);
-        o1[ct] = mfma_bf16(sa, f1[j], o1[ct]);
-      }
-      const u32x4 za = ld16(&Zr[l16 * LDT + 32 * j + 8 * g]);
-      d0 = mfma_bf16(za, f0[j], d0);
-      d1 = mfma_bf16(za, f1[j], d1);
+      for (int ct = 0; ct < DC; ++ct)
+        acco[ct] = mfma_bf16(ld16(&St[swz<M>(ct * 16 + l16, 32 * j + 8 * g)]), fq[j], acco[ct]);
+      accd = mfma_bf16(ld16(&Zr[swz<M>(l16, 32 * j + 8 * g)]), fq[j], accd);
     }
+    const float den = __shfl(accd[0] + accd[1], l16);
+    const float inv = 1.0f / den;
     // lane rows g and g ^ 1 swap halves of a column-tile pair (v_permlane16_swap) so that a lane
     // holds 8 consecutive columns of one query: one 16-byte store
-    auto store_tile = [&](const f32x4 (&acco)[DC], f32x4 accd, int64_t row) {
-      const float inv = 1.0f / __shfl(accd[0] + accd[1], l16);
+    const int64_t row = q0 + l16;
 #pragma unroll
-      for (int ct = 0; ct < DC; ct += 2) {
-        const uint32_t ax = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
-        const uint32_t ay = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
-        const uint32_t bx = pack_bf16(acco[ct + 1][0] * inv, acco[ct + 1][1] * inv);
-        const uint32_t by = pack_bf16(acco[ct + 1][2] * inv, acco[ct + 1][3] * inv);
-        const auto sx = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
-        const auto sy = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
-        u32x4 o;
-        o.x = sx[0];
-        o.y = sy[0];
-        o.z = sx[1];
-        o.w = sy[1];
-        if (row < a.n) st16(O + row * D + (ct + (g & 1)) * 16 + 8 * (g >> 1), o);
-      }
-    };
-    store_tile(o0, d0, q0 + l16);
-    store_tile(o1, d1, q1 + l16);
+    for (int ct = 0; ct < DC; ct += 2) {
+      const uint32_t ax = pack_bf16(acco[ct][0] * inv, acco[ct][1] * inv);
+      const uint32_t ay = pack_bf16(acco[ct][2] * inv, acco[ct][3] * inv);
+      const uint32_t bx = pack_bf16(acco[ct + 1][0] * inv, acco[ct + 1][1] * inv);
+      const uint32_t by = pack_bf16(acco[ct + 1][2] * inv, acco[ct + 1][3] * inv);
+      const auto sx = __builtin_amdgcn_permlane16_swap(ax, bx, false, false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(ay, by, false, false);
+      u32x4 o;
+      o.x = sx[0];
+      o.y = sy[0];
+      o.z = sx[1];
+      o.w = sy[1];
+      if (row < a.n) st16(O + row * D + (ct + (g & 1)) * 16 + 8 * (g >> 1), o);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) qb[ks] = qn[ks];
   }
 }
 
@@ -617,39 +597,43 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 //
 // LDS (bf16 unless noted): Kf[C][M+16] phi(K_c) token-major; Vs[2][C][D] V of this chunk and the
 // next; St[D][M+16] the state transposed, St[c][q] = S[q][c]; Zr[16][M+16] rows bf16(z) and
-// bf16(z - bf16(z)); Ws[M][D+16] the projection.  Work per wave: query tile it (waves w and 7-w
-// share tile it = min(w, 7-w) and split the value columns); the same token tile and half of the
-// features for the next chunk's key projection; a block of the fp32 state accumulators (feature
-// tiles NAW (w % 4).., column tiles NCW (w / 4)..; waves 0..3 also keep z).
-template <int D, int M>
+// bf16(z - bf16(z)); Ws[M][D+16] the projection.  Work per wave: one query tile, shared by
+// waves w and 7 - w when C = 64 (they split the value columns), or its own when C = 128 (tiles
+// w and 11 - w for the two waves of a SIMD, which balances the causal triangle); the same token
+// tile (and half the features when two waves share it) for the next chunk's key projection; a
+// block of the fp32 state accumulators (feature tiles NAW (w % 4).., column tiles NCW (w / 4)..;
+// waves 0..3 also keep z).  C = 64 double-buffers V (the next chunk's V is stored while this one
+// is read); C = 128 has LDS for one V tile only, stored with phi(K) between the barriers.
+template <int D, int M, int C>
 __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
-  constexpr int C = kFavorChunk;
   constexpr int NT = 512;
   constexpr int LDF = M + 16;      // 8 (mod 64) dwords
   constexpr int LDW = D + 16;
   constexpr int KA = D / 32;
   constexpr int MT = M / 16;       // feature tiles
   constexpr int MJ = M / 32;       // k-steps over features
-  constexpr int NI = C / 16;       // token tiles per chunk (4)
+  constexpr int NI = C / 16;       // token tiles per chunk
+  constexpr int NQW = 8 / NI;      // waves per query tile
+  constexpr int NVB = NQW;         // V buffers
   constexpr int NC = D / 16;       // value-column tiles
   constexpr int NAW = MT / 4;      // state feature tiles per wave
   constexpr int NCW = NC / 2;      // state column tiles per wave
-  constexpr int OCT = NC / 2;      // output column tiles per wave
-  constexpr int HF = MT / 2;       // key-projection feature tiles per wave
+  constexpr int OCT = NC / NQW;    // output column tiles per wave
+  constexpr int HF = MT / NQW;     // key-projection feature tiles per wave
   constexpr int KJ = C / 32;       // k-steps over the tokens of a chunk
   constexpr int PPR = D / 8;
   constexpr int RPV = C * PPR / NT;
   constexpr int64_t REC = favor_rec(D, M);
-  static_assert(NAW >= 1 && RPV >= 1 && OCT % 2 == 0 && NI == 4, "shape");
+  static_assert(NAW >= 1 && RPV >= 1 && OCT % 2 == 0 && (C == 64 || C == 128), "shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t Kf[C * LDF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NVB][C * D];
   __shared__ __attribute__((aligned(16))) uint16_t St[D * LDF];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDF];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[M * LDW];
   __shared__ float wmax[8];
-  __shared__ __attribute__((aligned(16))) float tm[2][C];   // per-token maxima of the two feature halves
-  __shared__ __attribute__((aligned(16))) float mk[C];      // m_j of this chunk's keys
+  __shared__ __attribute__((aligned(16))) float tm[NQW][C];  // per-token maxima (per feature part)
+  __shared__ __attribute__((aligned(16))) float mk[C];       // m_j of this chunk's keys
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -663,14 +647,19 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + bh * a.n * D;
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w);
 
-  const int it = wave < 4 ? wave : 7 - wave;  // query tile, and token tile of the key projection
-  const int oc0 = wave < 4 ? 0 : OCT;          // first output column tile
-  const int hf0 = wave < 4 ? 0 : HF;           // first key-projection feature tile
+  // query tile, and token tile of the key projection; tile t belongs to wave wave_of(t) (and to
+  // wave 7 - t as well when two waves share it)
+  const int it = wave < 4 ? wave : (NQW == 2 ? 7 - wave : 11 - wave);
+  auto wave_of = [](int t) { return t < 4 ? t : (NQW == 2 ? 7 - t : 11 - t); };
+  const int part = (NQW == 2 && wave >= 4) ? 1 : 0;  // which half of a shared tile's work
+  const int oc0 = part * OCT;                         // first output column tile
+  const int hf0 = part * HF;                          // first key-projection feature tile
   const int sa0 = NAW * (wave & 3), sc0 = NCW * (wave >> 2);
   const bool zown = wave < 4;
   const float s = a.scale;
   const float kconst = 0.5f * logf((float)M);
   const float hs2 = 0.5f * s * s;
+  const float sl2 = s * kLog2e;
 
   for (int e = tid; e < M * D / 8; e += NT) {
     const int f = e / (D / 8), c = (e % (D / 8)) * 8;
@@ -782,14 +771,15 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     // this half's maximum for token l16 (lanes l16, l16 + 16, ...), and the wave's maximum
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (g == 0) tm[wave < 4 ? 0 : 1][it * 16 + l16] = mx;
+    if (g == 0) tm[part][it * 16 + l16] = mx;
     return wave_max(mx);
   };
   // phi(K) of the projected rows on their token's scale, into Kf (operand order); a token past
   // the end (all exponents -inf) gets zero features
+  auto token_max = [&](int t) { return NQW == 2 ? fmaxf(tm[0][t], tm[NQW - 1][t]) : tm[0][t]; };
   auto store_kf = [&]() {
     const int t = it * 16 + l16;
-    const float mt = fmaxf(tm[0][t], tm[1][t]);
+    const float mt = token_max(t);
     const float sh = mt == kNegInf ? 0.f : mt;
 #pragma unroll
     for (int ft = 0; ft < HF; ++ft) {
@@ -800,20 +790,21 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       *reinterpret_cast<u32x2*>(&Kf[t * LDF + 32 * (f >> 1) + 8 * g + 4 * (f & 1)]) = w2;
     }
   };
-  // m_j of the chunk's tokens (into mk, by waves 0..3, one per token tile) and P_i of this
-  // lane's query: max(c_state, the maxima of the earlier token tiles (per wave, from wmax:
-  // tile t belongs to waves t and 7 - t), the prefix maximum within its own tile)
+  // m_j of the chunk's tokens (into mk, one wave per token tile) and P_i of this lane's query:
+  // max(c_state, the maxima of the earlier token tiles (from the waves' maxima in wmax), the
+  // prefix maximum within its own tile)
   auto chunk_maxima = [&](float c_state) {
     const int t = it * 16 + l16;
-    float x = fmaxf(tm[0][t], tm[1][t]);
-    if (wave < 4 && g == 0) mk[t] = x;
+    float x = token_max(t);
+    if (part == 0 && g == 0) mk[t] = x;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
       const float y = __shfl_up(x, off, 16);
       if (l16 >= off) x = fmaxf(x, y);
     }
     float base = c_state;
-    for (int tp = 0; tp < it; ++tp) base = fmaxf(base, fmaxf(wmax[tp], wmax[7 - tp]));
+    for (int tp = 0; tp < it; ++tp)
+      base = fmaxf(base, NQW == 2 ? fmaxf(wmax[tp], wmax[7 - tp]) : wmax[wave_of(tp)]);
     return fmaxf(base, x);
   };
 
@@ -838,7 +829,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   c_cur = c_next;        // scale of the state after this chunk
 
   int buf = 0;
-  for (int64_t c0 = t0; c0 < t1; c0 += C, buf ^= 1) {
+  for (int64_t c0 = t0; c0 < t1; c0 += C, buf ^= (NVB - 1)) {
     __syncthreads();  // Kf, Vs[buf], St, Zr of this chunk ready
     const uint16_t* Vc = Vs[buf];
     __builtin_amdgcn_sched_barrier(0);
@@ -861,12 +852,13 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       }
       mq = fmaxf(mq, __shfl_xor(mq, 16));
       mq = fmaxf(mq, __shfl_xor(mq, 32));
+      const float mq_l2 = mq * sl2;
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
-        fq[j].x = pack_bf16(fexp(s * (uq[2 * j][0] - mq)), fexp(s * (uq[2 * j][1] - mq)));
-        fq[j].y = pack_bf16(fexp(s * (uq[2 * j][2] - mq)), fexp(s * (uq[2 * j][3] - mq)));
-        fq[j].z = pack_bf16(fexp(s * (uq[2 * j + 1][0] - mq)), fexp(s * (uq[2 * j + 1][1] - mq)));
-        fq[j].w = pack_bf16(fexp(s * (uq[2 * j + 1][2] - mq)), fexp(s * (uq[2 * j + 1][3] - mq)));
+        fq[j].x = pack_bf16(fexp_shift(uq[2 * j][0], sl2, mq_l2), fexp_shift(uq[2 * j][1], sl2, mq_l2));
+        fq[j].y = pack_bf16(fexp_shift(uq[2 * j][2], sl2, mq_l2), fexp_shift(uq[2 * j][3], sl2, mq_l2));
+        fq[j].z = pack_bf16(fexp_shift(uq[2 * j + 1][0], sl2, mq_l2), fexp_shift(uq[2 * j + 1][1], sl2, mq_l2));
+        fq[j].w = pack_bf16(fexp_shift(uq[2 * j + 1][2], sl2, mq_l2), fexp_shift(uq[2 * j + 1][3], sl2, mq_l2));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -967,16 +959,20 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       accd = mfma_bf16(ones, af, accd);
     };
     {
+      // step m covers key tiles 2m and 2m + 1; the A products of step m + 1 are issued before
+      // the V products of step m so that the two overlap
+      const int mlast = it >> 1;
       f32x4 a0, a1;
       a_tiles(0, a0, a1);
-      if (it >= 2) {
-        const u32x4 af = pack_a(0, a0, a1);
-        a_tiles(1, a0, a1);
-        av_step(0, af);
-        av_step(1, pack_a(1, a0, a1));
-      } else {
-        av_step(0, pack_a(0, a0, a1));
+#pragma unroll
+      for (int m = 0; m < NI / 2 - 1; ++m) {
+        if (m < mlast) {
+          const u32x4 af = pack_a(m, a0, a1);
+          a_tiles(m + 1, a0, a1);
+          av_step(m, af);
+        }
       }
+      av_step(mlast, pack_a(mlast, a0, a1));
     }
 
     const float den = __shfl(accd[0] + accd[1], l16);
@@ -998,17 +994,18 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       if (row < t1) st16(O + row * D + (oc0 + ct + (g & 1)) * 16 + 8 * (g >> 1), o);
     }
 
-    // next chunk: key exponents and their maximum, V to the idle buffer
+    // next chunk: key exponents and their maximum, V to the idle buffer (if there is one)
     {
       const float mn = key_exponents(c0 + C);
       if (lane == 0) wmax[wave] = mn;
     }
-    store_v(Vs[buf ^ 1], c0 + C);
-    __syncthreads();  // every wave is done with Kf, St, Zr of this chunk; the maxima are in
+    if (NVB == 2) store_v(Vs[buf ^ 1], c0 + C);
+    __syncthreads();  // every wave is done with Kf, Vs, St, Zr of this chunk; the maxima are in
     c_next = c_cur;
 #pragma unroll
     for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
     al = fexp(c_cur - c_next);
+    if (NVB == 1) store_v(Vs[0], c0 + C);
     store_kf();
     pq = chunk_maxima(c_cur);
     write_state();  // the state after this chunk, on scale c_cur
@@ -1085,10 +1082,16 @@ hipError_t launch_favor_decode(const FavorDecodeArgs& a, int d, int m, hipStream
 
 namespace la {
 
-hipError_t launch_favor_causal(const FavorCausalArgs& a, int d, int m, hipStream_t s) {
+hipError_t launch_favor_causal(const FavorCausalArgs& a, int d, int m, int chunk, hipStream_t s) {
   return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
-    hipLaunchKernelGGL((favor_causal<decltype(Dc)::value, decltype(Mc)::value>),
-                       dim3((unsigned)(a.bh * a.segs)), dim3(512), 0, s, a);
+    constexpr int D = decltype(Dc)::value, M = decltype(Mc)::value;
+    if constexpr (favor_chunk_ok(D, M, 128)) {
+      if (chunk == 128) {
+        hipLaunchKernelGGL((favor_causal<D, M, 128>), dim3((unsigned)(a.bh * a.segs)), dim3(512), 0, s, a);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((favor_causal<D, M, 64>), dim3((unsigned)(a.bh * a.segs)), dim3(512), 0, s, a);
   });
 }
 

@@ -164,16 +164,19 @@ struct FavorCausalArgs {
   int64_t n;
   int64_t bh;
   int64_t segs;            // segments per head
-  int64_t seg_len;         // tokens per segment (multiple of kFavorChunk)
+  int64_t seg_len;         // tokens per segment (multiple of the chunk)
   float scale;
 };
-constexpr int kFavorChunk = 64;  // favor_causal: tokens per chunk
+// favor_causal chunks: 64 tokens, or 128 where phi(K_c), S^T, one V tile and W fit in LDS
+constexpr bool favor_chunk_ok(int64_t d, int64_t m, int64_t chunk) {
+  return favor_supported(d, m) && (chunk == 64 || (chunk == 128 && m <= 128));
+}
 
 hipError_t launch_favor_kv_state(const FavorStateArgs& a, int d, int m, hipStream_t s);
 hipError_t launch_favor_reduce(const FavorReduceArgs& a, int d, int m, hipStream_t s);
 hipError_t launch_favor_out(const FavorOutArgs& a, int d, int m, hipStream_t s);
 hipError_t launch_favor_decode(const FavorDecodeArgs& a, int d, int m, hipStream_t s);
-hipError_t launch_favor_causal(const FavorCausalArgs& a, int d, int m, hipStream_t s);
+hipError_t launch_favor_causal(const FavorCausalArgs& a, int d, int m, int chunk, hipStream_t s);
 // sn, zn, cn = the empty state (zeros, c = -inf) for every head
 hipError_t launch_favor_empty_state(const FavorCausalArgs& a, int d, int m, hipStream_t s);
 

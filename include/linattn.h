@@ -260,7 +260,8 @@ size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t 
  * Causal FAVOR+ attention (j <= i), chunked ("The recurrent view": the prefix sums S_i, z_i split
  * at each chunk start into the carried state and the masked pairwise part inside the chunk).
  *   q, k, v, out : [B][H][n][d] bf16; w : [m][d] bf16
- *   chunk        : 64 (the only chunk of this form; others LA_ERR_UNSUPPORTED)
+ *   chunk        : 64, or 128 when m <= 128 (others LA_ERR_UNSUPPORTED); the result does not
+ *                  depend on it beyond rounding
  *   Sn, zn, cn   : all NULL, or all given: receive the state after token n-1 as
  *                  exp(cn) * (Sn [B][H][m][d], zn [B][H][m]) fp32 (Sn 16-byte aligned, zn and cn
  *                  4-byte aligned), the input of la_favor_decode_step; for n = 0 the empty state

@@ -276,3 +276,38 @@ def test_favor_causal_last_row_equals_noncausal(ea):
     oc = from_dev(ea.la_favor_forward_causal(tq, tk, tv, tw, 0.35), "bf16")
     on = from_dev(ea.la_favor_forward_noncausal(tq, tk, tv, tw, 0.35), "bf16")
     assert normwise_err(oc[:, :, -1:], on[:, :, -1:]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("B,H,n,d,m", [(1, 2, 1000, 128, 128), (2, 3, 333, 64, 128), (1, 1, 129, 128, 64),
+                                       (2, 4, 4096, 128, 128), (3, 2, 77, 64, 64)])
+def test_favor_causal_chunk128_vs_oracle(ea, B, H, n, d, m):
+    q, k, v = _inputs(1000 + n + d + m, (B, H, n, d))
+    w = _proj(1001 + m + d, m, d, "orf")
+    scale = d ** -0.25
+    tq, tk, tv, tw = (to_dev(x, "bf16") for x in (q, k, v, w))
+    say("favor causal chunk 128", B, H, n, d, m)
+    out = from_dev(ea.la_favor_forward_causal(tq, tk, tv, tw, scale, chunk=128), "bf16")
+    ref = _causal_ref(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16"), scale)
+    err = normwise_err(out, ref)
+    say("  err", err)
+    assert err <= TOL_BF16
+    # chunk 64 and chunk 128 agree to rounding
+    o64 = from_dev(ea.la_favor_forward_causal(tq, tk, tv, tw, scale, chunk=64), "bf16")
+    assert normwise_err(out, o64) <= TOL_BF16
+
+
+def test_favor_causal_chunk128_final_state_and_large_exponents(ea):
+    torch = pytest.importorskip("torch")
+    B, H, n, d, m = 1, 2, 700, 128, 128
+    q, k, v = _inputs(1100, (B, H, n, d), 2.0)  # exponents -425..-104 (fp64 still holds the products)
+    w = _proj(1101, m, d, "iid")
+    say("favor causal chunk 128 large exponents + state")
+    out, S, z, c = ea.la_favor_forward_causal(*(to_dev(x, "bf16") for x in (q, k, v, w)), 1.0, chunk=128,
+                                              final_state=True)
+    Q, K, V, Wd = f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16")
+    ref = favor.quadratic(Q, K, V, Wd, 1.0, causal=True)
+    assert normwise_err(from_dev(out, "bf16"), ref) <= TOL_BF16
+    _, Sref, zref = favor.noncausal(Q, K, V, Wd, 1.0, return_state=True)
+    St, zt = _true_state(torch, S, z, c)
+    assert normwise_err(St, Sref) <= TOL_BF16
+    assert normwise_err(zt, zref, head_axes_last=1) <= TOL_BF16
