@@ -259,7 +259,8 @@ def _fca(lib, q=0x1000, k=0x2000, v=0x3000, w=0x5000, out=0x4000, Sn=0, zn=0, cn
 def test_validation_favor_causal():
     lib = _lib()
     S, Z, C = 0x200000, 0x300000, 0x380000
-    assert _fca(lib, chunk=128) == -4                          # chunk 64 only
+    assert _fca(lib, chunk=96) == -4
+    assert _fca(lib, chunk=128, m=256) == -4                   # chunk 128 needs m <= 128
     assert _fca(lib, dtype=0) == -4
     assert _fca(lib, d=128, m=256) == -4
     assert _fca(lib, scale=0.0) == -9
@@ -276,4 +277,5 @@ def test_validation_favor_causal():
     assert _fca(lib, n=4096, ws=0) == -6                       # one head: segments need sums
     assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 128, 64, 1) > 0
     assert ea.la_favor_causal_workspace_bytes(64, 8, 4096, 64, 128, 64, 1) == 0  # one segment per head
-    assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 128, 128, 1) == 0  # invalid chunk
+    assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 256, 128, 1) == 0  # invalid chunk
+    assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 128, 128, 1) > 0
