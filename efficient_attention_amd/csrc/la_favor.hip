@@ -43,9 +43,48 @@ __device__ __forceinline__ float fexp_shift(float u, float al2, float ml2) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(u, al2, -ml2));
 }
 
+// Cross-lane steps on the vector ALU (no LDS round trip; lane layouts checked on gfx950):
+// v_permlane16_swap of a value with itself returns the values of the even and of the odd 16-lane
+// row of the lane's row pair, v_permlane32_swap those of the lower and upper 32 lanes, and the
+// DPP row rotate / row shift move values within a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, 0xF, false));
+}
+// maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the same column of the four rows)
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+// sum over the same four lanes, in the same order on every lane: (r0 + r1) + (r2 + r3)
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(p[0]) + __int_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(q[0]) + __int_as_float(q[1]);
+}
+// the value of lane l % 16 (row 0) on every lane of its column
+__device__ __forceinline__ float from_row0(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  const auto q = __builtin_amdgcn_permlane32_swap(p[0], p[0], false, false);
+  return __int_as_float(q[0]);
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  x = fmaxf(x, dpp<0x128>(x, x));  // row_ror:8
+  x = fmaxf(x, dpp<0x124>(x, x));  // row_ror:4
+  x = fmaxf(x, dpp<0x122>(x, x));  // row_ror:2
+  x = fmaxf(x, dpp<0x121>(x, x));  // row_ror:1
+  return max_over_groups(x);
+}
+// inclusive prefix maximum over the lanes of a 16-lane row (row_shr:n; a lane with no source
+// keeps its own value)
+__device__ __forceinline__ float prefix_max16(float x) {
+  x = fmaxf(x, dpp<0x111>(x, x));
+  x = fmaxf(x, dpp<0x112>(x, x));
+  x = fmaxf(x, dpp<0x114>(x, x));
+  x = fmaxf(x, dpp<0x118>(x, x));
   return x;
 }
 
@@ -414,8 +453,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
       for (int r = 0; r < 4; ++r) mq = fmaxf(mq, u[ft][r]);
     }
-    mq = fmaxf(mq, __shfl_xor(mq, 16));
-    mq = fmaxf(mq, __shfl_xor(mq, 32));
+    mq = max_over_groups(mq);
     const float mq_l2 = mq * sl2;
     u32x4 fq[MJ];
 #pragma unroll
@@ -436,7 +474,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         acco[ct] = mfma_bf16(ld16(&St[swz<M>(ct * 16 + l16, 32 * j + 8 * g)]), fq[j], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[swz<M>(l16, 32 * j + 8 * g)]), fq[j], accd);
     }
-    const float den = __shfl(accd[0] + accd[1], l16);
+    const float den = from_row0(accd[0] + accd[1]);
     const float inv = 1.0f / den;
     // lane rows g and g ^ 1 swap halves of a column-tile pair (v_permlane16_swap) so that a lane
     // holds 8 consecutive columns of one query: one 16-byte store
@@ -751,8 +789,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KA; ++ks) ss += sumsq_bf16x8(kb[ks]);
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+    ss = sum_over_rows(ss);
     const bool ok = c0 + it * 16 + l16 < t1;
     const float off = ok ? hs2 * ss + kconst : __builtin_huge_valf();
     float mx = kNegInf;
@@ -769,8 +806,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       }
     }
     // this half's maximum for token l16 (lanes l16, l16 + 16, ...), and the wave's maximum
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_groups(mx);
     if (g == 0) tm[part][it * 16 + l16] = mx;
     return wave_max(mx);
   };
@@ -797,11 +833,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     const int t = it * 16 + l16;
     float x = token_max(t);
     if (part == 0 && g == 0) mk[t] = x;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const float y = __shfl_up(x, off, 16);
-      if (l16 >= off) x = fmaxf(x, y);
-    }
+    x = prefix_max16(x);
     float base = c_state;
     for (int tp = 0; tp < it; ++tp)
       base = fmaxf(base, NQW == 2 ? fmaxf(wmax[tp], wmax[7 - tp]) : wmax[wave_of(tp)]);
@@ -850,8 +882,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) mq = fmaxf(mq, uq[ft][r]);
       }
-      mq = fmaxf(mq, __shfl_xor(mq, 16));
-      mq = fmaxf(mq, __shfl_xor(mq, 32));
+      mq = max_over_groups(mq);
       const float mq_l2 = mq * sl2;
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
@@ -975,7 +1006,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       av_step(mlast, pack_a(mlast, a0, a1));
     }
 
-    const float den = __shfl(accd[0] + accd[1], l16);
+    const float den = from_row0(accd[0] + accd[1]);
     const float inv = 1.0f / den;
     const int64_t row = c0 + it * 16 + l16;
 #pragma unroll
