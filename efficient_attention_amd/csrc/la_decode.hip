@@ -6,9 +6,9 @@
 //     S <- S + phi(k) v^T,   z <- z + phi(k),   out = phi(q)^T S / phi(q)^T z.
 // The step is a pure read-modify-write stream over S (D*D fp32), so there is no MFMA: each of
 // the 256 threads owns 4 adjacent columns and D/RG rows, issues all its 16-byte state loads at
-// once, updates them with one FMA per element, writes them back and keeps a running column
-// sum of phi(q)_a * S'[a][c].  Partial column sums and the denominator are combined through
-// LDS in a fixed order, so the step is bitwise reproducible.
+// once, updates them with one FMA per element, writes them back (non-temporal stores) and keeps
+// a running column sum of phi(q)_a * S'[a][c].  Partial column sums and the denominator are
+// combined through LDS in a fixed order, so the step is bitwise reproducible.
 #include "la_common.h"
 #include "la_kernels.h"
 
@@ -74,7 +74,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     s[m].y += ka * v4.y;
     s[m].z += ka * v4.z;
     s[m].w += ka * v4.w;
-    *reinterpret_cast<f32x4*>(S + (int64_t)row * D + cg * 4) = s[m];
+    // non-temporal: the state is not read again before the next step, and by then the 256 MB
+    // memory-side cache has turned over (8192 heads are 541 MB); a normal store would leave up to
+    // 256 MB of dirty lines for the next kernel to write back
+    __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(S + (int64_t)row * D + cg * 4));
     num.x += qa * s[m].x;
     num.y += qa * s[m].y;
     num.z += qa * s[m].z;

@@ -597,7 +597,8 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
     const int row = rg + RG * r;
     const float ka = fk[row], qa = fq[row];
     sv[r] = sv[r] * al + ka * v4;
-    *reinterpret_cast<f32x4*>(S + (int64_t)row * D + cg * 4) = sv[r];
+    // non-temporal, as in decode_step_kernel: not read again before the next step
+    __builtin_nontemporal_store(sv[r], reinterpret_cast<f32x4*>(S + (int64_t)row * D + cg * 4));
     num += qa * sv[r];
   }
   *reinterpret_cast<f32x4*>(&red[rg][cg * 4]) = num;
