@@ -138,8 +138,8 @@ __global__ __launch_bounds__(256) void kv_state_bf16(KvStateArgs a, TB tb) {
   auto load = [&](int64_t t0, u32x4 (&k)[NP], u32x4 (&v)[NP]) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      k[p] = ld16_clamp(K, t0 + prow(p), gr.t1, D, pcol);
-      v[p] = ld16_clamp(V, t0 + prow(p), gr.t1, D, pcol);
+      k[p] = ld16_clamp_nt(K, t0 + prow(p), gr.t1, D, pcol);
+      v[p] = ld16_clamp_nt(V, t0 + prow(p), gr.t1, D, pcol);
     }
   };
   auto tile = [&](int64_t t0, u32x4 (&k)[NP], u32x4 (&v)[NP]) {
