@@ -205,6 +205,51 @@ def test_extreme_inputs(ea, form):
     assert normwise_err(g, ref) <= TOL_F32
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("form", ["noncausal", "causal"])
+def test_zero_denominator_rows(ea, form, dtype):
+    """The degenerate case of eq. Attention_i: a query whose features all underflow to 0 (every
+    entry -1e4, elu + 1 = exp(-1e4) = 0), or, causally, a query that sees only such keys, has
+    numerator and denominator 0; the result is the IEEE 0/0 (NaN), as the oracle's fp64
+    evaluation of the formula gives, and every other row is unaffected."""
+    d, n = 64, 300
+    q, k, v = random_inputs(13, (1, 2, n, d), dtype, 1.0 / np.sqrt(d))
+    q, k = f64(q, dtype).astype(np.float32), f64(k, dtype).astype(np.float32)
+    q[0, 0, [3, 17, 299]] = -1e4
+    q[0, 1, 150] = -1e4
+    k[0, 1, :5] = -1e4  # causal rows 0..4 of head 1 see only zero keys
+    q, k = encode(q, dtype), encode(k, dtype)
+    say("zero denominators", form, dtype)
+    g = run_forward(ea, form, q, k, v, dtype)
+    with np.errstate(invalid="ignore"):
+        ref = oracle_forward(form, q, k, v, dtype)
+    bad = np.isnan(ref).any(axis=-1)
+    assert bad[0, 0, [3, 17, 299]].all() and bad[0, 1, 150]
+    assert bad[0, 1, :5].all() == (form == "causal")
+    assert np.array_equal(np.isnan(g), np.isnan(ref))
+    assert np.isfinite(g[~bad]).all()
+    for h in range(2):
+        ok = ~bad[0, h]
+        assert normwise_err(g[0, h][ok][None], ref[0, h][ok][None]) <= TOL[dtype]
+
+
+def test_decode_zero_feature_key_leaves_state(ea):
+    """Decode with a key whose features are all 0 (entries -1e4): the state does not move, and
+    from the empty state the output is 0/0 (NaN); the next ordinary token then gives v."""
+    import torch
+    B, H, d = 2, 3, 128
+    q, k, v = random_inputs(14, (B, H, 2, d), "bf16", 1.0 / np.sqrt(d))
+    k0 = encode(np.full((B, H, d), -1e4, dtype=np.float32), "bf16")
+    S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+    z = torch.zeros((B, H, d), dtype=torch.float32, device="cuda")
+    say("decode zero-feature key")
+    o1 = from_dev(ea.la_decode_step(to_dev(q[:, :, 0], "bf16"), to_dev(k0, "bf16"), to_dev(v[:, :, 0], "bf16"), S, z), "bf16")
+    assert np.isnan(o1).all()
+    assert not bool(S.any()) and not bool(z.any())
+    o2 = from_dev(ea.la_decode_step(to_dev(q[:, :, 1], "bf16"), to_dev(k[:, :, 1], "bf16"), to_dev(v[:, :, 1], "bf16"), S, z), "bf16")
+    np.testing.assert_allclose(o2, f64(v[:, :, 1], "bf16"), rtol=2.0 ** -7, atol=0)  # v to a bf16 ulp
+
+
 @pytest.mark.parametrize("form", ["noncausal", "causal"])
 def test_deterministic(ea, form):
     d, n = 128, 1500
