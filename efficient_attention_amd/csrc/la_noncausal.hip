@@ -351,16 +351,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // fp32 stage 1: tile of 64 tokens kept in natural layout (the fp32 MFMA takes one k value
-// per lane, so no transpose is needed).
+// per lane, so no transpose is needed).  The next tile's rows are loaded into registers while
+// the current one is multiplied (unconditional loads, rows past the slice end clamped and then
+// zeroed), and the finished [KV | z] reuses the tile area, so that two workgroups fit on a CU
+// at D = 128 and four at D = 64.
 template <int D, class TB>
 __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a, TB tb) {
   constexpr int T = 64;
   constexpr int LD = D + 4;
   constexpr int NA = D / 64;
   constexpr int NC = D / 16;
-  __shared__ __attribute__((aligned(16))) float Kn[T * LD];
-  __shared__ __attribute__((aligned(16))) float Vn[T * LD];
-  __shared__ __attribute__((aligned(16))) float kv_lds[D * D + D];  // [KV | z]
+  constexpr int PPR = D / 4;            // 16-byte pieces per row
+  constexpr int NP = T * PPR / 256;     // pieces per thread and tensor
+  static_assert(D * D + D <= 2 * T * LD, "the state fits in the tile area");
+  __shared__ __attribute__((aligned(16))) float tiles[2 * T * LD];
+  float* Kn = tiles;
+  float* Vn = tiles + T * LD;
+  float* kv_lds = tiles;  // [KV | z], after the last tile
   float* z_lds = kv_lds + D * D;
 
   const GroupRange gr = group_range(a, tb);
@@ -378,23 +385,32 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a, TB tb) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[i][c] = zero4();
   }
+  auto prow = [&](int p) { return tid / PPR + p * (256 / PPR); };
+  const int pcol = (tid % PPR) * 4;
+  f32x4 kq[NP], vq[NP];
+  auto load = [&](int64_t t0) {  // row t1 - 1 stands in for rows past the end (a valid row)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int64_t r = t0 + prow(p) < gr.t1 ? t0 + prow(p) : gr.t1 - 1;
+      kq[p] = *reinterpret_cast<const f32x4*>(K + r * D + pcol);
+      vq[p] = *reinterpret_cast<const f32x4*>(V + r * D + pcol);
+    }
+  };
+  load(gr.t0);
   for (int64_t t0 = gr.t0; t0 < gr.t1; t0 += T) {
-    for (int idx = tid; idx < T * (D / 4); idx += 256) {
-      int row = idx / (D / 4), c4 = idx % (D / 4);
-      int64_t tok = t0 + row;
-      f32x4 kk = zero4(), vv = zero4();
-      if (tok < gr.t1) {
-        kk = *reinterpret_cast<const f32x4*>(K + tok * D + c4 * 4);
-        vv = *reinterpret_cast<const f32x4*>(V + tok * D + c4 * 4);
-        kk.x = phi(kk.x);
-        kk.y = phi(kk.y);
-        kk.z = phi(kk.z);
-        kk.w = phi(kk.w);
-      }
-      *reinterpret_cast<f32x4*>(&Kn[row * LD + c4 * 4]) = kk;
-      *reinterpret_cast<f32x4*>(&Vn[row * LD + c4 * 4]) = vv;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {  // phi on K; rows past the end are zero in both tiles
+      const bool ok = t0 + prow(p) < gr.t1;
+      f32x4 kk = kq[p];
+      kk.x = phi(kk.x);
+      kk.y = phi(kk.y);
+      kk.z = phi(kk.z);
+      kk.w = phi(kk.w);
+      *reinterpret_cast<u32x4*>(&Kn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, kk), ok);
+      *reinterpret_cast<u32x4*>(&Vn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, vq[p]), ok);
     }
     __syncthreads();
+    load(t0 + T);  // the next tile arrives while this one is multiplied
 #pragma unroll 4
     for (int s = 0; s < T / 4; ++s) {
 #pragma unroll
@@ -626,13 +642,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
 
 // fp32 output: same orientation with the fp32 MFMA (one k value per lane).  A lane loads 16
 // bytes of its query row, a[16m + 4g .. +3]; k-step 4m+e uses a = 16m + 4g + e on both
-// operands.  The normaliser phi(q).z is a plain fp32 dot product.
+// operands.  The normaliser phi(q).z is a plain fp32 dot product.  A wave takes its queries in
+// steps of BB 16-query blocks, which share every KV^T read from LDS, and loads the next step's
+// rows while it computes (unconditional loads; rows past the end read row n - 1 and are not
+// stored).  The KV^T reads are kept inside the loop (an empty asm statement hides that they
+// repeat): hoisted out of it, KV^T would occupy the register file and leave one wave per SIMD.
 template <int D, class TB>
 __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
   constexpr int LD = D + 4;
   constexpr int NC = D / 16;
+  constexpr int KM = D / 16;                 // 16-feature groups of the reduction
+  constexpr int BB = D == 64 ? 2 : 1;        // 16-query blocks per step
   constexpr int64_t QT = nc_queries(D, 0);  // queries per workgroup
   constexpr int QPW = (int)QT / 4;
+  constexpr int NB = QPW / (16 * BB);        // steps per wave
+  static_assert(NB % 2 == 0, "steps come in pairs");
   __shared__ __attribute__((aligned(16))) float KVt[D * LD];
   __shared__ float zs[D];
 
@@ -661,35 +685,71 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
 
   const float* Q = reinterpret_cast<const float*>(a.q) + sp.row0 * D;
   float* O = reinterpret_cast<float*>(a.out) + sp.row0 * D;
-  for (int blk = 0; blk < QPW / 16; ++blk) {
-    const int64_t row = q0 + blk * 16 + l16;
-    f32x4 acc[NC];
+  auto load = [&](int st, f32x4 (&q)[BB][KM]) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = zero4();
-    float dpart = 0.f;
+    for (int bb = 0; bb < BB; ++bb) {
+      const int64_t row = q0 + (int64_t)(BB * st + bb) * 16 + l16;
+      const int64_t r = row < n ? row : n - 1;
 #pragma unroll
-    for (int m = 0; m < D / 16; ++m) {
-      f32x4 qv = row < n ? *reinterpret_cast<const f32x4*>(Q + row * D + m * 16 + g * 4) : zero4();
-      float qf[4] = {phi(qv.x), phi(qv.y), phi(qv.z), phi(qv.w)};
+      for (int m = 0; m < KM; ++m) q[bb][m] = *reinterpret_cast<const f32x4*>(Q + r * D + m * 16 + g * 4);
+    }
+  };
+  auto compute = [&](int st, const f32x4 (&q)[BB][KM]) {
+    int kofs = l16 * LD;
+    asm volatile("" : "+v"(kofs));  // KV^T is re-read every step
+    const float* kvt = KVt + kofs;
+    f32x4 acc[BB][NC];
+    float dpart[BB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dpart += qf[e] * zs[m * 16 + g * 4 + e];
+    for (int bb = 0; bb < BB; ++bb) {
+      dpart[bb] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[bb][c] = zero4();
+    }
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      float qf[BB][4];
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb) {
+        qf[bb][0] = phi(q[bb][m].x);
+        qf[bb][1] = phi(q[bb][m].y);
+        qf[bb][2] = phi(q[bb][m].z);
+        qf[bb][3] = phi(q[bb][m].w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dpart[bb] += qf[bb][e] * zs[m * 16 + g * 4 + e];
+      }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        f32x4 kv = *reinterpret_cast<const f32x4*>(&KVt[(c * 16 + l16) * LD + m * 16 + g * 4]);
-        acc[c] = mfma_f32(kv.x, qf[0], acc[c]);
-        acc[c] = mfma_f32(kv.y, qf[1], acc[c]);
-        acc[c] = mfma_f32(kv.z, qf[2], acc[c]);
-        acc[c] = mfma_f32(kv.w, qf[3], acc[c]);
-      }
-    }
-    float den = sum_over_groups(dpart);
-    if (row < n) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(kvt + c * 16 * LD + m * 16 + g * 4);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        f32x4 o = {acc[c][0] / den, acc[c][1] / den, acc[c][2] / den, acc[c][3] / den};
-        *reinterpret_cast<f32x4*>(O + row * D + c * 16 + g * 4) = o;
+        for (int bb = 0; bb < BB; ++bb) {
+          acc[bb][c] = mfma_f32(kv.x, qf[bb][0], acc[bb][c]);
+          acc[bb][c] = mfma_f32(kv.y, qf[bb][1], acc[bb][c]);
+          acc[bb][c] = mfma_f32(kv.z, qf[bb][2], acc[bb][c]);
+          acc[bb][c] = mfma_f32(kv.w, qf[bb][3], acc[bb][c]);
+        }
       }
     }
+#pragma unroll
+    for (int bb = 0; bb < BB; ++bb) {
+      const float den = sum_over_groups(dpart[bb]);
+      const int64_t row = q0 + (int64_t)(BB * st + bb) * 16 + l16;
+      if (row < n) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          f32x4 o = {acc[bb][c][0] / den, acc[bb][c][1] / den, acc[bb][c][2] / den, acc[bb][c][3] / den};
+          *reinterpret_cast<f32x4*>(O + row * D + c * 16 + g * 4) = o;
+        }
+      }
+    }
+  };
+  f32x4 qa[BB][KM], qb[BB][KM];
+  load(0, qa);
+  for (int st = 0; st < NB; st += 2) {
+    load(st + 1, qb);
+    compute(st, qa);
+    load(st + 2, qa);  // past the wave's last step: clamped rows, never stored
+    compute(st + 1, qb);
   }
 }
 
