@@ -404,23 +404,34 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
   }
 }
 
-// fp32 kernel (no bf16 rounding anywhere).  The fp32 MFMA takes one k value per lane, so every
-// operand comes from natural token-major LDS rows.  Each wave owns state columns
-// {w, w+4, ...} in fp32 accumulators and produces the outputs of those columns for every
-// query of the chunk; the masked tile A^T is recomputed per wave (cheap at the sizes fp32 is
-// meant for) and, as in the bf16 kernel, fed back as an operand with permuted k.
+// fp32 kernel (no bf16 rounding anywhere).  The fp32 MFMA takes one k value per lane; a lane
+// holds 16-byte pieces of rows, features 16m + 4g .. 16m + 4g + 3, and k-step (m, e) pairs
+// feature 16m + 4g + e on both operands.  Each wave owns query tiles (tiles w and NI - 1 - w when
+// a chunk has 8, tile w when it has 4) and produces all output columns of them: the masked tile
+// A^T = phi(K) phi(Q)^T of each (key tile, query tile) pair is computed once, by its owner, and
+// fed back as an operand with permuted k, as in the bf16 kernel.  The inter-chunk product reads
+// S^T from LDS; the state accumulators are split by value columns (wave w owns column tiles
+// w, w + 4, ...) and written to S^T after each chunk's update.  The next chunk's K and V rows
+// are loaded into registers while the current chunk is computed.
 template <int D, int C, class TB>
 __global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
   constexpr int LD = D + 4;
-  constexpr int NI = C / 16;
-  constexpr int NCW = D / 64;
-  constexpr int NA = D / 16;
-  __shared__ __attribute__((aligned(16))) float Qn[C * LD];
+  constexpr int NI = C / 16;         // token tiles per chunk
+  constexpr int NCW = D / 64;        // state column tiles per wave
+  constexpr int NA = D / 16;         // feature tiles
+  constexpr int NC = D / 16;         // output column tiles
+  constexpr int KM = D / 16;         // 16-feature groups of a reduction over features
+  constexpr int TPW = NI / 4;        // query tiles per wave
+  constexpr int PPR = D / 4;         // 16-byte pieces per row
+  constexpr int NP = C * PPR / 256;  // K (and V) pieces per thread
+  static_assert(NI == 8 || NI == 4, "chunk");
   __shared__ __attribute__((aligned(16))) float Kn[C * LD];
   __shared__ __attribute__((aligned(16))) float Vn[C * LD];
+  __shared__ __attribute__((aligned(16))) float St[D * LD];  // S^T of the state before the chunk
   __shared__ float zf[D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
   const HeadSpan sp = head_span(tb, a.n, bh);
@@ -474,79 +485,120 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
   }
   if (tid < D) zf[tid] = zinit;
 
-  for (int64_t c0 = t0; c0 < t1; c0 += C) {
-    for (int idx = tid; idx < C * (D / 4); idx += 256) {
-      const int row = idx / (D / 4), c4 = idx % (D / 4);
-      const int64_t tok = c0 + row;
-      f32x4 qq = zero4(), kk = zero4(), vv = zero4();
-      if (tok < t1) {
-        qq = *reinterpret_cast<const f32x4*>(Q + tok * D + c4 * 4);
-        kk = *reinterpret_cast<const f32x4*>(K + tok * D + c4 * 4);
-        vv = *reinterpret_cast<const f32x4*>(V + tok * D + c4 * 4);
-        qq.x = phi(qq.x); qq.y = phi(qq.y); qq.z = phi(qq.z); qq.w = phi(qq.w);
-        kk.x = phi(kk.x); kk.y = phi(kk.y); kk.z = phi(kk.z); kk.w = phi(kk.w);
-      }
-      *reinterpret_cast<f32x4*>(&Qn[row * LD + c4 * 4]) = qq;
-      *reinterpret_cast<f32x4*>(&Kn[row * LD + c4 * 4]) = kk;
-      *reinterpret_cast<f32x4*>(&Vn[row * LD + c4 * 4]) = vv;
-    }
-    __syncthreads();
-
-    for (int it = 0; it < NI; ++it) {
-      f32x4 accA[NI];
+  // S^T of the initial state for the first chunk's inter-chunk product
+  auto write_st = [&]() {
 #pragma unroll
-      for (int jt = 0; jt < NI; ++jt) {
-        accA[jt] = zero4();
-        if (jt <= it) {
-          for (int ks = 0; ks < D / 4; ++ks)
-            accA[jt] = mfma_f32(Kn[(jt * 16 + l16) * LD + ks * 4 + g], Qn[(it * 16 + l16) * LD + ks * 4 + g], accA[jt]);
+    for (int at = 0; at < NA; ++at)
+#pragma unroll
+      for (int p = 0; p < NCW; ++p)
+        *reinterpret_cast<f32x4*>(&St[((wave + 4 * p) * 16 + l16) * LD + at * 16 + g * 4]) = accS[at][p];
+  };
+  write_st();
+
+  // K and V pieces: piece tid + 256 p of a chunk is row (tid / PPR) + (256 / PPR) p, columns
+  // 4 (tid % PPR) .. + 3.  Rows past the segment end read row t1 - 1 and are zeroed in LDS.
+  auto prow = [&](int p) { return tid / PPR + p * (256 / PPR); };
+  const int pcol = (tid % PPR) * 4;
+  f32x4 kq[NP], vq[NP];
+  auto load_kv = [&](int64_t c0) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int64_t r = c0 + prow(p) < t1 ? c0 + prow(p) : t1 - 1;
+      kq[p] = *reinterpret_cast<const f32x4*>(K + r * D + pcol);
+      vq[p] = *reinterpret_cast<const f32x4*>(V + r * D + pcol);
+    }
+  };
+  load_kv(t0);
+  for (int64_t c0 = t0; c0 < t1; c0 += C) {
+    // this wave's query rows (rows past the end read row t1 - 1; their outputs are not stored)
+    f32x4 qv[TPW][KM];
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp) {
+      const int it = tp == 0 ? wave : NI - 1 - wave;
+      const int64_t row = c0 + it * 16 + l16;
+      const int64_t r = row < t1 ? row : t1 - 1;
+#pragma unroll
+      for (int m = 0; m < KM; ++m) qv[tp][m] = *reinterpret_cast<const f32x4*>(Q + r * D + m * 16 + g * 4);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {  // phi on K; rows past the end are zero in both tiles
+      const bool ok = c0 + prow(p) < t1;
+      f32x4 kk = kq[p];
+      kk.x = phi(kk.x);
+      kk.y = phi(kk.y);
+      kk.z = phi(kk.z);
+      kk.w = phi(kk.w);
+      *reinterpret_cast<u32x4*>(&Kn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, kk), ok);
+      *reinterpret_cast<u32x4*>(&Vn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, vq[p]), ok);
+    }
+    __syncthreads();  // tiles, S^T and z of this chunk ready
+    load_kv(c0 + C);  // the next chunk's rows arrive while this one is computed
+
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp) {
+      const int it = tp == 0 ? wave : NI - 1 - wave;
+      f32x4 qf[KM];
+      float dpart = 0.f;  // phi(q) . z over this lane's features
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        qf[m].x = phi(qv[tp][m].x);
+        qf[m].y = phi(qv[tp][m].y);
+        qf[m].z = phi(qv[tp][m].z);
+        qf[m].w = phi(qv[tp][m].w);
+        dpart += qf[m].x * zf[m * 16 + g * 4] + qf[m].y * zf[m * 16 + g * 4 + 1] +
+                 qf[m].z * zf[m * 16 + g * 4 + 2] + qf[m].w * zf[m * 16 + g * 4 + 3];
+      }
+      f32x4 acco[NC];
+      f32x4 accd = zero4();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acco[c] = zero4();
+      // inter-chunk: S^T phi(Q)^T
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(&St[(c * 16 + l16) * LD + m * 16 + g * 4]);
+          acco[c] = mfma_f32(sv.x, qf[m].x, acco[c]);
+          acco[c] = mfma_f32(sv.y, qf[m].y, acco[c]);
+          acco[c] = mfma_f32(sv.z, qf[m].z, acco[c]);
+          acco[c] = mfma_f32(sv.w, qf[m].w, acco[c]);
+        }
+      // intra-chunk, one key tile at a time: A^T = phi(K_jt) phi(Q_it)^T (masked on the
+      // diagonal tile), then V^T A^T and the key sums 1^T A^T
+      for (int jt = 0; jt <= it; ++jt) {
+        f32x4 accA = zero4();
+#pragma unroll
+        for (int m = 0; m < KM; ++m) {
+          const f32x4 kf = *reinterpret_cast<const f32x4*>(&Kn[(jt * 16 + l16) * LD + m * 16 + g * 4]);
+          accA = mfma_f32(kf.x, qf[m].x, accA);
+          accA = mfma_f32(kf.y, qf[m].y, accA);
+          accA = mfma_f32(kf.z, qf[m].z, accA);
+          accA = mfma_f32(kf.w, qf[m].w, accA);
         }
         if (jt == it) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (g * 4 + r > l16) accA[jt][r] = 0.f;
+            if (g * 4 + r > l16) accA[r] = 0.f;
         }
-      }
-      f32x4 acco[NCW];
-      f32x4 accd = zero4();
-#pragma unroll
-      for (int p = 0; p < NCW; ++p) acco[p] = zero4();
-      // inter-chunk: k-slot g <-> feature 16*at + 4g + r; the state accumulator is the operand
-#pragma unroll
-      for (int at = 0; at < NA; ++at)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int fa = at * 16 + g * 4 + r;
-          const float qv = Qn[(it * 16 + l16) * LD + fa];
+          const int j = jt * 16 + g * 4 + r;
 #pragma unroll
-          for (int p = 0; p < NCW; ++p) acco[p] = mfma_f32(accS[at][p][r], qv, acco[p]);
-          accd = mfma_f32(l16 == 0 ? zf[fa] : 0.f, qv, accd);
-        }
-      // intra-chunk: k-slot g <-> key 16*jt + 4g + r; the A^T accumulator is the operand
-#pragma unroll
-      for (int jt = 0; jt < NI; ++jt) {
-        if (jt <= it) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = jt * 16 + g * 4 + r;
-#pragma unroll
-            for (int p = 0; p < NCW; ++p)
-              acco[p] = mfma_f32(Vn[j * LD + (wave + 4 * p) * 16 + l16], accA[jt][r], acco[p]);
-            accd = mfma_f32(l16 == 0 ? 1.f : 0.f, accA[jt][r], accd);
-          }
+          for (int c = 0; c < NC; ++c) acco[c] = mfma_f32(Vn[j * LD + c * 16 + l16], accA[r], acco[c]);
+          accd = mfma_f32(l16 == 0 ? 1.f : 0.f, accA[r], accd);
         }
       }
-      const float den = __shfl(accd[0], l16);
+      const float den = sum_over_groups(dpart) + __shfl(accd[0], l16);
       const int64_t row = c0 + it * 16 + l16;
       if (row < t1) {
 #pragma unroll
-        for (int p = 0; p < NCW; ++p) {
-          f32x4 o = {acco[p][0] / den, acco[p][1] / den, acco[p][2] / den, acco[p][3] / den};
-          *reinterpret_cast<f32x4*>(O + row * D + (wave + 4 * p) * 16 + g * 4) = o;
+        for (int c = 0; c < NC; ++c) {
+          f32x4 o = {acco[c][0] / den, acco[c][1] / den, acco[c][2] / den, acco[c][3] / den};
+          *reinterpret_cast<f32x4*>(O + row * D + c * 16 + g * 4) = o;
         }
       }
     }
-    __syncthreads();  // zf and the tiles are no longer read for outputs
+    __syncthreads();  // S^T, z and the tiles are no longer read for outputs
 
     // state update: S[:, own cols] += phi(K)^T V, z += column sums of phi(K)
     for (int ks = 0; ks < C / 4; ++ks) {
@@ -563,6 +615,7 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
       for (int j = 0; j < C; ++j) zs += Kn[j * LD + tid];
       zf[tid] += zs;
     }
+    write_st();
     __syncthreads();  // before the next chunk overwrites the tiles
   }
 
