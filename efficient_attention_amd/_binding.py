@@ -7,6 +7,7 @@ this module raises instead of falling back to anything else.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 
@@ -145,6 +146,20 @@ def workspace(nbytes: int, device: torch.device, stream_handle: int) -> torch.Te
     return buf
 
 
+def _on_stream(fn):
+    """Run an entry point with `stream` (a torch stream or a raw hipStream_t handle) as the
+    current stream, so that the tensors it allocates (out, workspace, states) come from that
+    stream's pool and are not handed to other work while its kernels still use them."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(s):
+            return fn(*args, stream=s, **kwargs)
+    return wrapper
+
+
 def _stream_handle(device: torch.device, stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -177,6 +192,7 @@ def _out_like(q, out):
     return out
 
 
+@_on_stream
 def la_forward_noncausal(q, k, v, out=None, ws=None, stream=None):
     """Non-causal forward over [B, H, n, d] tensors; returns out."""
     _check_qkv(q, k, v, 4)
@@ -195,6 +211,7 @@ def la_forward_noncausal(q, k, v, out=None, ws=None, stream=None):
     return out
 
 
+@_on_stream
 def la_forward_causal(q, k, v, chunk: int = 128, out=None, ws=None, stream=None):
     """Causal (j <= i) forward over [B, H, n, d] tensors; returns out."""
     _check_qkv(q, k, v, 4)
@@ -214,6 +231,7 @@ def la_forward_causal(q, k, v, chunk: int = 128, out=None, ws=None, stream=None)
     return out
 
 
+@_on_stream
 def la_forward_causal_state(q, k, v, chunk: int = 128, S0=None, z0=None, out=None, Sn=None, zn=None,
                             final_state: bool = True, ws=None, stream=None):
     """Causal forward continuing from the state (S0 [B, H, d, d], z0 [B, H, d], fp32; None for
@@ -250,6 +268,7 @@ def la_forward_causal_state(q, k, v, chunk: int = 128, S0=None, z0=None, out=Non
     return out, Sn, zn
 
 
+@_on_stream
 def la_decode_step(q, k, v, S, z, out=None, stream=None):
     """One decode step over [B, H, d] tensors; S [B, H, d, d] and z [B, H, d] (fp32) are
     updated in place; returns out."""
@@ -283,6 +302,7 @@ def la_state_sums_workspace_bytes(B: int, H: int, n: int, d: int, dtype, seg_len
     return int(load().la_state_sums_workspace_bytes(B, H, n, d, code, seg_len, nseg))
 
 
+@_on_stream
 def la_state_sums(k, v, seg_len: int, nseg: int, sums=None, ws=None, stream=None):
     """Per-segment [S | z] sums of [B, H, n, d] keys/values: returns fp32 [B, H, nseg, d*d + d]."""
     _check_qkv(k, k, v, 4)
@@ -304,6 +324,7 @@ def la_state_sums(k, v, seg_len: int, nseg: int, sums=None, ws=None, stream=None
     return sums
 
 
+@_on_stream
 def la_causal_segments(q, k, v, sums, seg_len: int, chunk: int = 128, out=None, stream=None):
     """Chunked causal pass where segment s starts from the sum of sums[:, :, :s]."""
     _check_qkv(q, k, v, 4)
@@ -356,6 +377,7 @@ def la_causal_varlen_workspace_bytes(cu_seqlens, heads: int, d: int, chunk: int,
     return int(load().la_causal_varlen_workspace_bytes(cu.ctypes.data, cu.size - 1, heads, d, chunk, code))
 
 
+@_on_stream
 def la_forward_noncausal_varlen(q, k, v, cu_seqlens, heads: int, out=None, ws=None, stream=None):
     """Non-causal forward over a variable-length batch: sequence s is the [heads, n_s, d] block
     at token offset cu_seqlens[s] (q, k, v hold heads * cu_seqlens[-1] rows of d); returns out."""
@@ -376,6 +398,7 @@ def la_forward_noncausal_varlen(q, k, v, cu_seqlens, heads: int, out=None, ws=No
     return out
 
 
+@_on_stream
 def la_forward_causal_varlen(q, k, v, cu_seqlens, heads: int, chunk: int = 128, out=None, ws=None, stream=None):
     """Causal forward over a variable-length batch (layout as la_forward_noncausal_varlen)."""
     cu = _offsets(cu_seqlens)
@@ -395,6 +418,7 @@ def la_forward_causal_varlen(q, k, v, cu_seqlens, heads: int, chunk: int = 128, 
     return out
 
 
+@_on_stream
 def la_decode_step_masked(q, k, v, S, z, active, out=None, stream=None):
     """la_decode_step for the sequences whose flag in `active` (uint8/bool GPU tensor [B]) is set;
     the others keep their state and out."""
@@ -430,6 +454,7 @@ def la_favor_noncausal_workspace_bytes(B: int, H: int, n: int, d: int, m: int, d
     return int(load().la_favor_noncausal_workspace_bytes(B, H, n, d, m, code))
 
 
+@_on_stream
 def la_favor_forward_noncausal(q, k, v, w, scale: float, out=None, ws=None, stream=None):
     """Non-causal attention with FAVOR+ features phi(x) = exp(W x' - |x'|^2/2)/sqrt(m), x' =
     scale x, over [B, H, n, d] tensors and the projection w [m, d]; returns out."""
@@ -451,6 +476,7 @@ def la_favor_forward_noncausal(q, k, v, w, scale: float, out=None, ws=None, stre
     return out
 
 
+@_on_stream
 def la_favor_decode_step(q, k, v, w, S, z, c, scale: float, out=None, stream=None):
     """One FAVOR+ decode step over [B, H, d] tensors; the state (S [B, H, m, d], z [B, H, m],
     c [B, H], fp32; true state exp(c) (S, z)) is updated in place; returns out."""
@@ -476,6 +502,7 @@ def la_favor_causal_workspace_bytes(B: int, H: int, n: int, d: int, m: int, chun
     return int(load().la_favor_causal_workspace_bytes(B, H, n, d, m, chunk, code))
 
 
+@_on_stream
 def la_favor_forward_causal(q, k, v, w, scale: float, chunk: int = 64, out=None, final_state: bool = False,
                             Sn=None, zn=None, cn=None, ws=None, stream=None):
     """Causal attention with FAVOR+ features over [B, H, n, d] tensors.  Returns out, or with

@@ -250,6 +250,31 @@ def test_decode_zero_feature_key_leaves_state(ea):
     np.testing.assert_allclose(o2, f64(v[:, :, 1], "bf16"), rtol=2.0 ** -7, atol=0)  # v to a bf16 ulp
 
 
+def test_calls_on_a_side_stream(ea):
+    """Entry points given another stream (a torch stream or its raw handle) run there, with
+    their outputs and workspaces allocated on it, while the default stream is busy; results
+    equal the default-stream calls bitwise."""
+    import torch
+    d = 128
+    q, k, v = random_inputs(15, (2, 4, 3000, d), "bf16", 1.0 / np.sqrt(d))
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    say("side stream")
+    ref = [ea.la_forward_noncausal(tq, tk, tv), ea.la_forward_causal(tq, tk, tv, chunk=128),
+           ea.la_forward_causal(tq, tk, tv, chunk=64)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    busy = torch.randn(4096, 4096, device="cuda")
+    for _ in range(4):
+        busy = busy @ busy.T * 1e-3  # default-stream work running meanwhile
+    got = [ea.la_forward_noncausal(tq, tk, tv, stream=side),
+           ea.la_forward_causal(tq, tk, tv, chunk=128, stream=side),
+           ea.la_forward_causal(tq, tk, tv, chunk=64, stream=side.cuda_stream)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("form", ["noncausal", "causal"])
 def test_deterministic(ea, form):
     d, n = 128, 1500
