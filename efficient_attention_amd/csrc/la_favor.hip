@@ -36,6 +36,7 @@
 namespace la {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 // exp(a (u - m)) as one FMA and the base-2 exponential: al2 = a log2(e), ml2 = m a log2(e)
@@ -129,23 +130,28 @@ __device__ __forceinline__ int favor_p_of_q(int q) {
 }
 
 // ================================================================ stage 1: state sums
-// One workgroup (NW = 8 waves, or 4 when M = 64) sums the features of one token slice:
+// Waves per workgroup of the state sums: 16 (one feature tile each) for M = 256 at D = 64, so
+// that four waves share a SIMD; 8 for M = 128 or 256 at D = 128; 4 for M = 64.
+#define FAVOR_NW(D, M) ((M) >= 256 && (D) == 64 ? 16 : (M) >= 128 ? 8 : 4)
+// One workgroup (NW waves) sums the features of one token slice:
 // S_p = sum_j phi(k_j) v_j^T, z_p = sum_j phi(k_j), with log-scale c_p.  The slice streams
-// through LDS in tiles of 64 tokens (double-buffered, one barrier per tile); wave w owns the
-// 16 FT features from w M / NW:
+// through LDS in tiles of 64 tokens (128 with 16 waves; double-buffered, one barrier per tile);
+// wave w owns the 16 FT features from w M / NW:
 //   U = K_tile W_w^T on MFMA (A = token rows of K from LDS, B = this wave's rows of W, held in
 //       registers for the whole slice) -> lane holds u for feature l16 of each of its feature
 //       tiles and tokens 16 tt + 4 g + r of the four token tiles tt;
-//   u = scale U - (scale^2 |k|^2 / 2 + ln(M) / 2) per token; the wave's running maximum c_w;
-//   S_w += exp(u - c_w)^T V_tile and z_w += exp(u - c_w)^T 1 on MFMA, the exp values packed to
+//   u = (scale U - (scale^2 |k|^2 / 2 + ln(M) / 2)) log2(e) per token, i.e. the exponent in
+//       base-2 units (one FMA per element); the wave's running maximum c_w;
+//   S_w += 2^(u - c_w)^T V_tile and z_w += 2^(u - c_w)^T 1 on MFMA, the exp values packed to
 //       bf16 as the A operand in the result's own layout (token tiles 2s, 2s + 1 form k-step s),
 //       V read transposed from LDS in the same token order.
-// At the end the waves' blocks are brought to the workgroup maximum and written.
+// At the end the waves' blocks are brought to the workgroup maximum and written, the log-scale
+// converted back to natural-log units.
 template <int D, int M>
-__global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStateArgs a) {
-  constexpr int NW = M >= 128 ? 8 : 4;
+__global__ __launch_bounds__(FAVOR_NW(D, M) * 64) void favor_kv_state(FavorStateArgs a) {
+  constexpr int NW = FAVOR_NW(D, M);
   constexpr int NT = 64 * NW;
-  constexpr int T = kFavorTile;
+  constexpr int T = NW == 16 ? 2 * kFavorTile : kFavorTile;
   constexpr int TT = T / 16;        // token tiles per tile
   constexpr int LDK = D + 16;
   constexpr int KA = D / 32;        // k-steps of the projection
@@ -184,6 +190,7 @@ __global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStat
   const float s = a.scale;
   const float kconst = 0.5f * logf((float)M);  // ln(sqrt(M))
   const float hs2 = 0.5f * s * s;
+  const float sl2 = s * kLog2e;  // exponents are carried in base-2 units inside this kernel
 
   // this wave's rows of W as B operands: column = feature, k = d
   u32x4 wr[FT][KA];
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStat
       float ss = sumsq_bf16x8(kr[p]);
 #pragma unroll
       for (int off = 1; off < PPR; off <<= 1) ss += __shfl_xor(ss, off);
-      if (tid % PPR == 0) kt[b][row] = ok ? hs2 * ss + kconst : __builtin_huge_valf();
+      if (tid % PPR == 0) kt[b][row] = ok ? (hs2 * ss + kconst) * kLog2e : __builtin_huge_valf();
     }
   };
 
@@ -251,14 +258,14 @@ __global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStat
         for (int ks = 0; ks < KA; ++ks) u[ft][ti] = mfma_bf16(ka[ks], wr[ft][ks], u[ft][ti]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          u[ft][ti][r] = s * u[ft][ti][r] - ktv[r];
+          u[ft][ti][r] = __builtin_fmaf(sl2, u[ft][ti][r], -ktv[r]);
           tmax = fmaxf(tmax, u[ft][ti][r]);
         }
       }
     }
     tmax = wave_max(tmax);
     if (tmax > cw) {  // wave-uniform: rescale what this wave has summed to the new maximum
-      const float al = fexp(cw - tmax);
+      const float al = __builtin_amdgcn_exp2f(cw - tmax);
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
         accz[ft] *= al;
@@ -276,10 +283,10 @@ __global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStat
       for (int ft = 0; ft < FT; ++ft) {
         const f32x4 u0 = u[ft][2 * st], u1 = u[ft][2 * st + 1];
         u32x4 af;
-        af.x = pack_bf16(fexp(u0[0] - cw), fexp(u0[1] - cw));
-        af.y = pack_bf16(fexp(u0[2] - cw), fexp(u0[3] - cw));
-        af.z = pack_bf16(fexp(u1[0] - cw), fexp(u1[1] - cw));
-        af.w = pack_bf16(fexp(u1[2] - cw), fexp(u1[3] - cw));
+        af.x = pack_bf16(__builtin_amdgcn_exp2f(u0[0] - cw), __builtin_amdgcn_exp2f(u0[1] - cw));
+        af.y = pack_bf16(__builtin_amdgcn_exp2f(u0[2] - cw), __builtin_amdgcn_exp2f(u0[3] - cw));
+        af.z = pack_bf16(__builtin_amdgcn_exp2f(u1[0] - cw), __builtin_amdgcn_exp2f(u1[1] - cw));
+        af.w = pack_bf16(__builtin_amdgcn_exp2f(u1[2] - cw), __builtin_amdgcn_exp2f(u1[3] - cw));
         accz[ft] = mfma_bf16(af, ones, accz[ft]);
 #pragma unroll
         for (int ct = 0; ct < DC; ++ct) acc[ft][ct] = mfma_bf16(af, bv[ct], acc[ft][ct]);
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStat
   float cmax = kNegInf;
 #pragma unroll
   for (int w = 0; w < NW; ++w) cmax = fmaxf(cmax, cw_sh[w]);
-  const float be = cw == kNegInf ? 0.f : fexp(cw - cmax);
+  const float be = cw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(cw - cmax);
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
     const int f0 = wave * FW + ft * 16 + 4 * g;
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(M >= 128 ? 512 : 256) void favor_kv_state(FavorStat
 #pragma unroll
       for (int r = 0; r < 4; ++r) rec[(int64_t)M * D + f0 + r] = accz[ft][r] * be;
   }
-  if (tid == 0) rec[(int64_t)M * D + M] = cmax;
+  if (tid == 0) rec[(int64_t)M * D + M] = cmax * kLn2;  // the record's scale is in natural-log units
 }
 
 // ================================================================ stage 2: one state per group
@@ -1084,7 +1091,7 @@ static hipError_t favor_dispatch(int d, int m, F&& f) {
 hipError_t launch_favor_kv_state(const FavorStateArgs& a, int d, int m, hipStream_t s) {
   return favor_dispatch(d, m, [&](auto Dc, auto Mc) {
     hipLaunchKernelGGL((favor_kv_state<decltype(Dc)::value, decltype(Mc)::value>),
-                       dim3((unsigned)(a.groups * a.slices)), dim3(decltype(Mc)::value >= 128 ? 512 : 256), 0, s, a);
+                       dim3((unsigned)(a.groups * a.slices)), dim3(FAVOR_NW(decltype(Dc)::value, decltype(Mc)::value) * 64), 0, s, a);
   });
 }
 
