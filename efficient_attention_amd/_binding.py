@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import functools
+import inspect
 import os
 import threading
 
@@ -150,8 +151,16 @@ def _on_stream(fn):
     """Run an entry point with `stream` (a torch stream or a raw hipStream_t handle) as the
     current stream, so that the tensors it allocates (out, workspace, states) come from that
     stream's pool and are not handed to other work while its kernels still use them."""
+    names = list(inspect.signature(fn).parameters)
+    pos = names.index("stream")
+    assert pos == len(names) - 1, "stream must be the last parameter"
+
     @functools.wraps(fn)
-    def wrapper(*args, stream=None, **kwargs):
+    def wrapper(*args, **kwargs):
+        if len(args) > pos:  # given positionally
+            kwargs["stream"] = args[pos]
+            args = args[:pos]
+        stream = kwargs.pop("stream", None)
         if stream is None:
             return fn(*args, **kwargs)
         s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
