@@ -209,6 +209,19 @@ def favor_flops(form, n_tokens, d, m, chunk=64):
     return n_tokens * 8 * m * d
 
 
+# Vector ALU issue of the chip: 256 CUs x 4 SIMDs x 16 lanes per cycle at 2.4 GHz (fp32 ops
+# without packed math).  A FAVOR+ feature value needs at least its exponent's affine shift and a
+# running maximum (2 ops) and one exponential, a quarter-rate transcendental (4 issue slots):
+# 6 lane-slots per feature value, 2 m feature values per query-key token pair and m per decode
+# head-step (the query's and the key's features).
+VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+FAVOR_SLOTS_PER_FEATURE = 6
+
+
+def favor_alu_floor_s(n_feature_values):
+    return n_feature_values * FAVOR_SLOTS_PER_FEATURE / VALU_LANE_OPS_PER_S
+
+
 def run_favor():
     """The FAVOR+ feature map on the same shapes as the elu + 1 workloads (seeded_inputs F3, F4,
     F5): non-causal B=8 H=16 n=16384 d=64 m=256, causal B=4 H=32 n=65536 d=128 m=128 chunk 64,
@@ -248,14 +261,18 @@ def run_favor():
 
     res = []
 
-    def report(name, w, ms, nbytes, flops, extra=None):
+    def report(name, w, ms, nbytes, flops, features, extra=None):
+        floors = {"hbm": nbytes / (HBM_PEAK_GBS * 1e9), "mfma": flops / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+                  "alu": favor_alu_floor_s(features)}
+        bound = max(floors, key=floors.get)
         r = {"workload": name, "form": w.form, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "m": w.m,
              "isolated_ms": ms, "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
              "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
              "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12,
              "pct_bf16_mfma_peak": 100 * flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-             "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-             "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) else "mfma"}
+             "algorithmic_bytes": nbytes, "algorithmic_flops": flops, "feature_values": features,
+             "floor_ms": {k: v * 1e3 for k, v in floors.items()}, "bound": bound,
+             "pct_of_roofline": 100 * floors[bound] / (ms * 1e-3)}
         if extra:
             r.update(extra)
         res.append(r)
@@ -272,7 +289,7 @@ def run_favor():
         else:
             ms = timed(lambda: ea.la_favor_forward_causal(q, k, v, W, scale, chunk=w.chunk, out=out))
         report(w.name, w, ms, algorithmic_bytes(w.B, w.H, w.n, w.d, 2),
-               favor_flops(w.form, w.B * w.H * w.n, w.d, w.m, w.chunk))
+               favor_flops(w.form, w.B * w.H * w.n, w.d, w.m, w.chunk), 2 * w.m * w.B * w.H * w.n)
         del q, k, v, out
     # decode: state of 1024 prior tokens from the causal forward, then one step
     w = F5
@@ -287,7 +304,7 @@ def run_favor():
     ms = timed(lambda: ea.la_favor_decode_step(q, k, v, W, S, z, c, scale, out=out))
     BH = w.B * w.H
     report(w.name, w, ms, BH * (2 * (w.m * w.d + w.m + 1) * 4 + 4 * w.d * 2), favor_flops("decode", BH, w.d, w.m),
-           {"note": "state [m][d] + z [m] + c fp32 read and written per head, q k v out bf16"})
+           2 * w.m * BH, {"note": "state [m][d] + z [m] + c fp32 read and written per head, q k v out bf16"})
     print(json.dumps({"metric": METRIC, "mode": "favor", "n_gpus": 1,
                       "data": "synthetic (seeded N(0,1) bf16 q/k/v on device, i.i.d. N(0,1) projection)",
                       "favor": res}), flush=True)
