@@ -392,8 +392,8 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a, TB tb) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int64_t r = t0 + prow(p) < gr.t1 ? t0 + prow(p) : gr.t1 - 1;
-      kq[p] = *reinterpret_cast<const f32x4*>(K + r * D + pcol);
-      vq[p] = *reinterpret_cast<const f32x4*>(V + r * D + pcol);
+      kq[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(K + r * D + pcol));
+      vq[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(V + r * D + pcol));
     }
   };
   load(gr.t0);
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
       const int64_t row = q0 + (int64_t)(BB * st + bb) * 16 + l16;
       const int64_t r = row < n ? row : n - 1;
 #pragma unroll
-      for (int m = 0; m < KM; ++m) q[bb][m] = *reinterpret_cast<const f32x4*>(Q + r * D + m * 16 + g * 4);
+      for (int m = 0; m < KM; ++m) q[bb][m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Q + r * D + m * 16 + g * 4));
     }
   };
   auto compute = [&](int st, const f32x4 (&q)[BB][KM]) {
