@@ -303,8 +303,21 @@ def run_favor():
     S0, z0, c0 = S.clone(), z.clone(), c.clone()
     ms = timed(lambda: ea.la_favor_decode_step(q, k, v, W, S, z, c, scale, out=out))
     BH = w.B * w.H
-    report(w.name, w, ms, BH * (2 * (w.m * w.d + w.m + 1) * 4 + 4 * w.d * 2), favor_flops("decode", BH, w.d, w.m),
-           2 * w.m * BH, {"note": "state [m][d] + z [m] + c fp32 read and written per head, q k v out bf16"})
+    step_bytes = BH * (2 * (w.m * w.d + w.m + 1) * 4 + 4 * w.d * 2)
+    # sustained: 64 consecutive steps (each pays for the previous one's writes), new tokens per step
+    nsteps = 64
+    sq, sk, sv = (draw((nsteps, w.B, w.H, w.d), 30 + t) for t in range(3))
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for t in range(nsteps):
+        ea.la_favor_decode_step(sq[t], sk[t], sv[t], W, S, z, c, scale, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_run = e0.elapsed_time(e1) / nsteps
+    report(w.name, w, ms, step_bytes, favor_flops("decode", BH, w.d, w.m),
+           2 * w.m * BH, {"note": "state [m][d] + z [m] + c fp32 read and written per head, q k v out bf16",
+                          "consecutive_steps": nsteps, "ms_per_step_consecutive": ms_run,
+                          "pct_hbm_peak_consecutive": 100 * step_bytes / (ms_run * 1e-3) / 1e9 / HBM_PEAK_GBS})
     print(json.dumps({"metric": METRIC, "mode": "favor", "n_gpus": 1,
                       "data": "synthetic (seeded N(0,1) bf16 q/k/v on device, i.i.d. N(0,1) projection)",
                       "favor": res}), flush=True)
