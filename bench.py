@@ -472,6 +472,27 @@ def main():
         Q4, K4, V4, C4.chunk, S4in, Z4in, out=O4, Sn=S4out, zn=Z4out))
     del flush
 
+    # the two small fp32 workloads (parity cases; their time is launch latency, reported for
+    # information): warm calls back to back, median per call
+    small = {}
+    for name in ("C1", "C2"):
+        w = WORKLOADS[name]
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev) for x in forward_inputs(w))
+        fn = (lambda: ea.la_forward_noncausal(q, k, v)) if w.form == "noncausal" else \
+             (lambda: ea.la_forward_causal(q, k, v, chunk=w.chunk))
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(20):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1))
+        small[name] = {"form": w.form, "dtype": "f32", "B": w.B, "H": w.H, "n": w.n, "d": w.d,
+                       "chunk": w.chunk, "median_ms": float(np.median(ts))}
+
     # C5 as its own workload: 512 consecutive decode steps of all 8192 heads from the state of
     # the 1024 prior tokens, each step's q, k, v distinct (drawn on the device, seeded, N(0,1)/sqrt(d))
     log("decode: 512 consecutive steps")
@@ -538,6 +559,7 @@ def main():
             "total_ms": total5, "median_step_ms": float(np.median(step5)), "min_step_ms": float(step5.min()),
             "max_step_ms": float(step5.max()), "tokens_per_s": C5.B * C5.n / (total5 * 1e-3),
             "algorithmic_GBps": gbs(b5 * C5.n, total5), "pct_hbm_peak": pct(b5 * C5.n, total5)},
+        "small_fp32_C1_C2": small,
         "decode_C5": {"ms": stage_ms["decode_step"], "tokens_per_s": C5.B / (stage_ms["decode_step"] * 1e-3),
                       "algorithmic_GBps": gbs(b5, stage_ms["decode_step"]),
                       "pct_hbm_peak": pct(b5, stage_ms["decode_step"]),
