@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
     python bench.py --grid      # the metric's grid of shapes, each forward alone (see run_grid)
     python bench.py --favor     # the FAVOR+ feature map on the same shapes (see run_favor)
+    python bench.py --shard     # one GPU's share of the workloads under eight-way sharding (see run_shard)
 
 One step = the whole hot path over one batch of each synthetic workload:
   * non-causal forward, bf16, B=8 H=16 n=16384 d=64 (feature map, split-n KV/z sums, output);
@@ -196,6 +197,88 @@ def run_grid():
                       "grid": points}), flush=True)
 
 
+def run_shard():
+    """One GPU's share of the workloads under the sharding of eight GPUs: by heads (C3 and C4
+    with 16 of their 128 heads, C5 with 1024 of its 8192 heads) and, for the causal form, by
+    sequence (C4 with n / 8 = 8192 tokens of every head, from an incoming state, writing the
+    outgoing one: the per-GPU step of the cross-GPU prefix scan).  Seeded inputs drawn on the
+    device; each call timed alone after a cache-evicting read (median of 5)."""
+    import torch
+
+    import efficient_attention_amd as ea
+    from seeded_inputs import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    flush = torch.ones(1 << 28, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        times = []
+        for _ in range(5):
+            flush.sum()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    def draw(shape, tag):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(zlib.crc32(repr(("shard",) + tuple(shape) + (tag,)).encode()))
+        return (torch.randn(*shape, device=dev, generator=gen) * shape[-1] ** -0.5).to(torch.bfloat16)
+
+    points = []
+
+    def report(name, shape, ms, nbytes, tokens, extra=None):
+        r = {"shard": name, "shape": shape, "isolated_ms": ms, "tokens_per_s": tokens / (ms * 1e-3),
+             "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+             "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if extra:
+            r.update(extra)
+        points.append(r)
+        print("[bench] shard %s" % json.dumps(r), file=sys.stderr, flush=True)
+
+    C3, C4, C5 = WORKLOADS["C3"], WORKLOADS["C4"], WORKLOADS["C5"]
+    # by heads: 16 of 128 heads
+    for w, form in ((C3, "noncausal"), (C4, "causal")):
+        shape = (1, 16, w.n, w.d)
+        q, k, v = (draw(shape, t) for t in range(3))
+        out = torch.empty_like(q)
+        fn = (lambda: ea.la_forward_noncausal(q, k, v, out=out)) if form == "noncausal" else \
+             (lambda: ea.la_forward_causal(q, k, v, chunk=w.chunk, out=out))
+        report("%s by heads (16 of 128)" % w.name, list(shape), timed(fn), algorithmic_bytes(*shape, 2), w.n,
+               {"form": form, "segments_per_head": (-(-w.n // ea.la_causal_plan(*shape, w.chunk, torch.bfloat16))
+                                                     if form == "causal" else None)})
+        del q, k, v, out
+    # by sequence: C4 with n / 8 tokens of all 128 heads, state in and out
+    shape = (C4.B, C4.H, C4.n // 8, C4.d)
+    q, k, v = (draw(shape, 10 + t) for t in range(3))
+    out = torch.empty_like(q)
+    S0 = torch.rand((C4.B, C4.H, C4.d, C4.d), device=dev) * 0.01
+    z0 = torch.rand((C4.B, C4.H, C4.d), device=dev) + 1.0
+    Sn, zn = torch.empty_like(S0), torch.empty_like(z0)
+    state_bytes = 2 * C4.B * C4.H * (C4.d * C4.d + C4.d) * 4
+    ms = timed(lambda: ea.la_forward_causal_state(q, k, v, C4.chunk, S0, z0, out=out, Sn=Sn, zn=zn))
+    report("C4 by sequence (n/8 = %d tokens, state in and out)" % shape[2], list(shape), ms,
+           algorithmic_bytes(*shape, 2) + state_bytes, C4.B * shape[2],
+           {"form": "causal", "segments_per_head": -(-shape[2] // ea.la_causal_plan(*shape, C4.chunk, torch.bfloat16))})
+    del q, k, v, out, S0, z0, Sn, zn
+    # decode by sequences: 32 of 256
+    B5 = C5.B // 8
+    S = torch.rand((B5, C5.H, C5.d, C5.d), device=dev) * 0.01
+    z = torch.rand((B5, C5.H, C5.d), device=dev) + 1.0
+    q, k, v = (draw((B5, C5.H, C5.d), 20 + t) for t in range(3))
+    out = torch.empty_like(q)
+    ms = timed(lambda: ea.la_decode_step(q, k, v, S, z, out=out))
+    report("C5 by sequences (32 of 256)", [B5, C5.H, C5.d], ms, decode_bytes(B5 * C5.H, C5.d, 2), B5,
+           {"form": "decode"})
+    print(json.dumps({"metric": METRIC, "mode": "shard", "n_gpus": 1,
+                      "data": "synthetic (seeded N(0,1)/sqrt(d) bf16 on device)", "shard": points}), flush=True)
+
+
 def favor_flops(form, n_tokens, d, m, chunk=64):
     """Algorithmic MFMA work of the FAVOR+ forms per call (2 flops per multiply-add):
     non-causal per head-token: key and query projections (2 * 2md), state update (2md + 2m),
@@ -329,6 +412,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shard", action="store_true",
+                    help="time one GPU's share of the workloads under eight-way sharding instead of the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 2 GiB (reference for HBM counters)")
     ap.add_argument("--grid", action="store_true",
@@ -346,6 +431,9 @@ def main():
         return
     if args.favor:
         run_favor()
+        return
+    if args.shard:
+        run_shard()
         return
 
     import torch

@@ -474,7 +474,7 @@ __device__ __forceinline__ void head_state(const NcOutArgs& a, int64_t bh, int t
 // so the query tile passes through a wave-private LDS tile (phi applied on the way in), and
 // so does the output tile on its way out.  On this device streaming whole rows is ~8% faster
 // than streaming the 64-byte row pieces the operand layout would load directly.
-template <int D, class TB>
+template <int D, class TB, int QTV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2))) void nc_out_bf16(NcOutArgs a, TB tb) {
   constexpr int LD = D + 16;  // row stride of 8 mod 64 dwords: conflict-free 16-row reads
   constexpr int NC = D / 16;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
   constexpr int RPI = 64 / BPR;        // rows per wave-wide access
   constexpr int NL = QB / RPI;         // wave-wide accesses per batch
   constexpr int ST = QB * D;           // staging tile (QB rows x D) elements
-  constexpr int64_t QT = nc_queries(D, 1);  // queries per workgroup
+  constexpr int64_t QT = QTV;  // queries per workgroup (nc_queries, or less when the heads are few)
   constexpr int QPW = (int)QT / 4;          // queries per wave
   __shared__ __attribute__((aligned(16))) uint16_t KVt[D * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LD];
@@ -789,14 +789,30 @@ hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s) {
   return d == 64 ? launch_state_reduce_t<64>(a, s) : launch_state_reduce_t<128>(a, s);
 }
 
+// bf16 output tiles: nc_queries(D, 1) queries per workgroup, halved (down to 512 at D = 64,
+// 2048 at D = 128, where smaller tiles spill registers) while the launch would leave compute
+// units idle (fewer than 256 workgroups, e.g. a few heads)
+template <int D, class TB, int QTV>
+static void launch_nc_out_bf16(const NcOutArgs& a, hipStream_t s, const TB& tb) {
+  const int64_t tiles = (a.n + QTV - 1) / QTV;
+  if constexpr (QTV > (D == 128 ? 2048 : 512)) {
+    if (a.bh * tiles < 256) {
+      launch_nc_out_bf16<D, TB, QTV / 2>(a, s, tb);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((nc_out_bf16<D, TB, QTV>), dim3((unsigned)(a.bh * tiles)), dim3(256), 0, s, a, tb);
+}
+
 template <int D, class TB>
 static void launch_nc_out_tb(const NcOutArgs& a, int dtype, hipStream_t s, const TB& tb) {
+  if (dtype == 1) {
+    launch_nc_out_bf16<D, TB, (int)nc_queries(D, 1)>(a, s, tb);
+    return;
+  }
   const int64_t qt = nc_queries(D, dtype);
   const int64_t blocks = a.bh * ((a.n + qt - 1) / qt);
-  if (dtype == 1)
-    hipLaunchKernelGGL((nc_out_bf16<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
-  else
-    hipLaunchKernelGGL((nc_out_f32<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
+  hipLaunchKernelGGL((nc_out_f32<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
 }
 
 template <int D>
