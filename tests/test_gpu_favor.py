@@ -311,3 +311,36 @@ def test_favor_causal_chunk128_final_state_and_large_exponents(ea):
     St, zt = _true_state(torch, S, z, c)
     assert normwise_err(St, Sref) <= TOL_BF16
     assert normwise_err(zt, zref, head_axes_last=1) <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------- invariants
+@pytest.mark.parametrize("form", ["noncausal", "causal"])
+def test_favor_forward_invariants_and_determinism(ea, form):
+    """Properties every positive feature map gives eq. Attention_i, checked on the FAVOR+ forwards:
+    outputs are convex combinations of value rows (within each column's range of the keys seen),
+    a constant value row comes back unchanged, and two runs are bitwise equal."""
+    B, H, n, d, m = 2, 3, 700, 64, 256
+    q, k, v = _inputs(900 + (form == "causal"), (B, H, n, d))
+    w = _proj(901, m, d, "orf")
+    scale = d ** -0.25
+    tq, tk, tv, tw = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(w, "bf16")
+    fwd = ea.la_favor_forward_noncausal if form == "noncausal" else ea.la_favor_forward_causal
+    say("favor invariants", form)
+    a = from_dev(fwd(tq, tk, tv, tw, scale), "bf16")
+    b = from_dev(fwd(tq, tk, tv, tw, scale), "bf16")
+    assert np.array_equal(a, b)
+    V = f64(v, "bf16")
+    if form == "noncausal":
+        lo = V.min(axis=2, keepdims=True)
+        hi = V.max(axis=2, keepdims=True)
+    else:
+        lo = np.minimum.accumulate(V, axis=2)
+        hi = np.maximum.accumulate(V, axis=2)
+    span = np.abs(V).max()
+    slack = 2e-2 * span  # bf16 features and outputs
+    assert np.all(a >= lo - slack) and np.all(a <= hi + slack)
+    # a constant value row c: every output row is c
+    row = np.linspace(-1.5, 2.0, d, dtype=np.float32)
+    vc = encode(np.broadcast_to(row, (B, H, n, d)).copy(), "bf16")
+    c = from_dev(fwd(tq, tk, to_dev(vc, "bf16"), tw, scale), "bf16")
+    np.testing.assert_allclose(c, np.broadcast_to(f64(vc, "bf16")[0, 0, 0], c.shape), rtol=1e-2, atol=1e-2)
