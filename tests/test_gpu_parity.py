@@ -250,6 +250,24 @@ def test_decode_zero_feature_key_leaves_state(ea):
     np.testing.assert_allclose(o2, f64(v[:, :, 1], "bf16"), rtol=2.0 ** -7, atol=0)  # v to a bf16 ulp
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_noncausal_permutations(ea, dtype):
+    """Eq. Attention_i sums over the keys: permuting the rows of (K, V) together leaves the
+    non-causal outputs unchanged (to rounding: the sums are taken in another order), and
+    permuting the rows of Q permutes the outputs (bitwise: each query row is computed alone)."""
+    d, n = 64, 1500
+    q, k, v = random_inputs(16, (1, 2, n, d), dtype, 1.0 / np.sqrt(d))
+    rng = np.random.default_rng(16)
+    pk = rng.permutation(n)
+    pq = rng.permutation(n)
+    say("permutations", dtype)
+    g = run_forward(ea, "noncausal", q, k, v, dtype)
+    gk = run_forward(ea, "noncausal", q, k[:, :, pk].copy(), v[:, :, pk].copy(), dtype)
+    gq = run_forward(ea, "noncausal", q[:, :, pq].copy(), k, v, dtype)
+    assert normwise_err(gk, g) <= TOL[dtype]
+    assert np.array_equal(gq, g[:, :, pq])
+
+
 def test_calls_on_a_side_stream(ea):
     """Entry points given another stream (a torch stream or its raw handle) run there, with
     their outputs and workspaces allocated on it, while the default stream is busy; results
