@@ -250,6 +250,22 @@ def test_decode_zero_feature_key_leaves_state(ea):
     np.testing.assert_allclose(o2, f64(v[:, :, 1], "bf16"), rtol=2.0 ** -7, atol=0)  # v to a bf16 ulp
 
 
+@pytest.mark.parametrize("form", ["noncausal", "causal"])
+def test_linear_in_values(ea, form):
+    """The output is linear in V for fixed Q, K (eq. Attention_i: fixed weights times values):
+    out(a V1 + b V2) = a out(V1) + b out(V2), fp32 within its bar."""
+    d, n = 128, 900
+    q, k, v1 = random_inputs(17, (1, 2, n, d), "f32", 1.0 / np.sqrt(d))
+    _, _, v2 = random_inputs(18, (1, 2, n, d), "f32", 1.0)
+    a, b = np.float32(0.75), np.float32(-1.25)
+    v3 = (a * v1 + b * v2).astype(np.float32)
+    say("linearity", form)
+    g1 = run_forward(ea, form, q, k, v1, "f32")
+    g2 = run_forward(ea, form, q, k, v2, "f32")
+    g3 = run_forward(ea, form, q, k, v3, "f32")
+    assert normwise_err(g3, float(a) * g1 + float(b) * g2) <= TOL_F32
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_noncausal_permutations(ea, dtype):
     """Eq. Attention_i sums over the keys: permuting the rows of (K, V) together leaves the
