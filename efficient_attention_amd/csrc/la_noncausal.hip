@@ -647,13 +647,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
 // rows while it computes (unconditional loads; rows past the end read row n - 1 and are not
 // stored).  The KV^T reads are kept inside the loop (an empty asm statement hides that they
 // repeat): hoisted out of it, KV^T would occupy the register file and leave one wave per SIMD.
-template <int D, class TB>
+template <int D, class TB, int QTV>
 __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
   constexpr int LD = D + 4;
   constexpr int NC = D / 16;
   constexpr int KM = D / 16;                 // 16-feature groups of the reduction
   constexpr int BB = D == 64 ? 2 : 1;        // 16-query blocks per step
-  constexpr int64_t QT = nc_queries(D, 0);  // queries per workgroup
+  constexpr int64_t QT = QTV;  // queries per workgroup (nc_queries, or less when the heads are few)
   constexpr int QPW = (int)QT / 4;
   constexpr int NB = QPW / (16 * BB);        // steps per wave
   static_assert(NB % 2 == 0, "steps come in pairs");
@@ -804,15 +804,26 @@ static void launch_nc_out_bf16(const NcOutArgs& a, hipStream_t s, const TB& tb) 
   hipLaunchKernelGGL((nc_out_bf16<D, TB, QTV>), dim3((unsigned)(a.bh * tiles)), dim3(256), 0, s, a, tb);
 }
 
+// fp32 output tiles likewise, down to 256 queries at D = 64 and 128 at D = 128 (the smallest
+// tiles that keep the kernel's steps in pairs)
+template <int D, class TB, int QTV>
+static void launch_nc_out_f32(const NcOutArgs& a, hipStream_t s, const TB& tb) {
+  const int64_t tiles = (a.n + QTV - 1) / QTV;
+  if constexpr (QTV > (D == 64 ? 256 : 128)) {
+    if (a.bh * tiles < 256) {
+      launch_nc_out_f32<D, TB, QTV / 2>(a, s, tb);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((nc_out_f32<D, TB, QTV>), dim3((unsigned)(a.bh * tiles)), dim3(256), 0, s, a, tb);
+}
+
 template <int D, class TB>
 static void launch_nc_out_tb(const NcOutArgs& a, int dtype, hipStream_t s, const TB& tb) {
-  if (dtype == 1) {
+  if (dtype == 1)
     launch_nc_out_bf16<D, TB, (int)nc_queries(D, 1)>(a, s, tb);
-    return;
-  }
-  const int64_t qt = nc_queries(D, dtype);
-  const int64_t blocks = a.bh * ((a.n + qt - 1) / qt);
-  hipLaunchKernelGGL((nc_out_f32<D, TB>), dim3((unsigned)blocks), dim3(256), 0, s, a, tb);
+  else
+    launch_nc_out_f32<D, TB, (int)nc_queries(D, 0)>(a, s, tb);
 }
 
 template <int D>
