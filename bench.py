@@ -72,9 +72,22 @@ def measured_traffic():
         return None
 
 
+def cpu_model():
+    """The host CPU's model string (/proc/cpuinfo), else what platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
     """The fp64 oracle, as it stands, single-threaded, on a bounded sample of the step's work,
-    scaled to the whole step by head counts (heads are independent and equal-sized)."""
+    scaled to the whole step by head counts (heads are independent and equal-sized).  The
+    process is pinned to one core (in-process affinity) while the oracle runs."""
     import oracle
     from seeded_inputs import bf16_bits_to_f32
 
@@ -82,6 +95,17 @@ def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
         return bf16_bits_to_f32(x).astype(np.float64)
 
     oracle._load()
+    saved = os.sched_getaffinity(0)
+    core = min(saved)
+    os.sched_setaffinity(0, {core})
+    try:
+        return _cpu_baseline_pinned(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec, f64, core)
+    finally:
+        os.sched_setaffinity(0, saved)
+
+
+def _cpu_baseline_pinned(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec, f64, core):
+    import oracle
     # non-causal: 2 heads of n = 16384
     Q, K, V = f64(q3[0, :2]), f64(k3[0, :2]), f64(v3[0, :2])
     t = time.perf_counter()
@@ -92,10 +116,11 @@ def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
     t = time.perf_counter()
     oracle.causal_recurrent(Q, K, V)
     t_c = (time.perf_counter() - t) * (C4.B * C4.H)
-    # decode: one step for 1024 of the 8192 heads
+    # decode: one step for 128 of the 8192 heads (4 sequences x 32 heads)
     dq, dk, dv, S0, z0 = dec
+    dq, dk, dv = f64(dq[:4]), f64(dk[:4]), f64(dv[:4])
     t = time.perf_counter()
-    oracle.decode_step(f64(dq[:4]), f64(dk[:4]), f64(dv[:4]), S0[:4], z0[:4])
+    oracle.decode_step(dq, dk, dv, S0[:4], z0[:4])
     t_d = (time.perf_counter() - t) * (C5.B * C5.H) / (4 * C5.H)
     step_s = t_nc + t_c + t_d
     tokens = C3.B * C3.n + C4.B * C4.n + C5.B
@@ -106,9 +131,11 @@ def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
         "kind": "oracle",
         "sample": ("fp64 C oracle, 1 thread: non-causal 2 of 128 heads (n=16384), causal 1 of 128 "
                    "heads (n=65536, recurrence), decode 1 step of 128 of 8192 heads; each scaled by "
-                   "its head count to one step of %d tokens; step time %.1f s" % (tokens, step_s)),
+                   "its head count to one step of %d tokens; step time %.1f s; process pinned to one core"
+                   % (tokens, step_s)),
         "host_cores": os.cpu_count(),
-        "cpu_model": platform.processor() or platform.machine(),
+        "pinned_core": core,
+        "cpu_model": cpu_model(),
     }
 
 

@@ -34,4 +34,5 @@ from ._binding import (  # noqa: F401
     la_state_sums_workspace_bytes,
     la_status_string,
     load,
+    release_workspaces,
 )

@@ -131,8 +131,10 @@ def la_causal_workspace_bytes(B: int, H: int, n: int, d: int, chunk: int, dtype)
     return int(load().la_causal_workspace_bytes(B, H, n, d, chunk, code))
 
 
-# One reusable workspace per (device, stream): calls queued on one stream never use it
-# concurrently, and each call initialises the part it uses.
+# One reusable workspace per (device, stream) for calls that are not given one: calls queued on
+# one stream never use it concurrently, and each call initialises the part it uses.  It grows to
+# the largest size asked for; release_workspaces() drops them (torch's caching allocator keeps the
+# memory for reuse until torch.cuda.empty_cache()).
 _ws_cache: dict = {}
 
 
@@ -140,11 +142,24 @@ def workspace(nbytes: int, device: torch.device, stream_handle: int) -> torch.Te
     if nbytes == 0:
         return None
     key = (device.index, stream_handle)
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
+    with _lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
     return buf
+
+
+def release_workspaces(device=None) -> int:
+    """Drop the cached workspaces (of one device, or all); returns how many bytes they held.
+    Call it when no queued call can still use them (e.g. after a synchronisation), or pass the
+    workspaces explicitly (ws=) to keep their lifetime in the caller's hands."""
+    idx = None if device is None else torch.device(device).index
+    freed = 0
+    with _lock:
+        for key in [k for k in _ws_cache if idx is None or k[0] == idx]:
+            freed += _ws_cache.pop(key).numel()
+    return freed
 
 
 def _on_stream(fn):
@@ -333,14 +348,30 @@ def la_state_sums(k, v, seg_len: int, nseg: int, sums=None, ws=None, stream=None
     return sums
 
 
+def _check_segment_sums(sums, B, H, n, d, seg_len, device):
+    """The sums la_causal_segments reads: [B, H, ceil(n / seg_len) - 1, d*d + d] fp32 on `device`
+    (the leading segments' [S | z]), or None when each head is one segment."""
+    if seg_len <= 0:
+        raise ValueError("seg_len must be positive")
+    lead = -(-n // seg_len) - 1 if n > 0 else 0
+    if lead <= 0:
+        if sums is not None:
+            raise ValueError("one segment per head takes no sums (sums must be None)")
+        return
+    shape = (B, H, lead, d * d + d)
+    if sums is None or sums.dtype != torch.float32 or tuple(sums.shape) != shape \
+            or not sums.is_contiguous() or sums.device != device:
+        raise ValueError("sums must be a contiguous float32 tensor of shape %s on %s (the "
+                         "ceil(n / seg_len) - 1 leading segments' sums)" % (shape, device))
+
+
 @_on_stream
 def la_causal_segments(q, k, v, sums, seg_len: int, chunk: int = 128, out=None, stream=None):
     """Chunked causal pass where segment s starts from the sum of sums[:, :, :s]."""
     _check_qkv(q, k, v, 4)
     out = _out_like(q, out)
     B, H, n, d = q.shape
-    if sums is not None and (sums.dtype != torch.float32 or not sums.is_contiguous() or sums.device != q.device):
-        raise ValueError("sums must be a contiguous float32 GPU tensor")
+    _check_segment_sums(sums, B, H, n, d, seg_len, q.device)
     sh = _stream_handle(q.device, stream)
     st = load().la_causal_segments(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    sums.data_ptr() if sums is not None else None,

@@ -215,7 +215,7 @@ const char* la_status_string(int status) {
   }
 }
 
-size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype) {
+size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, la_dtype_t dtype) {
   int64_t bh = 0;
   size_t bytes = 0;
   if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
@@ -224,7 +224,7 @@ size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, 
 }
 
 int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
-                         int64_t H, int64_t n, int64_t d, int dtype, void* workspace,
+                         int64_t H, int64_t n, int64_t d, la_dtype_t dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
@@ -259,7 +259,7 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
 }
 
 size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk,
-                                 int dtype) {
+                                 la_dtype_t dtype) {
   int64_t bh = 0;
   size_t bytes = 0;
   if (check_causal(B, H, n, d, chunk, dtype, &bh, &bytes) != LA_OK) return 0;
@@ -270,7 +270,7 @@ size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
   return causal_ws_bytes(plan_state(bh * (segs - 1), seg_len, (int)d, dtype), (int)d);
 }
 
-int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, la_dtype_t dtype,
                    int64_t* seg_len) {
   int64_t bh = 0;
   size_t bytes = 0;
@@ -281,7 +281,7 @@ int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, in
   return LA_OK;
 }
 
-size_t la_state_sums_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype,
+size_t la_state_sums_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, la_dtype_t dtype,
                                      int64_t seg_len, int64_t nseg) {
   int64_t bh = 0;
   size_t bytes = 0;
@@ -291,7 +291,7 @@ size_t la_state_sums_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d,
 }
 
 int la_state_sums(const void* k, const void* v, float* sums, int64_t B, int64_t H, int64_t n,
-                  int64_t d, int dtype, int64_t seg_len, int64_t nseg, void* workspace,
+                  int64_t d, la_dtype_t dtype, int64_t seg_len, int64_t nseg, void* workspace,
                   size_t workspace_bytes, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
@@ -322,7 +322,7 @@ int la_state_sums(const void* k, const void* v, float* sums, int64_t B, int64_t 
 
 int la_causal_segments(const void* q, const void* k, const void* v, void* out,
                        const float* sums, int64_t B, int64_t H, int64_t n, int64_t d,
-                       int64_t chunk, int dtype, int64_t seg_len, void* stream) {
+                       int64_t chunk, la_dtype_t dtype, int64_t seg_len, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
   int st = check_causal(B, H, n, d, chunk, dtype, &bh, &bytes);
@@ -359,7 +359,7 @@ int la_causal_segments(const void* q, const void* k, const void* v, void* out,
 }
 
 int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
-                      int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                      int64_t H, int64_t n, int64_t d, int64_t chunk, la_dtype_t dtype,
                       void* workspace, size_t workspace_bytes, void* stream) {
   return la_forward_causal_state(q, k, v, out, nullptr, nullptr, nullptr, nullptr, B, H, n, d,
                                  chunk, dtype, workspace, workspace_bytes, stream);
@@ -367,7 +367,7 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
 
 int la_forward_causal_state(const void* q, const void* k, const void* v, void* out,
                             const float* S0, const float* z0, float* Sn, float* zn, int64_t B,
-                            int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                            int64_t H, int64_t n, int64_t d, int64_t chunk, la_dtype_t dtype,
                             void* workspace, size_t workspace_bytes, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
@@ -441,7 +441,7 @@ int la_forward_causal_state(const void* q, const void* k, const void* v, void* o
 }
 
 static int decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
-                       const uint8_t* active, int64_t B, int64_t H, int64_t d, int dtype, void* stream) {
+                       const uint8_t* active, int64_t B, int64_t H, int64_t d, la_dtype_t dtype, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
   int st = check_shape(B, H, 1, d, dtype, &bh, &bytes);
@@ -453,9 +453,13 @@ static int decode_step(const void* q, const void* k, const void* v, float* S, fl
     return LA_ERR_ALIGN;
   const size_t sbytes = (size_t)bh * (size_t)(d * d) * sizeof(float);
   const size_t zbytes = (size_t)bh * (size_t)d * sizeof(float);
-  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, S, sbytes) ||
-      overlaps(out, bytes, z, zbytes) || overlaps(S, sbytes, z, zbytes))
+  // S and z are written in place while other workgroups still read q, k and v
+  const void* ins[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(out, bytes, ins[i], bytes) || overlaps(S, sbytes, ins[i], bytes) ||
+        overlaps(z, zbytes, ins[i], bytes))
+      return LA_ERR_ALIAS;
+  if (overlaps(out, bytes, S, sbytes) || overlaps(out, bytes, z, zbytes) || overlaps(S, sbytes, z, zbytes))
     return LA_ERR_ALIAS;
   if (active && (overlaps(active, (size_t)B, out, bytes) || overlaps(active, (size_t)B, S, sbytes) ||
                  overlaps(active, (size_t)B, z, zbytes)))
@@ -477,19 +481,23 @@ static int decode_step(const void* q, const void* k, const void* v, float* S, fl
 }
 
 int la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
-                   int64_t B, int64_t H, int64_t d, int dtype, void* stream) {
+                   int64_t B, int64_t H, int64_t d, la_dtype_t dtype, void* stream) {
   return decode_step(q, k, v, S, z, out, nullptr, B, H, d, dtype, stream);
 }
 
 int la_decode_step_masked(const void* q, const void* k, const void* v, float* S, float* z,
                           void* out, const uint8_t* active, int64_t B, int64_t H, int64_t d,
-                          int dtype, void* stream) {
-  if (!active && B * H > 0) return LA_ERR_NULL;
+                          la_dtype_t dtype, void* stream) {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  const int st = check_shape(B, H, 1, d, dtype, &bh, &bytes);  // B * H is known not to overflow
+  if (st != LA_OK) return st;
+  if (!active && bh > 0) return LA_ERR_NULL;
   return decode_step(q, k, v, S, z, out, active, B, H, d, dtype, stream);
 }
 
 size_t la_noncausal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
-                                           int64_t d, int dtype) {
+                                           int64_t d, la_dtype_t dtype) {
   Varlen vl;
   if (make_varlen(cu_seqlens, nseq, H, d, dtype, &vl) != LA_OK || vl.bh == 0 || vl.maxn == 0) return 0;
   return nc_ws_bytes(plan_state(vl.bh, vl.maxn, (int)d, dtype), (int)d);
@@ -497,7 +505,7 @@ size_t la_noncausal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t ns
 
 int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, void* out,
                                 const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
-                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                                la_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   Varlen vl;
   int st = make_varlen(cu_seqlens, nseq, H, d, dtype, &vl);
   if (st != LA_OK) return st;
@@ -530,7 +538,7 @@ int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, voi
 }
 
 size_t la_causal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
-                                        int64_t d, int64_t chunk, int dtype) {
+                                        int64_t d, int64_t chunk, la_dtype_t dtype) {
   Varlen vl;
   if (make_varlen(cu_seqlens, nseq, H, d, dtype, &vl) != LA_OK || vl.bh == 0 || vl.maxn == 0) return 0;
   if (chunk != 64 && chunk != 128) return 0;
@@ -542,7 +550,7 @@ size_t la_causal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq,
 
 int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* out,
                              const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
-                             int64_t chunk, int dtype, void* workspace, size_t workspace_bytes,
+                             int64_t chunk, la_dtype_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
   Varlen vl;
   int st = make_varlen(cu_seqlens, nseq, H, d, dtype, &vl);
@@ -594,7 +602,7 @@ int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* 
 
 // ---------------------------------------------------------------- FAVOR+
 size_t la_favor_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
-                                          int dtype) {
+                                          la_dtype_t dtype) {
   int64_t bh = 0;
   size_t bytes = 0;
   if (check_favor(B, H, n, d, m, dtype, &bh, &bytes) != LA_OK || bh == 0 || n == 0) return 0;
@@ -603,7 +611,7 @@ size_t la_favor_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64
 
 int la_favor_forward_noncausal(const void* q, const void* k, const void* v, const void* w,
                                void* out, int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
-                               float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               float scale, la_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
@@ -661,7 +669,7 @@ int la_favor_forward_noncausal(const void* q, const void* k, const void* v, cons
 
 int la_favor_decode_step(const void* q, const void* k, const void* v, const void* w, float* S,
                          float* z, float* c, void* out, int64_t B, int64_t H, int64_t d, int64_t m,
-                         float scale, int dtype, void* stream) {
+                         float scale, la_dtype_t dtype, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;
   int st = check_favor(B, H, 1, d, m, dtype, &bh, &bytes);
@@ -702,7 +710,7 @@ int la_favor_decode_step(const void* q, const void* k, const void* v, const void
 }
 
 size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
-                                       int64_t chunk, int dtype) {
+                                       int64_t chunk, la_dtype_t dtype) {
   int64_t bh = 0;
   size_t bytes = 0;
   if (check_favor(B, H, n, d, m, dtype, &bh, &bytes) != LA_OK || bh == 0 || n == 0) return 0;
@@ -712,7 +720,7 @@ size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t 
 
 int la_favor_forward_causal(const void* q, const void* k, const void* v, const void* w, void* out,
                             float* Sn, float* zn, float* cn, int64_t B, int64_t H, int64_t n,
-                            int64_t d, int64_t m, int64_t chunk, float scale, int dtype,
+                            int64_t d, int64_t m, int64_t chunk, float scale, la_dtype_t dtype,
                             void* workspace, size_t workspace_bytes, void* stream) {
   int64_t bh = 0;
   size_t bytes = 0;

@@ -31,8 +31,10 @@
  * Inputs whose phi underflows to zero for every feature (entries below about -87 in fp32)
  * give the IEEE result of 0/0, as the formula would.
  *
- * Supported shapes: d in {64, 128}; chunk in {64, 128}; element types fp32 and bf16
- * (state and accumulation are always fp32).
+ * Supported shapes: d in {64, 128}; element types fp32 and bf16 (state and accumulation are
+ * always fp32); causal chunk in {64, 128} for bf16, and for fp32 with d * chunk <= 8192 (d = 64:
+ * 64 or 128; d = 128: 64 only -- the fp32 kernel keeps two chunk tiles and the transposed state
+ * in LDS), else LA_ERR_UNSUPPORTED.
  */
 #ifndef LINATTN_H
 #define LINATTN_H
@@ -46,7 +48,15 @@ extern "C" {
 
 #define LA_ABI_VERSION 1
 
-typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+/* Element type of q, k, v and out.  The two range markers give the type every int value, so an
+ * unknown code passed across the ABI is a defined value, which every entry point rejects with
+ * LA_ERR_DTYPE. */
+typedef enum {
+  LA_DTYPE_F32 = 0,
+  LA_DTYPE_BF16 = 1,
+  LA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  LA_DTYPE_RANGE_MAX_ = 2147483647
+} la_dtype_t;
 
 enum {
   LA_OK = 0,
@@ -69,7 +79,7 @@ const char* la_status_string(int status);
 
 /* Bytes of device workspace la_forward_noncausal needs for this shape (0 for an empty
  * shape; (size_t)0 also for unsupported arguments, which the call itself reports). */
-size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype);
+size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, la_dtype_t dtype);
 
 /*
  * Non-causal forward: every query attends to all n keys of its (b, h).
@@ -85,17 +95,18 @@ size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, 
  * the queries.
  */
 int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
-                         int64_t H, int64_t n, int64_t d, int dtype, void* workspace,
+                         int64_t H, int64_t n, int64_t d, la_dtype_t dtype, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace la_forward_causal needs (may be 0). */
 size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk,
-                                 int dtype);
+                                 la_dtype_t dtype);
 
 /*
  * Causal forward: query i attends to keys j <= i (inclusive) of its (b, h).
  *   q, k, v, out : as for la_forward_noncausal
- *   chunk        : 64 or 128; the tile of the chunked evaluation.  Within a chunk the masked
+ *   chunk        : 64 or 128 (fp32: d * chunk <= 8192, so 64 at d = 128; others give
+ *                  LA_ERR_UNSUPPORTED); the tile of the chunked evaluation.  Within a chunk the masked
  *                  pairwise weights are used directly, earlier tokens enter through the
  *                  running state (S, z) ("The recurrent view"); the result does not depend
  *                  on chunk beyond rounding.
@@ -103,7 +114,7 @@ size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
  *                  non-causal workspace (may be NULL when that size is 0).
  */
 int la_forward_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
-                      int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                      int64_t H, int64_t n, int64_t d, int64_t chunk, la_dtype_t dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -124,7 +135,7 @@ int la_forward_causal(const void* q, const void* k, const void* v, void* out, in
  */
 int la_forward_causal_state(const void* q, const void* k, const void* v, void* out,
                             const float* S0, const float* z0, float* Sn, float* zn, int64_t B,
-                            int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+                            int64_t H, int64_t n, int64_t d, int64_t chunk, la_dtype_t dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -147,19 +158,19 @@ int la_forward_causal_state(const void* q, const void* k, const void* v, void* o
  * sum_{s' < s} sums[b][h][s'] (zero for s = 0), so sums must hold ceil(n/seg_len) - 1 entries
  * per head: [B][H][ceil(n/seg_len) - 1][d*d + d] (may be NULL when that count is 0).
  */
-int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, int dtype,
+int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, la_dtype_t dtype,
                    int64_t* seg_len);
 
-size_t la_state_sums_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int dtype,
+size_t la_state_sums_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, la_dtype_t dtype,
                                      int64_t seg_len, int64_t nseg);
 
 int la_state_sums(const void* k, const void* v, float* sums, int64_t B, int64_t H, int64_t n,
-                  int64_t d, int dtype, int64_t seg_len, int64_t nseg, void* workspace,
+                  int64_t d, la_dtype_t dtype, int64_t seg_len, int64_t nseg, void* workspace,
                   size_t workspace_bytes, void* stream);
 
 int la_causal_segments(const void* q, const void* k, const void* v, void* out,
                        const float* sums, int64_t B, int64_t H, int64_t n, int64_t d,
-                       int64_t chunk, int dtype, int64_t seg_len, void* stream);
+                       int64_t chunk, la_dtype_t dtype, int64_t seg_len, void* stream);
 
 /*
  * Variable-length batches: nseq sequences of n_s tokens each, every one laid out as the fixed
@@ -174,18 +185,18 @@ int la_causal_segments(const void* q, const void* k, const void* v, void* out,
  * LA_ERR_SHAPE, a NULL cu_seqlens LA_ERR_NULL.
  */
 size_t la_noncausal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
-                                           int64_t d, int dtype);
+                                           int64_t d, la_dtype_t dtype);
 
 int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, void* out,
                                 const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
-                                int dtype, void* workspace, size_t workspace_bytes, void* stream);
+                                la_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t la_causal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,
-                                        int64_t d, int64_t chunk, int dtype);
+                                        int64_t d, int64_t chunk, la_dtype_t dtype);
 
 int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* out,
                              const int64_t* cu_seqlens, int64_t nseq, int64_t H, int64_t d,
-                             int64_t chunk, int dtype, void* workspace, size_t workspace_bytes,
+                             int64_t chunk, la_dtype_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream);
 
 /*
@@ -200,7 +211,7 @@ int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* 
  * The state is the whole checkpoint: copying S and z out and back resumes bit-exactly.
  */
 int la_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* out,
-                   int64_t B, int64_t H, int64_t d, int dtype, void* stream);
+                   int64_t B, int64_t H, int64_t d, la_dtype_t dtype, void* stream);
 
 /*
  * la_decode_step for the sequences whose flag is set: active is a DEVICE array of B bytes
@@ -210,7 +221,7 @@ int la_decode_step(const void* q, const void* k, const void* v, float* S, float*
  */
 int la_decode_step_masked(const void* q, const void* k, const void* v, float* S, float* z,
                           void* out, const uint8_t* active, int64_t B, int64_t H, int64_t d,
-                          int dtype, void* stream);
+                          la_dtype_t dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * FAVOR+ feature map.  "Efficient Transformers: Linear Attention and Flash Attention" (section
@@ -238,7 +249,7 @@ int la_decode_step_masked(const void* q, const void* k, const void* v, float* S,
 
 /* Workspace bytes of la_favor_forward_noncausal for this shape (0 for an empty or invalid one). */
 size_t la_favor_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
-                                          int dtype);
+                                          la_dtype_t dtype);
 
 /*
  * Non-causal FAVOR+ attention: out_i = phi(q_i)^T S / phi(q_i)^T z over all n keys of the head.
@@ -249,12 +260,12 @@ size_t la_favor_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64
  */
 int la_favor_forward_noncausal(const void* q, const void* k, const void* v, const void* w,
                                void* out, int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
-                               float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               float scale, la_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
 /* Workspace bytes of la_favor_forward_causal (0: none needed, or an invalid shape). */
 size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t m,
-                                       int64_t chunk, int dtype);
+                                       int64_t chunk, la_dtype_t dtype);
 
 /*
  * Causal FAVOR+ attention (j <= i), chunked ("The recurrent view": the prefix sums S_i, z_i split
@@ -271,7 +282,7 @@ size_t la_favor_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t 
  */
 int la_favor_forward_causal(const void* q, const void* k, const void* v, const void* w, void* out,
                             float* Sn, float* zn, float* cn, int64_t B, int64_t H, int64_t n,
-                            int64_t d, int64_t m, int64_t chunk, float scale, int dtype,
+                            int64_t d, int64_t m, int64_t chunk, float scale, la_dtype_t dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -287,7 +298,7 @@ int la_favor_forward_causal(const void* q, const void* k, const void* v, const v
  */
 int la_favor_decode_step(const void* q, const void* k, const void* v, const void* w, float* S,
                          float* z, float* c, void* out, int64_t B, int64_t H, int64_t d, int64_t m,
-                         float scale, int dtype, void* stream);
+                         float scale, la_dtype_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

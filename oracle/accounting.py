@@ -1,68 +1,69 @@
-"""Analytic cost accounting that the pages print for linear vs standard attention.
+"""Analytic cost figures the pages print for linear and softmax attention.
 
 TEST INFRASTRUCTURE ONLY (same rule as the rest of ``oracle/``).
 
-Restated from:
-  * "Linear Attention > Memory Efficiency" (mbrenndoerfer.com, Language AI Handbook ch. 123,
-    section 7), code cell In[17] and its table Out[19]: the standard form stores the n x n
-    weights (n^2 values); the linear form stores the D x d aggregate plus the D-vector key
-    sum (D*d + D values), independent of n.
-  * "Linear Attention > Computational Complexity Analysis" (same chapter, section 6), code
-    cell In[14] and its table Out[15]: standard attention costs 2n^2 d (QK^T) + 5n^2
-    (softmax) + 2n^2 d (weights times V); linear attention costs 2nd (feature map, a
-    simplified count) + 2nDd (phi(K)^T V) + 2nDd (phi(Q) KV) + 2nD + n (normalisation).
+What the formulas are (restated, not transcribed):
+  * "Linear Attention > Computational Complexity Analysis" (mbrenndoerfer.com, Language AI
+    Handbook ch. 123, section 6) counts linear attention at 2nd + 4nDd + 2nD + n operations:
+    every token pays 2d for the feature map (the page calls this count simplified), 2Dd for its
+    share of phi(K)^T V, 2Dd for phi(q) times the aggregate, 2D for the normaliser's dot product
+    and one division.  Softmax attention pays 4n^2 d + 5n^2: two n x n x d products and five
+    operations per score for the softmax.  Its table Out[15] prints both at d = D = 64.
+  * "Linear Attention > Memory Efficiency" (same chapter, section 7): the softmax form keeps n^2
+    scores, the linear form a D x d aggregate and a D-vector key sum, whatever n is.  Its table
+    Out[19] prints both in fp32 at d = 64, the first in MB of 10^6 bytes and the second in KB of
+    1024 bytes.
   * Hoefler, "Let's Stop Calling Everything 'Linear Attention'", section 2 (memory-load
-    traffic): a decode step's time is bounded below by the bytes it moves divided by the
-    effective bandwidth.
+    traffic): a decode step cannot take less than the bytes it moves over the bandwidth.
 
+D is the feature dimension; for an elementwise feature map such as elu + 1 it equals d.
 Pinned by ``tests/test_accounting.py`` against every printed row of both tables.
 """
 from __future__ import annotations
 
 
-def memory_standard_attention(n: int, d: int, dtype_bytes: int = 4) -> int:
-    """Bytes of the n x n attention weights (independent of d)."""
-    return n * n * dtype_bytes
+def linear_flops_per_token(d: int, features: int) -> int:
+    """Operations one token costs in the linear form: 2d + 4Dd + 2D + 1."""
+    return 2 * d + 4 * features * d + 2 * features + 1
 
 
-def memory_linear_attention(n: int, d: int, D: int | None = None, dtype_bytes: int = 4) -> int:
-    """Bytes of the D x d key-value aggregate plus the D-vector key sum (independent of n)."""
-    if D is None:
-        D = d
-    return D * d * dtype_bytes + D * dtype_bytes
+def linear_attention_flops(n: int, d: int, features: int | None = None) -> int:
+    """n tokens of the linear form (the cost is the same for every token)."""
+    return n * linear_flops_per_token(d, d if features is None else features)
 
 
-def flops_standard_attention(n: int, d: int) -> int:
-    return 2 * n * n * d + 5 * n * n + 2 * n * n * d
+def softmax_attention_flops(n: int, d: int) -> int:
+    """n^2 scores, each costing 4d for the two products and 5 for the softmax."""
+    return n * n * (4 * d + 5)
 
 
-def flops_linear_attention(n: int, d: int, D: int | None = None) -> int:
-    if D is None:
-        D = d
-    feature = 2 * n * d
-    kv = 2 * n * D * d
-    qkv = 2 * n * D * d
-    norm = 2 * n * D + n
-    return feature + kv + qkv + norm
+def linear_state_bytes(d: int, features: int | None = None, word: int = 4) -> int:
+    """The D x d aggregate and the D-vector key sum: what the linear form keeps, for any n."""
+    D = d if features is None else features
+    return D * (d + 1) * word  # D*d + D words
 
 
-def decode_time_floor_s(bytes_per_step: int, bandwidth_bytes_per_s: float) -> float:
-    """Lower bound on one decode step's time: bytes moved / effective bandwidth."""
-    return bytes_per_step / bandwidth_bytes_per_s
+def score_matrix_bytes(n: int, word: int = 4) -> int:
+    """The n x n scores of the softmax form."""
+    return n * n * word
 
 
-# Formatting used by the printed tables (reproduced so that a test can compare strings).
-def fmt_flops(x: int) -> str:
-    if x >= 1e9:
-        return "%.2fG" % (x / 1e9)
-    return "%.1fM" % (x / 1e6)
+def decode_floor_seconds(step_bytes: int, bytes_per_second: float) -> float:
+    """A decode step cannot beat its traffic over the bandwidth."""
+    return step_bytes / bytes_per_second
 
 
-def fmt_mem_mb(x: int) -> str:
-    """The memory table's MB is 10^6 bytes."""
+# The tables' number formats, so that a test can compare the printed strings.
+def as_ops(x: int) -> str:
+    """Operation counts: mega (10^6) below a giga (10^9), one decimal; giga with two."""
+    return "%.2fG" % (x / 1e9) if x >= 1e9 else "%.1fM" % (x / 1e6)
+
+
+def as_megabytes(x: int) -> str:
+    """The memory table's MB: 10^6 bytes, one decimal."""
     return "%.1f MB" % (x / 1e6)
 
 
-def fmt_mem_kb(x: int) -> str:
-    """The memory table's KB is 1024 bytes (16,640 B prints as 16.2 KB)."""
+def as_kibibytes(x: int) -> str:
+    """The memory table's KB: 1024 bytes, one decimal (16,640 B prints as 16.2 KB)."""
     return "%.1f KB" % (x / 1024)

@@ -171,6 +171,47 @@ def test_validation_decode():
     assert _dec(lib, z=0x20004) == -5
     assert _dec(lib, out=0x10000) == -7                      # out aliases S
     assert _dec(lib, z=0x10000 + 64) == -7                   # z inside S
+    assert _dec(lib, S=0x1000) == -7                         # S over q (written in place while q is read)
+    assert _dec(lib, z=0x3000) == -7                         # z over v
+    # masked: B and H are validated before the flags are looked at
+    mk = lambda B, H, act: lib.la_decode_step_masked(P(0x1000), P(0x2000), P(0x3000), P(0x10000), P(0x20000),
+                                                     P(0x4000), P(act), B, H, 64, 1, None)
+    assert mk(1 << 40, 1 << 40, None) == -2                  # B * H overflows: a shape error
+    assert mk(-1, 2, None) == -2
+    assert mk(0, 2, None) == 0                               # no heads: no flags needed
+    assert mk(1, 1, 0x10000) == -7                           # flags inside S
+
+
+def test_dtype_codes_outside_the_enum():
+    # la_dtype_t covers every int, so any other code is reported, never assumed valid
+    lib = _lib()
+    for code in (2, 7, -1, -(1 << 31), (1 << 31) - 1):
+        assert _nc(lib, dtype=code) == -3
+        assert _dec(lib, dtype=code) == -3
+
+
+def test_segment_sums_shape_is_checked():
+    # the binding of la_causal_segments rejects sums of the wrong shape before the library reads
+    # them (the kernel reads [B][H][ceil(n / seg_len) - 1][d*d + d] floats)
+    torch = pytest.importorskip("torch")
+    chk = ea._binding._check_segment_sums
+    cpu = torch.device("cpu")
+    B, H, n, d, seg = 2, 3, 1000, 64, 256                      # 4 segments: 3 leading sums
+    good = torch.zeros((B, H, 3, d * d + d), dtype=torch.float32)
+    chk(good, B, H, n, d, seg, cpu)
+    for bad in (torch.zeros((B, H, 4, d * d + d)),              # la_state_sums(..., nseg=4) layout
+                torch.zeros((B, H, 2, d * d + d)),              # too few: reads past the end
+                torch.zeros((B, H, 3, d * d)),                  # z missing
+                torch.zeros((B, H, 3, d * d + d), dtype=torch.float64),
+                torch.zeros((H, B, 3, d * d + d)).transpose(0, 1),  # not contiguous
+                None):
+        with pytest.raises(ValueError):
+            chk(bad, B, H, n, d, seg, cpu)
+    chk(None, B, H, 200, d, seg, cpu)                           # one segment: no sums
+    with pytest.raises(ValueError):
+        chk(good, B, H, 200, d, seg, cpu)
+    with pytest.raises(ValueError):
+        chk(good, B, H, n, d, 0, cpu)
 
 
 def test_causal_plan_and_stage_validation():

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from gpu_util import f64, from_dev, need_gpu, say, to_dev
-from metrics import TOL_BF16, normwise_err
+from metrics import TOL_BF16, normwise_err, rowwise_err
 from oracle import favor
 from seeded_inputs import encode, orf_draws, projection
 
@@ -205,7 +205,7 @@ def test_favor_causal_vs_oracle(ea, B, H, n, d, m, kind):
     out = from_dev(ea.la_favor_forward_causal(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
                                               to_dev(w, "bf16"), scale), "bf16")
     ref = _causal_ref(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16"), scale)
-    err = normwise_err(out, ref)
+    err = rowwise_err(out, ref)
     say("  err", err)
     assert err <= TOL_BF16
 
@@ -220,7 +220,7 @@ def test_favor_causal_exponents_beyond_fp32(ea, amp, scale):
                                               to_dev(w, "bf16"), scale), "bf16")
     ref = favor.quadratic(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16"), scale, causal=True)
     assert np.all(np.isfinite(ref))
-    err = normwise_err(out, ref)
+    err = rowwise_err(out, ref)
     say("  err", err)
     assert err <= TOL_BF16
 
@@ -241,7 +241,7 @@ def test_favor_causal_final_state_then_decode(ea, n, d, m):
     Q, K, V, Wd = f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16")
     ref, Sref, zref = favor.causal_recurrent(Q, K, V, Wd, scale, return_state=True)
     _, Spre, zpre = favor.causal_recurrent(Q[:, :, :n], K[:, :, :n], V[:, :, :n], Wd, scale, return_state=True)
-    assert normwise_err(from_dev(out, "bf16"), ref[:, :, :n]) <= TOL_BF16
+    assert rowwise_err(from_dev(out, "bf16"), ref[:, :, :n]) <= TOL_BF16
     St, zt = _true_state(torch, S, z, c)
     assert normwise_err(St, Spre) <= TOL_BF16
     assert normwise_err(zt, zpre, head_axes_last=1) <= TOL_BF16
@@ -288,12 +288,12 @@ def test_favor_causal_chunk128_vs_oracle(ea, B, H, n, d, m):
     say("favor causal chunk 128", B, H, n, d, m)
     out = from_dev(ea.la_favor_forward_causal(tq, tk, tv, tw, scale, chunk=128), "bf16")
     ref = _causal_ref(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16"), scale)
-    err = normwise_err(out, ref)
+    err = rowwise_err(out, ref)
     say("  err", err)
     assert err <= TOL_BF16
     # chunk 64 and chunk 128 agree to rounding
     o64 = from_dev(ea.la_favor_forward_causal(tq, tk, tv, tw, scale, chunk=64), "bf16")
-    assert normwise_err(out, o64) <= TOL_BF16
+    assert rowwise_err(out, o64) <= TOL_BF16
 
 
 def test_favor_causal_chunk128_final_state_and_large_exponents(ea):
@@ -306,7 +306,7 @@ def test_favor_causal_chunk128_final_state_and_large_exponents(ea):
                                               final_state=True)
     Q, K, V, Wd = f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), f64(w, "bf16")
     ref = favor.quadratic(Q, K, V, Wd, 1.0, causal=True)
-    assert normwise_err(from_dev(out, "bf16"), ref) <= TOL_BF16
+    assert rowwise_err(from_dev(out, "bf16"), ref) <= TOL_BF16
     _, Sref, zref = favor.noncausal(Q, K, V, Wd, 1.0, return_state=True)
     St, zt = _true_state(torch, S, z, c)
     assert normwise_err(St, Sref) <= TOL_BF16

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from gpu_util import f64, from_dev, need_gpu, say, to_dev
-from metrics import TOL_BF16, normwise_err
+from metrics import TOL_BF16, form_err, normwise_err, rowwise_err
 from seeded_inputs import WORKLOADS, decode_inputs, forward_inputs
 
 pytestmark = pytest.mark.gpu
@@ -49,8 +49,8 @@ def _check_forward(ea, name, form):
         say(name, "oracle head", b, h)
         Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
         ref = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
-        e = normwise_err(g[b, h], ref)
-        print("%s head (%d,%d) normwise err %.3e" % (name, b, h, e))
+        e = form_err(form, g[b, h], ref)
+        print("%s head (%d,%d) err %.3e" % (name, b, h, e))
         assert e <= TOL_BF16
     # sampled rows of other heads, by the quadratic definition
     rng = np.random.default_rng(7)
@@ -62,7 +62,7 @@ def _check_forward(ea, name, form):
         say(name, "oracle rows", b, h, len(rows))
         Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
         ref = oracle.rows(Q, K, V, rows, causal=(form == "causal"))
-        e = normwise_err(g[b, h][rows][None], ref[None])
+        e = form_err(form, g[b, h][rows][None], ref[None])
         assert e <= TOL_BF16, (b, h, e)
 
 
@@ -147,8 +147,8 @@ def test_c4_causal_in_two_pieces_with_state(ea):
     assert np.all(np.isfinite(g))
     say("C4 pieces vs one call")
     whole = from_dev(ea.la_forward_causal(tq, tk, tv, chunk=w.chunk), w.dtype)
-    e = normwise_err(g, whole)
-    print("C4 two pieces vs one call normwise err %.3e" % e)
+    e = rowwise_err(g, whole)
+    print("C4 two pieces vs one call rowwise err %.3e" % e)
     assert e <= TOL_BF16
     rng = np.random.default_rng(11)
     extra = [0, cut - 1, cut, cut + 1, w.n - 1]
@@ -158,7 +158,7 @@ def test_c4_causal_in_two_pieces_with_state(ea):
         say("C4 pieces oracle rows", b, h, len(rows))
         Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
         ref = oracle.rows(Q, K, V, rows, causal=True)
-        assert normwise_err(g[b, h][rows][None], ref[None]) <= TOL_BF16
+        assert rowwise_err(g[b, h][rows][None], ref[None]) <= TOL_BF16
     say("C4 pieces final state of every head")
     Sg, zg = S2.cpu().numpy(), z2.cpu().numpy()
     worst = 0.0
@@ -205,11 +205,11 @@ def test_grid_point_full_size(ea, form, dtype, n, d):
         rows = _sample_rows(n, extra, rng, count=10)
         say("grid", form, dtype, n, d, "oracle rows", b, h)
         ref = oracle.rows(Q, K, V, rows, causal=(form == "causal"))
-        assert normwise_err(G[rows][None], ref[None]) <= tol, (b, h)
+        assert form_err(form, G[rows][None], ref[None]) <= tol, (b, h)
         if n == 16384 and (b, h) == (0, 0):
             say("grid", form, dtype, n, d, "oracle head")
             whole = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
-            assert normwise_err(G, whole) <= tol
+            assert form_err(form, G, whole) <= tol
 
 
 
@@ -238,8 +238,8 @@ def _favor_forward(ea, name):
     say(name, "oracle head", b, h)
     Q, K, V = (f64(x[b, h], "bf16") for x in (q, k, v))
     ref = favor.causal_recurrent(Q, K, V, Wd, scale) if causal else favor.noncausal(Q, K, V, Wd, scale)
-    e = normwise_err(g[b, h], ref)
-    print("%s head (%d,%d) normwise err %.3e" % (name, b, h, e))
+    e = form_err(w.form, g[b, h], ref)
+    print("%s head (%d,%d) err %.3e" % (name, b, h, e))
     assert e <= TOL_BF16
     # sampled rows of other heads, by the definition
     rng = np.random.default_rng(8)
@@ -251,7 +251,7 @@ def _favor_forward(ea, name):
         say(name, "oracle rows", b, h, len(rows))
         Q, K, V = (f64(x[b, h], "bf16") for x in (q, k, v))
         ref = favor.rows(Q, K, V, Wd, scale, rows, causal)
-        e = normwise_err(g[b, h][rows][None], ref[None])
+        e = form_err(w.form, g[b, h][rows][None], ref[None])
         assert e <= TOL_BF16, (b, h, e)
 
 
