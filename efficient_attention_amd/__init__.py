@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     la_forward_causal_state,
     la_forward_causal_varlen,
     la_forward_noncausal,
+    la_forward_noncausal_noalloc,
+    LA_NOALLOC_SCRATCH_BYTES,
     la_forward_noncausal_varlen,
     la_noncausal_varlen_workspace_bytes,
     la_causal_varlen_workspace_bytes,

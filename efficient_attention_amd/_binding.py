@@ -30,7 +30,9 @@ EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
            "la_noncausal_varlen_workspace_bytes", "la_forward_noncausal_varlen",
            "la_causal_varlen_workspace_bytes", "la_forward_causal_varlen", "la_decode_step_masked",
            "la_favor_noncausal_workspace_bytes", "la_favor_forward_noncausal", "la_favor_decode_step",
-           "la_favor_causal_workspace_bytes", "la_favor_forward_causal")
+           "la_favor_causal_workspace_bytes", "la_favor_forward_causal", "la_forward_noncausal_noalloc")
+
+LA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/linattn.h
 
 _lib = None
 _lock = threading.Lock()
@@ -63,6 +65,8 @@ def load():
         lib.la_noncausal_workspace_bytes.restype = SZ
         lib.la_forward_noncausal.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]
         lib.la_forward_noncausal.restype = I
+        lib.la_forward_noncausal_noalloc.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P]
+        lib.la_forward_noncausal_noalloc.restype = I
         lib.la_causal_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
         lib.la_causal_workspace_bytes.restype = SZ
         lib.la_forward_causal.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
@@ -232,6 +236,20 @@ def la_forward_noncausal(q, k, v, out=None, ws=None, stream=None):
                                      ws.numel() * ws.element_size() if ws is not None else 0, sh)
     if st != LA_OK:
         raise LinAttnError(st, "la_forward_noncausal")
+    return out
+
+
+@_on_stream
+def la_forward_noncausal_noalloc(q, k, v, out=None, stream=None):
+    """la_forward_noncausal with the library's own per-GPU scratch instead of a workspace (the C
+    entry point allocates nothing; pass `out` to allocate nothing here either); returns out."""
+    _check_qkv(q, k, v, 4)
+    out = _out_like(q, out)
+    B, H, n, d = q.shape
+    st = load().la_forward_noncausal_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                             B, H, n, d, _dtype_code(q), _stream_handle(q.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_forward_noncausal_noalloc")
     return out
 
 

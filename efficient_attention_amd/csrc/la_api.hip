@@ -5,8 +5,13 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "la_kernels.h"
 #include "linattn.h"
+
+// Device memory of la_forward_noncausal_noalloc (see scratch_address below).
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -193,6 +198,73 @@ FavorCausalPlan plan_favor_causal(int64_t bh, int64_t n, int d, int m, int64_t c
   return p;
 }
 
+// The non-causal call's checks that do not involve the workspace (same order for both entry
+// points that take one), its plan and the bytes of one [B][H][n][d] tensor.
+struct NcCall {
+  int64_t bh = 0;
+  size_t bytes = 0;
+  StatePlan plan;
+  size_t need = 0;
+};
+
+int check_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                    int64_t n, int64_t d, int dtype, NcCall* c) {
+  int st = check_shape(B, H, n, d, dtype, &c->bh, &c->bytes);
+  if (st != LA_OK) return st;
+  if (c->bh == 0 || n == 0) return LA_OK;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
+  c->plan = plan_state(c->bh, n, (int)d, dtype);
+  c->need = nc_ws_bytes(c->plan, (int)d);
+  if (overlaps(out, c->bytes, q, c->bytes) || overlaps(out, c->bytes, k, c->bytes) ||
+      overlaps(out, c->bytes, v, c->bytes))
+    return LA_ERR_ALIAS;
+  if (!grid_ok(c->plan.groups * c->plan.slices) || !grid_ok(c->bh * cdiv(n, la::nc_queries((int)d, dtype))))
+    return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
+// Both stages on `stream`, the slice partials in `ws` (c.need bytes, validated by the caller).
+int run_noncausal(const NcCall& c, const void* q, const void* k, const void* v, void* out, int64_t n,
+                  int d, int dtype, void* ws, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* parts = reinterpret_cast<float*>(ws);
+  la::KvStateArgs ka = state_args(c.plan, k, v, parts, parts, n, n, 1);
+  if (la::launch_kv_state(ka, d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  la::NcOutArgs oa;  // the output kernel adds each head's slices itself
+  oa.q = q;
+  oa.out = out;
+  oa.state = parts;
+  oa.slices = c.plan.slices;
+  oa.n = n;
+  oa.bh = c.bh;
+  if (la::launch_nc_out(oa, d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  return LA_OK;
+}
+
+// ---- scratch of la_forward_noncausal_noalloc
+// One array per GPU, reserved when the library's code is loaded on that GPU and held until the
+// process ends.  On the host, `scratch` names a stand-in, not device memory: host code takes the
+// array's device address from hipGetSymbolAddress, once per device (with that device current),
+// and passes only that address on.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not looked up)
+
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,36 +298,26 @@ size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, 
 int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
                          int64_t H, int64_t n, int64_t d, la_dtype_t dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  int64_t bh = 0;
-  size_t bytes = 0;
-  int st = check_shape(B, H, n, d, dtype, &bh, &bytes);
-  if (st != LA_OK) return st;
-  if (bh == 0 || n == 0) return LA_OK;
-  if (!q || !k || !v || !out) return LA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
-  const StatePlan p = plan_state(bh, n, (int)d, dtype);
-  const size_t need = nc_ws_bytes(p, (int)d);
-  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  NcCall c;
+  int st = check_noncausal(q, k, v, out, B, H, n, d, dtype, &c);
+  if (st != LA_OK || c.bh == 0 || n == 0) return st;
+  if (!workspace || workspace_bytes < c.need) return LA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LA_ERR_ALIGN;
-  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-      overlaps(out, bytes, v, bytes) || overlaps(out, bytes, workspace, need))
-    return LA_ERR_ALIAS;
-  if (!grid_ok(p.groups * p.slices) || !grid_ok(bh * cdiv(n, la::nc_queries((int)d, dtype))))
-    return LA_ERR_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = reinterpret_cast<char*>(workspace);
-  float* parts = reinterpret_cast<float*>(ws);
-  la::KvStateArgs ka = state_args(p, k, v, parts, parts, n, n, 1);
-  if (la::launch_kv_state(ka, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
-  la::NcOutArgs oa;  // the output kernel adds each head's slices itself
-  oa.q = q;
-  oa.out = out;
-  oa.state = parts;
-  oa.slices = p.slices;
-  oa.n = n;
-  oa.bh = bh;
-  if (la::launch_nc_out(oa, (int)d, dtype, s) != hipSuccess) return LA_ERR_HIP;
-  return LA_OK;
+  if (overlaps(out, c.bytes, workspace, c.need)) return LA_ERR_ALIAS;
+  return run_noncausal(c, q, k, v, out, n, (int)d, dtype, workspace, stream);
+}
+
+int la_forward_noncausal_noalloc(const void* q, const void* k, const void* v, void* out, int64_t B,
+                                 int64_t H, int64_t n, int64_t d, la_dtype_t dtype, void* stream) {
+  NcCall c;
+  int st = check_noncausal(q, k, v, out, B, H, n, d, dtype, &c);
+  if (st != LA_OK || c.bh == 0 || n == 0) return st;
+  if (c.need > LA_NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;  // before any HIP call
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != LA_OK) return st;
+  if (overlaps(out, c.bytes, ws, c.need)) return LA_ERR_ALIAS;
+  return run_noncausal(c, q, k, v, out, n, (int)d, dtype, ws, stream);
 }
 
 size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk,

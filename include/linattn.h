@@ -98,6 +98,25 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
                          int64_t H, int64_t n, int64_t d, la_dtype_t dtype, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * la_forward_noncausal for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and the
+ * same results (bit for bit), with the slice partials kept in a device array of the library
+ * instead of a caller's workspace.  The call allocates nothing and frees nothing.
+ *   q, k, v, out, B, H, n, d, dtype, stream : as for la_forward_noncausal
+ * The array holds LA_NOALLOC_SCRATCH_BYTES bytes per GPU; it is reserved when the library's code
+ * is loaded on a GPU and held until the process ends.  A shape whose partials need more
+ * (la_noncausal_workspace_bytes(...) > LA_NOALLOC_SCRATCH_BYTES: B * H above about 4000 at d = 64
+ * or 500 at d = 128) returns LA_ERR_WORKSPACE before anything is launched.  Every call on
+ * one GPU shares that GPU's array, and each call initialises what it uses: calls that overlap on
+ * one GPU (on different streams, or from different threads without ordering) race and may return
+ * wrong results.  The first call on a device looks up the array's device address there (a HIP
+ * failure is LA_ERR_HIP; a device index of 64 or more is LA_ERR_UNSUPPORTED).
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int la_forward_noncausal_noalloc(const void* q, const void* k, const void* v, void* out, int64_t B,
+                                 int64_t H, int64_t n, int64_t d, la_dtype_t dtype, void* stream);
+
 /* Bytes of device workspace la_forward_causal needs (may be 0). */
 size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk,
                                  la_dtype_t dtype);

@@ -99,6 +99,35 @@ def test_validation_noncausal():
     assert _nc(lib, out=0x100000 + 64) == -7                  # out inside the workspace
 
 
+def test_validation_noncausal_noalloc():
+    # every check happens before the library looks up its scratch (no HIP call on these paths)
+    lib = _lib()
+    na = lambda q=0x1000, k=0x2000, v=0x3000, out=0x4000, B=1, H=1, n=8, d=64, dtype=1: \
+        lib.la_forward_noncausal_noalloc(P(q), P(k), P(v), P(out), B, H, n, d, dtype, None)
+    assert na(dtype=7) == -3
+    assert na(n=-1) == -2
+    assert na(d=96) == -4
+    assert na(n=0, q=0, out=0) == 0
+    assert na(q=0) == -1
+    assert na(out=0x4008) == -5
+    assert na(out=0x1000) == -7
+    limit = ea.LA_NOALLOC_SCRATCH_BYTES
+    assert limit == _header_shift_constant("LA_NOALLOC_SCRATCH_BYTES")
+    # a shape whose partials exceed the scratch is refused with the workspace error
+    big = (4096, 2, 64)  # B*H = 8192 heads at d = 128: one 66 KB state each
+    assert ea.la_noncausal_workspace_bytes(big[0], big[1], big[2], 128, 1) > limit
+    far = 1 << 36  # inputs and output far apart (no overlap)
+    assert na(q=far, k=2 * far, v=3 * far, out=4 * far, B=big[0], H=big[1], n=big[2], d=128) == -6
+    # the bench's non-causal workload fits
+    assert ea.la_noncausal_workspace_bytes(8, 16, 16384, 64, 1) <= limit
+    assert ea.la_noncausal_workspace_bytes(4, 32, 16384, 128, 1) <= limit
+
+
+def _header_shift_constant(name):
+    m = re.search(r"#define\s+%s\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)" % name, open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
 def test_validation_causal():
     lib = _lib()
     assert _ca(lib, chunk=96) == -4
