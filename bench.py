@@ -4,6 +4,7 @@
     python bench.py --grid      # the metric's grid of shapes, each forward alone (see run_grid)
     python bench.py --favor     # the FAVOR+ feature map on the same shapes (see run_favor)
     python bench.py --shard     # one GPU's share of the workloads under eight-way sharding (see run_shard)
+    python bench.py --ceiling   # attainable-bandwidth ceilings: copy, read, the causal kernel's pattern
 
 One step = the whole hot path over one batch of each synthetic workload:
   * non-causal forward, bf16, B=8 H=16 n=16384 d=64 (feature map, split-n KV/z sums, output);
@@ -137,6 +138,76 @@ def _cpu_baseline_pinned(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec, f64, core):
         "pinned_core": core,
         "cpu_model": cpu_model(),
     }
+
+
+def measure_ceilings(ea, torch, dev, stream, q, k, v, out, seg_len, reps=7, segment_variants=()):
+    """Effective bandwidth of three access patterns with checkable results (include/la_ceiling.h):
+    a plain copy of q into out, a read-only stream over q, and the chunked causal kernel's own
+    pattern (out = q + k + v with its launch shape, chunks and stores) at seg_len, and optionally at
+    other segment lengths.  Each run alone after a cache-evicting read, median of `reps`."""
+    flush = torch.ones(1 << 28, dtype=torch.float64, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        times = []
+        for _ in range(reps):
+            flush.sum()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times)), float(np.min(times))
+
+    nb = q.numel() * q.element_size()
+    res = {}
+
+    def put(name, nbytes, fn, extra=None):
+        med, mn = timed(fn)
+        r = {"bytes": nbytes, "ms": med, "min_ms": mn, "GBps": nbytes / (med * 1e-3) / 1e9,
+             "pct_hbm_peak": 100 * nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if extra:
+            r.update(extra)
+        res[name] = r
+
+    put("copy", 2 * nb, lambda: ea.la_ceiling_copy(q, out))
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    put("read", nb, lambda: ea.la_ceiling_read(q, sink=sink))
+    put("causal_pattern", 4 * nb, lambda: ea.la_ceiling_causal_pattern(q, k, v, seg_len, out=out),
+        {"seg_len": seg_len, "segments_per_head": -(-q.shape[2] // seg_len)})
+    for sl in segment_variants:
+        put("causal_pattern_seg%d" % sl, 4 * nb, lambda: ea.la_ceiling_causal_pattern(q, k, v, sl, out=out),
+            {"seg_len": sl, "segments_per_head": -(-q.shape[2] // sl)})
+    del flush
+    return res
+
+
+def run_ceiling():
+    """The attainable-bandwidth ceilings on the C4 tensors (2 GiB each, bf16 [4, 32, 65536, 128]):
+    plain copy, read-only stream, and the chunked causal kernel's pattern at 1, 2 (the kernel's own
+    plan) and 4 segments per head."""
+    import torch
+
+    import efficient_attention_amd as ea
+    from seeded_inputs import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    C4 = WORKLOADS["C4"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(zlib.crc32(b"ceiling"))
+    q, k, v = [(torch.randn(C4.B, C4.H, C4.n, C4.d, device=dev, generator=gen) * C4.d ** -0.5).to(torch.bfloat16)
+               for _ in range(3)]
+    out = torch.empty_like(q)
+    seg_len = ea.la_causal_plan(C4.B, C4.H, C4.n, C4.d, C4.chunk, torch.bfloat16)
+    res = measure_ceilings(ea, torch, dev, stream, q, k, v, out, seg_len,
+                           segment_variants=[sl for sl in (C4.n, C4.n // 4) if sl != seg_len])
+    for name, r in res.items():
+        print("[bench] ceiling %s %s" % (name, json.dumps(r)), file=sys.stderr, flush=True)
+    print(json.dumps({"metric": METRIC, "mode": "ceiling", "n_gpus": 1,
+                      "data": "synthetic (seeded N(0,1)/sqrt(d) bf16 on device, C4 shape)", "ceilings": res}),
+          flush=True)
 
 
 def run_grid():
@@ -447,6 +518,8 @@ def main():
                     help="time every forward of the metric's shape grid instead of the step")
     ap.add_argument("--favor", action="store_true",
                     help="time the FAVOR+ feature map's forms on the same shapes instead of the step")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="measure the attainable-bandwidth ceilings (copy, read, causal pattern) instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -461,6 +534,9 @@ def main():
         return
     if args.shard:
         run_shard()
+        return
+    if args.ceiling:
+        run_ceiling()
         return
 
     import torch
@@ -628,6 +704,9 @@ def main():
     total5 = ev5[0].elapsed_time(ev5[C5.n])
     del D5
 
+    log("ceilings")
+    ceilings = measure_ceilings(ea, torch, dev, stream, Q4, K4, V4, O4, seg_len, reps=5)
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
@@ -682,10 +761,14 @@ def main():
     }
     # dominant kernel: the chunked causal kernel (one launch per la_causal_segments call)
     ach = gbs(b4, stage_ms["causal_chunked"])
+    attainable = ceilings["causal_pattern"]["GBps"]
     roofline = {"kernel": "causal_bf16<128,128> (la_causal_segments, C4)", "bound": "hbm",
                 "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                 "traffic": measured_traffic(), "algorithmic_bytes_per_launch": b4,
-                "avg_launch_ms": stage_ms["causal_chunked"]}
+                "avg_launch_ms": stage_ms["causal_chunked"],
+                "attainable_GBps": attainable, "frac_of_attainable": ach / attainable,
+                "attainable_note": "la_ceiling_causal_pattern on the C4 tensors: the kernel's launch shape, "
+                                   "chunks, loads and stores with out = q + k + v, alone after a cache-evicting read"}
 
     res = {
         "metric": METRIC,
@@ -710,6 +793,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": roofline,
+        "ceilings": ceilings,
         "breakdown": breakdown,
     }
     if not args.no_cpu_baseline:

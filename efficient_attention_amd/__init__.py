@@ -15,6 +15,9 @@ from ._binding import (  # noqa: F401
     la_causal_plan,
     la_causal_segments,
     la_causal_workspace_bytes,
+    la_ceiling_causal_pattern,
+    la_ceiling_copy,
+    la_ceiling_read,
     la_decode_step,
     la_decode_step_masked,
     la_favor_causal_workspace_bytes,

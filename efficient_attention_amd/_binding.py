@@ -30,7 +30,9 @@ EXPORTS = ("la_abi_version", "la_status_string", "la_noncausal_workspace_bytes",
            "la_noncausal_varlen_workspace_bytes", "la_forward_noncausal_varlen",
            "la_causal_varlen_workspace_bytes", "la_forward_causal_varlen", "la_decode_step_masked",
            "la_favor_noncausal_workspace_bytes", "la_favor_forward_noncausal", "la_favor_decode_step",
-           "la_favor_causal_workspace_bytes", "la_favor_forward_causal", "la_forward_noncausal_noalloc")
+           "la_favor_causal_workspace_bytes", "la_favor_forward_causal", "la_forward_noncausal_noalloc",
+           # include/la_ceiling.h
+           "la_ceiling_copy", "la_ceiling_read_sink_words", "la_ceiling_read", "la_ceiling_causal_pattern")
 
 LA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/linattn.h
 
@@ -105,6 +107,14 @@ def load():
         lib.la_favor_forward_causal.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, F, I,
                                                 P, SZ, P]
         lib.la_favor_forward_causal.restype = I
+        lib.la_ceiling_copy.argtypes = [P, P, SZ, P]
+        lib.la_ceiling_copy.restype = I
+        lib.la_ceiling_read_sink_words.argtypes = []
+        lib.la_ceiling_read_sink_words.restype = SZ
+        lib.la_ceiling_read.argtypes = [P, SZ, P, P]
+        lib.la_ceiling_read.restype = I
+        lib.la_ceiling_causal_pattern.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P]
+        lib.la_ceiling_causal_pattern.restype = I
         _lib = lib
     return _lib
 
@@ -595,4 +605,53 @@ def la_favor_forward_causal(q, k, v, w, scale: float, chunk: int = 64, out=None,
         raise LinAttnError(st, "la_favor_forward_causal")
     if final_state:
         return out, Sn, zn, cn
+    return out
+
+
+# ---------------------------------------------------------------- memory-system ceilings (include/la_ceiling.h)
+def _check_bytes_tensor(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous GPU tensor" % name)
+    return t.numel() * t.element_size()
+
+
+@_on_stream
+def la_ceiling_copy(src, dst, stream=None):
+    """dst = src (same number of bytes, a multiple of 16) by the plain-copy measurement kernel."""
+    nb = _check_bytes_tensor(src, "src")
+    if _check_bytes_tensor(dst, "dst") != nb:
+        raise ValueError("src and dst must hold the same number of bytes")
+    st = load().la_ceiling_copy(src.data_ptr(), dst.data_ptr(), nb, _stream_handle(src.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_ceiling_copy")
+    return dst
+
+
+@_on_stream
+def la_ceiling_read(src, sink=None, stream=None):
+    """Reads every byte of src once; returns the per-workgroup XOR words (uint32 as int32)."""
+    nb = _check_bytes_tensor(src, "src")
+    words = int(load().la_ceiling_read_sink_words())
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=src.device)
+    elif sink.dtype != torch.int32 or sink.numel() < words or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous int32 tensor of at least %d words" % words)
+    st = load().la_ceiling_read(src.data_ptr(), nb, sink.data_ptr(), _stream_handle(src.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_ceiling_read")
+    return sink
+
+
+@_on_stream
+def la_ceiling_causal_pattern(q, k, v, seg_len: int, out=None, stream=None):
+    """out = q + k + v ([B, H, n, 128] bf16) with the chunked causal kernel's memory pattern."""
+    _check_qkv(q, k, v, 4)
+    out = _out_like(q, out)
+    B, H, n, d = q.shape
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the causal pattern measurement takes bf16 tensors")
+    st = load().la_ceiling_causal_pattern(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n, d,
+                                          seg_len, _stream_handle(q.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_ceiling_causal_pattern")
     return out

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
-SOURCES = ["la_api.hip", "la_noncausal.hip", "la_causal.hip", "la_decode.hip", "la_favor.hip"]
+SOURCES = ["la_api.hip", "la_noncausal.hip", "la_causal.hip", "la_decode.hip", "la_favor.hip", "la_ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -1,5 +1,5 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol that
-include/linattn.h declares, and rejects bad arguments before launching anything.
+include/*.h declares, and rejects bad arguments before launching anything.
 
 The validation calls pass fake (never dereferenced) addresses: every case here fails or
 returns before the library touches HIP.
@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "linattn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 ea = pytest.importorskip("efficient_attention_amd")
 
@@ -23,9 +24,11 @@ def _lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(la_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def _header_constant(name):
@@ -349,3 +352,21 @@ def test_validation_favor_causal():
     assert ea.la_favor_causal_workspace_bytes(64, 8, 4096, 64, 128, 64, 1) == 0  # one segment per head
     assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 256, 128, 1) == 0  # invalid chunk
     assert ea.la_favor_causal_workspace_bytes(1, 1, 4096, 64, 128, 128, 1) > 0
+
+
+def test_validation_ceilings():
+    lib = _lib()
+    assert lib.la_ceiling_copy(P(0x1000), P(0x100000), 100, None) == -2          # not a multiple of 16
+    assert lib.la_ceiling_copy(P(0x1000), P(0x100000), 0, None) == 0
+    assert lib.la_ceiling_copy(None, P(0x100000), 64, None) == -1
+    assert lib.la_ceiling_copy(P(0x1008), P(0x100000), 64, None) == -5
+    assert lib.la_ceiling_copy(P(0x1000), P(0x1010), 64, None) == -7            # overlap
+    assert lib.la_ceiling_read_sink_words() > 0
+    assert lib.la_ceiling_read(P(0x1000), 48, None, None) == -1
+    assert lib.la_ceiling_read(P(0x1000), 48, P(0x1010), None) == -7
+    cp = lambda d=128, seg=256, n=1000, out=0x4000000: lib.la_ceiling_causal_pattern(
+        P(0x1000000), P(0x2000000), P(0x3000000), P(out), 1, 2, n, d, seg, None)
+    assert cp(d=64) == -4
+    assert cp(seg=100) == -2
+    assert cp(n=0) == 0
+    assert cp(out=0x1000000) == -7
