@@ -761,14 +761,20 @@ def main():
     }
     # dominant kernel: the chunked causal kernel (one launch per la_causal_segments call)
     ach = gbs(b4, stage_ms["causal_chunked"])
+    # the ceiling is timed alone after a cache-evicting read, so it is compared with the kernel
+    # timed the same way (inside the step the kernel can find some of k and v in the 256 MB
+    # memory-side cache, read there by the state sums just before it)
     attainable = ceilings["causal_pattern"]["GBps"]
+    iso_ach = gbs(b4, iso_ms["causal_chunked"])
     roofline = {"kernel": "causal_bf16<128,128> (la_causal_segments, C4)", "bound": "hbm",
                 "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                 "traffic": measured_traffic(), "algorithmic_bytes_per_launch": b4,
                 "avg_launch_ms": stage_ms["causal_chunked"],
-                "attainable_GBps": attainable, "frac_of_attainable": ach / attainable,
-                "attainable_note": "la_ceiling_causal_pattern on the C4 tensors: the kernel's launch shape, "
-                                   "chunks, loads and stores with out = q + k + v, alone after a cache-evicting read"}
+                "attainable_GBps": attainable, "isolated_achieved_GBps": iso_ach,
+                "frac_of_attainable": iso_ach / attainable,
+                "attainable_note": "la_ceiling_causal_pattern on the C4 tensors (the kernel's launch shape, "
+                                   "chunks, loads and stores with out = q + k + v); it and isolated_achieved "
+                                   "are timed alone after a cache-evicting read"}
 
     res = {
         "metric": METRIC,
