@@ -414,7 +414,8 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
 // w, w + 4, ...) and written to S^T after each chunk's update.  The next chunk's K and V rows
 // are loaded into registers while the current chunk is computed.
 template <int D, int C, class TB>
-__global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 4096 ? 3 : 1))) void causal_f32(
+    CausalArgs a, TB tb) {  // three workgroups per CU where the LDS allows (d = 64, 64-token chunks)
   constexpr int LD = D + 4;
   constexpr int NI = C / 16;         // token tiles per chunk
   constexpr int NCW = D / 64;        // state column tiles per wave
@@ -485,6 +486,13 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
   }
   if (tid < D) zf[tid] = zinit;
 
+  // The key sums z run on the MFMA pipe beside the state update, phi(K)^T times a column of ones
+  // (result column 0: lanes l16 == 0, rows 4g + r of the feature tile), each wave for feature
+  // tiles wave + 4i; they are written to zf after each chunk for the next chunk's normalisers.
+  constexpr int NZW = NA / 4;
+  const float one_col = l16 == 0 ? 1.f : 0.f;
+  f32x4 accz[NZW];
+
   // S^T of the initial state for the first chunk's inter-chunk product
   auto write_st = [&]() {
 #pragma unroll
@@ -494,6 +502,11 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
         *reinterpret_cast<f32x4*>(&St[((wave + 4 * p) * 16 + l16) * LD + at * 16 + g * 4]) = accS[at][p];
   };
   write_st();
+  __syncthreads();  // zf holds the initial key sums
+#pragma unroll
+  for (int i = 0; i < NZW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accz[i][r] = l16 == 0 ? zf[(wave + 4 * i) * 16 + g * 4 + r] : 0.f;
 
   // K and V pieces: piece tid + 256 p of a chunk is row (tid / PPR) + (256 / PPR) p, columns
   // 4 (tid % PPR) .. + 3.  Rows past the segment end read row t1 - 1 and are zeroed in LDS.
@@ -591,16 +604,21 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
       const float den = sum_over_groups(dpart) + __shfl(accd[0], l16);
       const int64_t row = c0 + it * 16 + l16;
       if (row < t1) {
+        // one IEEE division per row, then products (within 1.5 ulp of a division per element);
+        // a denominator too small for its reciprocal to be finite keeps the exact divisions
+        const float inv = 1.0f / den;
+        const bool tiny = !(den >= 0x1p-120f);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          f32x4 o = {acco[c][0] / den, acco[c][1] / den, acco[c][2] / den, acco[c][3] / den};
+          f32x4 o = {acco[c][0] * inv, acco[c][1] * inv, acco[c][2] * inv, acco[c][3] * inv};
+          if (tiny) o = f32x4{acco[c][0] / den, acco[c][1] / den, acco[c][2] / den, acco[c][3] / den};
           *reinterpret_cast<f32x4*>(O + row * D + c * 16 + g * 4) = o;
         }
       }
     }
     __syncthreads();  // S^T, z and the tiles are no longer read for outputs
 
-    // state update: S[:, own cols] += phi(K)^T V, z += column sums of phi(K)
+    // state update: S[:, own cols] += phi(K)^T V, z[own feature tiles] += phi(K)^T 1
     for (int ks = 0; ks < C / 4; ++ks) {
 #pragma unroll
       for (int at = 0; at < NA; ++at) {
@@ -609,11 +627,15 @@ __global__ __launch_bounds__(256) void causal_f32(CausalArgs a, TB tb) {
         for (int p = 0; p < NCW; ++p)
           accS[at][p] = mfma_f32(ak, Vn[(ks * 4 + g) * LD + (wave + 4 * p) * 16 + l16], accS[at][p]);
       }
+#pragma unroll
+      for (int i = 0; i < NZW; ++i)
+        accz[i] = mfma_f32(Kn[(ks * 4 + g) * LD + (wave + 4 * i) * 16 + l16], one_col, accz[i]);
     }
-    if (tid < D) {
-      float zs = 0.f;
-      for (int j = 0; j < C; ++j) zs += Kn[j * LD + tid];
-      zf[tid] += zs;
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < NZW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zf[(wave + 4 * i) * 16 + g * 4 + r] = accz[i][r];
     }
     write_st();
     __syncthreads();  // before the next chunk overwrites the tiles

@@ -735,9 +735,14 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
       const float den = sum_over_groups(dpart[bb]);
       const int64_t row = q0 + (int64_t)(BB * st + bb) * 16 + l16;
       if (row < n) {
+        // one IEEE division per row, then products (within 1.5 ulp of a division per element);
+        // a denominator too small for its reciprocal to be finite keeps the exact divisions
+        const float inv = 1.0f / den;
+        const bool tiny = !(den >= 0x1p-120f);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          f32x4 o = {acc[bb][c][0] / den, acc[bb][c][1] / den, acc[bb][c][2] / den, acc[bb][c][3] / den};
+          f32x4 o = {acc[bb][c][0] * inv, acc[bb][c][1] * inv, acc[bb][c][2] * inv, acc[bb][c][3] * inv};
+          if (tiny) o = f32x4{acc[bb][c][0] / den, acc[bb][c][1] / den, acc[bb][c][2] / den, acc[bb][c][3] / den};
           *reinterpret_cast<f32x4*>(O + row * D + c * 16 + g * 4) = o;
         }
       }
