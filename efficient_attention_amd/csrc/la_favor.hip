@@ -532,7 +532,8 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 
   f32x4 sv[RPT];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) sv[r] = *reinterpret_cast<const f32x4*>(S + (int64_t)(rg + RG * r) * D + cg * 4);
+  for (int r = 0; r < RPT; ++r)  // non-temporal, as in decode_step_kernel: read once per step
+    sv[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (int64_t)(rg + RG * r) * D + cg * 4));
 
   const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + h * D;
   const uint16_t* k = reinterpret_cast<const uint16_t*>(a.k) + h * D;
