@@ -90,10 +90,15 @@ __device__ __forceinline__ float prefix_max16(float x) {
 }
 
 // sum of squares of 8 bf16 values, in fp32, fixed order
-__device__ __forceinline__ float sumsq_bf16x8(u32x4 x) {
-  float a = bf_lo(x.x), b = bf_hi(x.x), c = bf_lo(x.y), d = bf_hi(x.y);
-  float e = bf_lo(x.z), f = bf_hi(x.z), g = bf_lo(x.w), h = bf_hi(x.w);
-  return ((a * a + b * b) + (c * c + d * d)) + ((e * e + f * f) + (g * g + h * h));
+// acc + the squares of 8 bf16 values, two products per packed dot instruction (each product is
+// exact in fp32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sq2_bf16(uint32_t w, float acc) {
+  const bf16x2_t x = __builtin_bit_cast(bf16x2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+}
+__device__ __forceinline__ float sumsq_bf16x8(u32x4 x, float acc = 0.f) {
+  return sq2_bf16(x.w, sq2_bf16(x.z, sq2_bf16(x.y, sq2_bf16(x.x, acc))));
 }
 
 __device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
@@ -358,9 +363,14 @@ __global__ __launch_bounds__(256) void favor_reduce(FavorReduceArgs a) {
 //   f = exp(scale (U - max_f U)) packed to bf16 in the result layout: the B operand of the next
 //       product, k slot e of lane group g = stored feature 32 j + 8 g + e;
 //   out^T = St f (A = 16-byte rows of St), den = Zr f; out = out^T / den.
+// element (row, col) of a [.][LEN] tile, 16-byte pieces permuted by the row: 16-row operand
+// reads (ds_read_b128) are conflict-free when the permutation spans 16 rows on rows of 16 or more
+// pieces (XOR with row & 7 there costs a 2-way conflict on every read, measured on gfx950), and
+// 8 rows on 128-byte rows
 template <int LEN>
-__device__ __forceinline__ int swz(int row, int col) {  // element (row, col) of a [.][LEN] tile
-  return row * LEN + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int RM = LEN / 8 >= 16 ? 15 : 7;
+  return row * LEN + ((((col >> 3) ^ (row & RM))) << 3) + (col & 7);
 }
 
 template <int D, int M>
@@ -672,8 +682,13 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   constexpr int RPV = C * PPR / NT;
   constexpr int64_t REC = favor_rec(D, M);
   static_assert(NAW >= 1 && RPV >= 1 && OCT % 2 == 0 && (C == 64 || C == 128), "shape");
+  // a second copy of the chunk's key features, on the state's scale, where LDS has room for it
+  constexpr int kLdsBase = 2 * (C * LDF + NVB * C * D + D * LDF + 16 * LDF + M * LDW) +
+                           4 * (8 + NQW * C + C);
+  constexpr bool KCS = kLdsBase + 2 * C * LDF <= 160 * 1024;
 
   __shared__ __attribute__((aligned(16))) uint16_t Kf[C * LDF];
+  __shared__ __attribute__((aligned(16))) uint16_t Kc[KCS ? C * LDF : 8];  // phi(K_c), state's scale
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NVB][C * D];
   __shared__ __attribute__((aligned(16))) uint16_t St[D * LDF];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDF];
@@ -797,7 +812,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   auto key_exponents = [&](int64_t c0) {
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KA; ++ks) ss += sumsq_bf16x8(kb[ks]);
+    for (int ks = 0; ks < KA; ++ks) ss = sumsq_bf16x8(kb[ks], ss);
     ss = sum_over_rows(ss);
     const bool ok = c0 + it * 16 + l16 < t1;
     const float off = ok ? hs2 * ss + kconst : __builtin_huge_valf();
@@ -819,20 +834,33 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     if (g == 0) tm[part][it * 16 + l16] = mx;
     return wave_max(mx);
   };
-  // phi(K) of the projected rows on their token's scale, into Kf (operand order); a token past
-  // the end (all exponents -inf) gets zero features
+  // phi(K) of the projected rows on their token's scale, into Kf (operand order), and the same
+  // features on the scale c_state of the state they are added to, into Kc: exp(u - c) =
+  // exp(u - m_j) exp(m_j - c), so that the state update takes V as it is; a token past the end
+  // (all exponents -inf) gets zero features in both
   auto token_max = [&](int t) { return NQW == 2 ? fmaxf(tm[0][t], tm[NQW - 1][t]) : tm[0][t]; };
-  auto store_kf = [&]() {
+  auto store_kf = [&](float c_state) {
     const int t = it * 16 + l16;
     const float mt = token_max(t);
-    const float sh = mt == kNegInf ? 0.f : mt;
+    const float sh_l2 = mt == kNegInf ? 0.f : mt * kLog2e;
+    const float et = (mt == kNegInf || c_state == kNegInf) ? 0.f : fexp(mt - c_state);
 #pragma unroll
     for (int ft = 0; ft < HF; ++ft) {
       const int f = hf0 + ft;
+      float w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = fexp_shift(uk[ft][r], kLog2e, sh_l2);
       u32x2 w2;
-      w2.x = pack_bf16(fexp(uk[ft][0] - sh), fexp(uk[ft][1] - sh));
-      w2.y = pack_bf16(fexp(uk[ft][2] - sh), fexp(uk[ft][3] - sh));
-      *reinterpret_cast<u32x2*>(&Kf[t * LDF + 32 * (f >> 1) + 8 * g + 4 * (f & 1)]) = w2;
+      w2.x = pack_bf16(w[0], w[1]);
+      w2.y = pack_bf16(w[2], w[3]);
+      const int o = t * LDF + 32 * (f >> 1) + 8 * g + 4 * (f & 1);
+      *reinterpret_cast<u32x2*>(&Kf[o]) = w2;
+      if constexpr (KCS) {
+        u32x2 c2;
+        c2.x = pack_bf16(w[0] * et, w[1] * et);
+        c2.y = pack_bf16(w[2] * et, w[3] * et);
+        *reinterpret_cast<u32x2*>(&Kc[o]) = c2;
+      }
     }
   };
   // m_j of the chunk's tokens (into mk, one wave per token tile) and P_i of this lane's query:
@@ -863,7 +891,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
   float al = c_cur == kNegInf ? 0.f : fexp(c_cur - c_next);
-  store_kf();
+  store_kf(c_next);
   float pq = chunk_maxima(c_cur);  // P_i of this lane's query in the coming chunk
   write_state();  // the initial state, on scale c_cur
   float c_prev = c_cur;  // scale of the state in St
@@ -905,45 +933,67 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     load_q(c0 + C);
     __builtin_amdgcn_sched_barrier(0);
 
-    // (i) state: rescale to this chunk's log-scale, then S += phi~(K_c)^T (e V_c), z += phi~(K_c)^T e
-    // with e_j = exp(m_j - c) for the tokens of the operands' k slots
-#pragma unroll
-    for (int i = 0; i < NAW; ++i) {
-      accz[i] *= al;
-#pragma unroll
-      for (int j = 0; j < NCW; ++j) accS[i][j] *= al;
-    }
-#pragma unroll
-    for (int ks = 0; ks < KJ; ++ks) {
-      const f32x4 m_lo = *reinterpret_cast<const f32x4*>(&mk[ks * 32 + 4 * g]);
-      const f32x4 m_hi = *reinterpret_cast<const f32x4*>(&mk[ks * 32 + 16 + 4 * g]);
-      float e8[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        e8[r] = fexp(m_lo[r] - c_cur);
-        e8[4 + r] = fexp(m_hi[r] - c_cur);
-      }
-      u32x4 bz;  // column 0: the factors; other columns zero
-      bz.x = pack_bf16(e8[0], e8[1]);
-      bz.y = pack_bf16(e8[2], e8[3]);
-      bz.z = pack_bf16(e8[4], e8[5]);
-      bz.w = pack_bf16(e8[6], e8[7]);
-      bz = keep_if(bz, zown && l16 == 0);
-      u32x4 bv[NCW];
-#pragma unroll
-      for (int j = 0; j < NCW; ++j) {
-        const u32x4 raw = ld_v_rows<D>(Vc, ks * 32, (sc0 + j) * 16, l16, g);
-        bv[j].x = pack_bf16(bf_lo(raw.x) * e8[0], bf_hi(raw.x) * e8[1]);
-        bv[j].y = pack_bf16(bf_lo(raw.y) * e8[2], bf_hi(raw.y) * e8[3]);
-        bv[j].z = pack_bf16(bf_lo(raw.z) * e8[4], bf_hi(raw.z) * e8[5]);
-        bv[j].w = pack_bf16(bf_lo(raw.w) * e8[6], bf_hi(raw.w) * e8[7]);
-      }
+    // (i) state: rescale to this chunk's log-scale c (skipped when c did not move: al = 1 is the
+    // usual case once the running maximum has settled), then S += phi(K_c)^T V_c and
+    // z += phi(K_c)^T 1 with the key features on scale c (Kc)
+    if (al != 1.f) {
 #pragma unroll
       for (int i = 0; i < NAW; ++i) {
-        const u32x4 ak = ld_rows_operand(Kf, LDF, ks * 32, (sa0 + i) * 16, l16, g);
-        accz[i] = mfma_bf16(ak, bz, accz[i]);
+        accz[i] *= al;
 #pragma unroll
-        for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_bf16(ak, bv[j], accS[i][j]);
+        for (int j = 0; j < NCW; ++j) accS[i][j] *= al;
+      }
+    }
+    if constexpr (KCS) {
+      const u32x4 zones = zown ? ones : zero_u4();
+#pragma unroll
+      for (int ks = 0; ks < KJ; ++ks) {
+        u32x4 bv[NCW];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) bv[j] = ld_v_rows<D>(Vc, ks * 32, (sc0 + j) * 16, l16, g);
+#pragma unroll
+        for (int i = 0; i < NAW; ++i) {
+          const u32x4 ak = ld_rows_operand(Kc, LDF, ks * 32, (sa0 + i) * 16, l16, g);
+          accz[i] = mfma_bf16(ak, zones, accz[i]);
+#pragma unroll
+          for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_bf16(ak, bv[j], accS[i][j]);
+        }
+      }
+    } else {
+      // no room for the second copy: the factors e_j = exp(m_j - c) go on the V operand (and on
+      // the ones column of z) instead
+#pragma unroll
+      for (int ks = 0; ks < KJ; ++ks) {
+        const f32x4 m_lo = *reinterpret_cast<const f32x4*>(&mk[ks * 32 + 4 * g]);
+        const f32x4 m_hi = *reinterpret_cast<const f32x4*>(&mk[ks * 32 + 16 + 4 * g]);
+        float e8[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e8[r] = fexp(m_lo[r] - c_cur);
+          e8[4 + r] = fexp(m_hi[r] - c_cur);
+        }
+        u32x4 bz;  // column 0: the factors; other columns zero
+        bz.x = pack_bf16(e8[0], e8[1]);
+        bz.y = pack_bf16(e8[2], e8[3]);
+        bz.z = pack_bf16(e8[4], e8[5]);
+        bz.w = pack_bf16(e8[6], e8[7]);
+        bz = keep_if(bz, zown && l16 == 0);
+        u32x4 bv[NCW];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+          const u32x4 raw = ld_v_rows<D>(Vc, ks * 32, (sc0 + j) * 16, l16, g);
+          bv[j].x = pack_bf16(bf_lo(raw.x) * e8[0], bf_hi(raw.x) * e8[1]);
+          bv[j].y = pack_bf16(bf_lo(raw.y) * e8[2], bf_hi(raw.y) * e8[3]);
+          bv[j].z = pack_bf16(bf_lo(raw.z) * e8[4], bf_hi(raw.z) * e8[5]);
+          bv[j].w = pack_bf16(bf_lo(raw.w) * e8[6], bf_hi(raw.w) * e8[7]);
+        }
+#pragma unroll
+        for (int i = 0; i < NAW; ++i) {
+          const u32x4 ak = ld_rows_operand(Kf, LDF, ks * 32, (sa0 + i) * 16, l16, g);
+          accz[i] = mfma_bf16(ak, bz, accz[i]);
+#pragma unroll
+          for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_bf16(ak, bv[j], accS[i][j]);
+        }
       }
     }
 
@@ -959,11 +1009,14 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
         acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[l16 * LDF + 32 * j + 8 * g]), fq[j], accd);
     }
+    const float pq_l2 = pq * kLog2e;
     {
       const float sc = fexp(c_prev - pq);
+      if (sc != 1.f) {
 #pragma unroll
-      for (int ct = 0; ct < OCT; ++ct) acco[ct] *= sc;
-      accd *= sc;
+        for (int ct = 0; ct < OCT; ++ct) acco[ct] *= sc;
+        accd *= sc;
+      }
     }
 
     // (iii) this chunk: A^T = phi(K_c) f^T masked to key <= query, then V^T A^T and ones A^T
@@ -981,8 +1034,8 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       const f32x4 m1 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 16 + 4 * g]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        a0[r] *= fexp(m0[r] - pq);
-        a1[r] *= fexp(m1[r] - pq);
+        a0[r] *= fexp_shift(m0[r], kLog2e, pq_l2);
+        a1[r] *= fexp_shift(m1[r], kLog2e, pq_l2);
         if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
         if (2 * m + 1 > it || (2 * m + 1 == it && g * 4 + r > l16)) a1[r] = 0.f;
       }
@@ -1046,7 +1099,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
     al = fexp(c_cur - c_next);
     if (NVB == 1) store_v(Vs[0], c0 + C);
-    store_kf();
+    store_kf(c_next);
     pq = chunk_maxima(c_cur);
     write_state();  // the state after this chunk, on scale c_cur
     c_prev = c_cur;
