@@ -33,7 +33,8 @@ __device__ __forceinline__ const float* seg_state_ptr(const CausalArgs& a, int64
 //   Kn[C][D]      phi(K) of the chunk, token-major, row stride D + 16;
 //   Vn[2][C][D]   V of this chunk and of the next one (stored while this one is in use),
 //                 token-major, rows of D elements with the 16-byte pieces of row r permuted;
-//   St[D][D]      the running state transposed, St[c][a] = S[a][c], rounded to bf16;
+//   St[D][D]      the running state transposed, St[c][a] = S[a][c], rounded to bf16, 16-byte
+//                 pieces permuted by the row (pswz);
 //   Zr[16][D]     a normaliser tile: row 0 = bf16(z), row 1 = bf16(z - row 0), rows 2..15 zero;
 //   zf[D]         fp32 z at the segment start.
 // Operands whose reduction index is the token (phi(K)^T and V in the state update, V^T in the
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
 
   __shared__ __attribute__((aligned(16))) uint16_t Kn[C * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Vn[2 * C * D];
-  __shared__ __attribute__((aligned(16))) uint16_t St[D * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t St[D * D];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDK];
   __shared__ float zf[D];
 
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
         u32x2 w2;
         w2.x = pack_bf16(accS[i][j][0], accS[i][j][1]);
         w2.y = pack_bf16(accS[i][j][2], accS[i][j][3]);
-        *reinterpret_cast<u32x2*>(&St[((sc0 + j) * 16 + l16) * LDK + (sa0 + i) * 16 + g * 4]) = w2;
+        *reinterpret_cast<u32x2*>(&St[pswz<D>((sc0 + j) * 16 + l16, (sa0 + i) * 16 + g * 4)]) = w2;
       }
   };
   write_state_bf16();
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
     for (int ks = 0; ks < KA; ++ks) {
 #pragma unroll
       for (int ct = 0; ct < OCT; ++ct)
-        acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDK + ks * 32 + g * 8]), qf[ks], acco[ct]);
+        acco[ct] = mfma_bf16(ld16(&St[pswz<D>((oc0 + ct) * 16 + l16, ks * 32 + g * 8)]), qf[ks], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[l16 * LDK + ks * 32 + g * 8]), qf[ks], accd);
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -189,6 +189,19 @@ constexpr int tsize() { return ROWS * (T + 16) + ROWS; }
 // group of 16 lanes, lane i receives element i % 4 of the four 16-bit values read by lane
 // 4e + i / 4, for e = 0..3.  So when lane j of the group addresses T[R + j / 4][C0 + 4 (j % 4)] of a
 // row-major tile T, lane i receives T[R + e][C0 + i]: four rows of one column.
+// Element (row, col) of an unpadded bf16 tile [.][LEN] whose 16-byte pieces are permuted by the
+// row: piece p of row r sits at p ^ (r & 15) (r & 7 on 128-byte rows).  Measured on gfx950
+// (LDS bank-conflict counters): the 16-row operand read (ds_read_b128, lane = row l16, piece g)
+// is conflict-free, and the MFMA-result write (ds_write_b64, lane = row l16, 8 bytes at column
+// 4 g) is 2-way, against 4-way for the same write on rows padded by 32 bytes (read either way:
+// conflict-free) and 2-way reads with a permutation of 8 rows on rows of 16 or more pieces.
+template <int LEN>
+__device__ __forceinline__ int pswz(int row, int col) {
+  static_assert(LEN % 64 == 0, "rows of at least 8 pieces");
+  constexpr int RM = LEN / 8 >= 16 ? 15 : 7;
+  return row * LEN + ((((col >> 3) ^ (row & RM))) << 3) + (col & 7);
+}
+
 __device__ __forceinline__ u32x2 ld_tr16(const uint16_t* p) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   const v4i16 v =

@@ -363,15 +363,6 @@ __global__ __launch_bounds__(256) void favor_reduce(FavorReduceArgs a) {
 //   f = exp(scale (U - max_f U)) packed to bf16 in the result layout: the B operand of the next
 //       product, k slot e of lane group g = stored feature 32 j + 8 g + e;
 //   out^T = St f (A = 16-byte rows of St), den = Zr f; out = out^T / den.
-// element (row, col) of a [.][LEN] tile, 16-byte pieces permuted by the row: 16-row operand
-// reads (ds_read_b128) are conflict-free when the permutation spans 16 rows on rows of 16 or more
-// pieces (XOR with row & 7 there costs a 2-way conflict on every read, measured on gfx950), and
-// 8 rows on 128-byte rows
-template <int LEN>
-__device__ __forceinline__ int swz(int row, int col) {
-  constexpr int RM = LEN / 8 >= 16 ? 15 : 7;
-  return row * LEN + ((((col >> 3) ^ (row & RM))) << 3) + (col & 7);
-}
 
 template <int D, int M>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void favor_out(FavorOutArgs a) {
@@ -436,19 +427,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
   for (int i = 0; i < SP; ++i) {
     const int e = tid + i * NT;
-    *reinterpret_cast<uint32_t*>(&St[swz<M>(e % D, 2 * (e / D))]) = pack_bf16(sv[i][0], sv[i][1]);
+    *reinterpret_cast<uint32_t*>(&St[pswz<M>(e % D, 2 * (e / D))]) = pack_bf16(sv[i][0], sv[i][1]);
   }
   for (int e = tid; e < 16 * M; e += NT) Zr[e] = 0;
 #pragma unroll
   for (int i = 0; i < WP; ++i) {
     const int e = tid + i * NT;
-    st16(&Ws[swz<D>(e / (D / 8), (e % (D / 8)) * 8)], wv[i]);
+    st16(&Ws[pswz<D>(e / (D / 8), (e % (D / 8)) * 8)], wv[i]);
   }
   __syncthreads();  // Zr cleared before its first two rows are written
   if (tid < M) {
     const __bf16 hi = (__bf16)zq;
-    Zr[swz<M>(0, tid)] = __builtin_bit_cast(uint16_t, hi);
-    Zr[swz<M>(1, tid)] = __builtin_bit_cast(uint16_t, (__bf16)(zq - (float)hi));
+    Zr[pswz<M>(0, tid)] = __builtin_bit_cast(uint16_t, hi);
+    Zr[pswz<M>(1, tid)] = __builtin_bit_cast(uint16_t, (__bf16)(zq - (float)hi));
   }
   __syncthreads();
 
@@ -466,7 +457,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     for (int ft = 0; ft < MT; ++ft) {
       u[ft] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KA; ++ks) u[ft] = mfma_bf16(ld16(&Ws[swz<D>(ft * 16 + l16, ks * 32 + g * 8)]), qb[ks], u[ft]);
+      for (int ks = 0; ks < KA; ++ks) u[ft] = mfma_bf16(ld16(&Ws[pswz<D>(ft * 16 + l16, ks * 32 + g * 8)]), qb[ks], u[ft]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) mq = fmaxf(mq, u[ft][r]);
     }
@@ -488,8 +479,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     for (int j = 0; j < MJ; ++j) {
 #pragma unroll
       for (int ct = 0; ct < DC; ++ct)
-        acco[ct] = mfma_bf16(ld16(&St[swz<M>(ct * 16 + l16, 32 * j + 8 * g)]), fq[j], acco[ct]);
-      accd = mfma_bf16(ld16(&Zr[swz<M>(l16, 32 * j + 8 * g)]), fq[j], accd);
+        acco[ct] = mfma_bf16(ld16(&St[pswz<M>(ct * 16 + l16, 32 * j + 8 * g)]), fq[j], acco[ct]);
+      accd = mfma_bf16(ld16(&Zr[pswz<M>(l16, 32 * j + 8 * g)]), fq[j], accd);
     }
     const float den = from_row0(accd[0] + accd[1]);
     const float inv = 1.0f / den;
@@ -652,8 +643,9 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 // query features), so the products are unchanged; the state is converted back to feature order
 // where it crosses the kernel's boundary.
 //
-// LDS (bf16 unless noted): Kf[C][M+16] phi(K_c) token-major; Vs[2][C][D] V of this chunk and the
-// next; St[D][M+16] the state transposed, St[c][q] = S[q][c]; Zr[16][M+16] rows bf16(z) and
+// LDS (bf16 unless noted): Kf[C][M+16] phi(K_c) token-major (rows of M with pieces permuted by
+// pswz where Kc exists); Vs[2][C][D] V of this chunk and the next; St[D][M] the state
+// transposed, St[c][q] = S[q][c], pieces permuted by pswz; Zr[16][M+16] rows bf16(z) and
 // bf16(z - bf16(z)); Ws[M][D+16] the projection.  Work per wave: one query tile, shared by
 // waves w and 7 - w when C = 64 (they split the value columns), or its own when C = 128 (tiles
 // w and 11 - w for the two waves of a SIMD, which balances the causal triangle); the same token
@@ -689,8 +681,11 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t Kf[C * LDF];
   __shared__ __attribute__((aligned(16))) uint16_t Kc[KCS ? C * LDF : 8];  // phi(K_c), state's scale
+  // Kf permuted (pswz) where only 16-row operand reads see it; with no Kc it is also the
+  // transposed operand of the state update (ld_rows_operand), which wants the padded rows
+  auto kfo = [](int t, int c) { return KCS ? pswz<M>(t, c) : t * LDF + c; };
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NVB][C * D];
-  __shared__ __attribute__((aligned(16))) uint16_t St[D * LDF];
+  __shared__ __attribute__((aligned(16))) uint16_t St[D * M];
   __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDF];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[M * LDW];
   __shared__ float wmax[8];
@@ -763,7 +758,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
         u32x2 w2;
         w2.x = pack_bf16(accS[i][j][0], accS[i][j][1]);
         w2.y = pack_bf16(accS[i][j][2], accS[i][j][3]);
-        *reinterpret_cast<u32x2*>(&St[((sc0 + j) * 16 + l16) * LDF + (sa0 + i) * 16 + g * 4]) = w2;
+        *reinterpret_cast<u32x2*>(&St[pswz<M>((sc0 + j) * 16 + l16, (sa0 + i) * 16 + g * 4)]) = w2;
       }
     if (zown && l16 == 0) {
 #pragma unroll
@@ -853,13 +848,13 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       u32x2 w2;
       w2.x = pack_bf16(w[0], w[1]);
       w2.y = pack_bf16(w[2], w[3]);
-      const int o = t * LDF + 32 * (f >> 1) + 8 * g + 4 * (f & 1);
-      *reinterpret_cast<u32x2*>(&Kf[o]) = w2;
+      const int col = 32 * (f >> 1) + 8 * g + 4 * (f & 1);
+      *reinterpret_cast<u32x2*>(&Kf[kfo(t, col)]) = w2;
       if constexpr (KCS) {
         u32x2 c2;
         c2.x = pack_bf16(w[0] * et, w[1] * et);
         c2.y = pack_bf16(w[2] * et, w[3] * et);
-        *reinterpret_cast<u32x2*>(&Kc[o]) = c2;
+        *reinterpret_cast<u32x2*>(&Kc[t * LDF + col]) = c2;
       }
     }
   };
@@ -1006,7 +1001,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     for (int j = 0; j < MJ; ++j) {
 #pragma unroll
       for (int ct = 0; ct < OCT; ++ct)
-        acco[ct] = mfma_bf16(ld16(&St[((oc0 + ct) * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], acco[ct]);
+        acco[ct] = mfma_bf16(ld16(&St[pswz<M>((oc0 + ct) * 16 + l16, 32 * j + 8 * g)]), fq[j], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[l16 * LDF + 32 * j + 8 * g]), fq[j], accd);
     }
     const float pq_l2 = pq * kLog2e;
@@ -1025,8 +1020,8 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       a1 = zero4();
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
-        a0 = mfma_bf16(ld16(&Kf[(2 * m * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], a0);
-        a1 = mfma_bf16(ld16(&Kf[((2 * m + 1) * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], a1);
+        a0 = mfma_bf16(ld16(&Kf[kfo(2 * m * 16 + l16, 32 * j + 8 * g)]), fq[j], a0);
+        a1 = mfma_bf16(ld16(&Kf[kfo((2 * m + 1) * 16 + l16, 32 * j + 8 * g)]), fq[j], a1);
       }
     };
     auto pack_a = [&](int m, f32x4 a0, f32x4 a1) {

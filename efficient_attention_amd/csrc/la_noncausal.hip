@@ -517,13 +517,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + sp.row0 * D;
   uint16_t* Ts = stage + wave * ST;  // this wave's staging tile: phi(Q) in, then the outputs
 
-  // Staging tile layout: row r, 16-byte block b at r * D + 8 (b ^ f(r % 16)).  The XOR makes
-  // three patterns conflict-free on the 64 banks: whole rows (the HBM side), 16 rows of one
-  // block (operand reads) and 16 rows x 8 bytes (accumulator writes).
-  auto sofs = [](int r, int b) {
-    const int r16 = r & 15;
-    return r * D + ((b ^ (D == 64 ? ((r16 & 7) ^ (r16 >> 3)) : r16)) << 3);
-  };
+  // Staging tile layout: row r, 16-byte block b at r * D + 8 (b ^ (r & 7)) (D = 64, 8 blocks
+  // per row) or 8 (b ^ (r & 15)) (D = 128).  Measured with the LDS bank-conflict counters on
+  // gfx950: whole-row accesses (the HBM side) and the 16-row operand reads are conflict-free,
+  // the accumulator writes (16 rows x 8 bytes) 2-way, which no permutation tried avoids.
+  auto sofs = [](int r, int b) { return r * D + ((b ^ (r & (D == 64 ? 7 : 15))) << 3); };
 
   // Queries go in batches: in batch b the four waves take consecutive runs of QB queries.  For
   // D = 128 a batch holds two 16-query blocks, which share every KV^T operand read from LDS:
