@@ -524,7 +524,7 @@ def main():
                     help="measure the attainable-bandwidth ceilings (copy, read, causal pattern) instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

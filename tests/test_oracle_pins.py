@@ -342,3 +342,57 @@ def test_state_matmul_equals_loop():
     S2, z2 = oracle.state_from_tokens_matmul(k, v)
     np.testing.assert_allclose(S2, S1, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(z2, z1, rtol=1e-13)
+
+
+def _classes(x):
+    """0 finite, 1 +inf, 2 -inf, 3 NaN."""
+    c = np.zeros(x.shape, dtype=np.int8)
+    c[np.isposinf(x)] = 1
+    c[np.isneginf(x)] = 2
+    c[np.isnan(x)] = 3
+    return c
+
+
+def test_nonfinite_inputs_follow_the_formula():
+    """IEEE behaviour of eq. Attention_i ("Linear attention: reordering the matmuls") on NaN and
+    +-inf entries, derived by hand: phi(-inf) = e^-inf = 0 drops a feature; phi(+inf) = +inf and
+    phi(NaN) = NaN; a query whose features are all -inf has phi(q) = 0, hence 0/0.  The three
+    forms (non-causal, causal recurrence, decode) must give exactly these classes."""
+    n, d = 6, 4
+    rng = np.random.default_rng(77)
+    q, k, v = (rng.standard_normal((1, 1, n, d)) * 0.5 for _ in range(3))
+    q[0, 0, 1, :] = -np.inf      # query 1: phi(q) = 0 -> 0/0 in every column
+    q[0, 0, 2, 0] = -np.inf      # query 2: one feature drops out, row stays finite
+    k[0, 0, 3, 2] = np.nan       # key 3: NaN reaches every query that sees it
+    v[0, 0, 4, 1] = np.inf       # value (4, 1): +inf in column 1 of every query that sees key 4
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        nc = oracle.noncausal_linear(q, k, v)
+        ca = oracle.causal_recurrent(q, k, v)
+        S, z = np.zeros((1, 1, d, d)), np.zeros((1, 1, d))
+        dec = []
+        for t in range(n):
+            o, S, z = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], S, z)
+            dec.append(o)
+        dec = np.stack(dec, axis=2)
+    # non-causal: every query sees key 3 (NaN) -> every element NaN
+    assert (_classes(nc) == 3).all()
+    # causal: rows 0 and 2 see keys 0..i < 3 -> finite; row 1 is 0/0; rows 3.. see key 3 -> NaN
+    exp = np.zeros((n, d), dtype=np.int8)
+    exp[1, :] = 3
+    exp[3:, :] = 3
+    assert np.array_equal(_classes(ca)[0, 0], exp)
+    assert np.array_equal(_classes(dec)[0, 0], exp)
+    # the finite causal rows equal the same rows without the non-finite entries further on
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    k2[0, 0, 3, 2] = 0.0
+    v2[0, 0, 4, 1] = 0.0
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ca2 = oracle.causal_recurrent(q2, k2, v2)
+    assert np.array_equal(ca[0, 0, [0, 2]], ca2[0, 0, [0, 2]])
+    # +inf in a value without the NaN key: column 1 of rows >= 4 is +inf (positive weights), the
+    # other columns stay finite
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        ca3 = oracle.causal_recurrent(q, k2, v)
+    c3 = _classes(ca3)[0, 0]
+    assert (c3[4:, 1] == 1).all() and (c3[4:, [0, 2, 3]] == 0).all() and (c3[[0, 2, 3], :] == 0).all()
+    assert (c3[1, :] == 3).all()
