@@ -487,12 +487,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
   }
   if (tid < D) zf[tid] = zinit;
 
-  // The key sums z run on the MFMA pipe beside the state update, phi(K)^T times a column of ones
-  // (result column 0: lanes l16 == 0, rows 4g + r of the feature tile), each wave for feature
-  // tiles wave + 4i; they are written to zf after each chunk for the next chunk's normalisers.
+  // The key sums z are added on the vector ALU beside the state update (whose MFMA pipe is the
+  // busy one), each wave for feature tiles wave + 4i: lane (l16, g) sums the keys 4 ks + g of
+  // feature 16 (wave + 4i) + l16 over the chunk, the four lane groups are summed once, and zf
+  // takes the chunk's sums for the next chunk's normalisers.
   constexpr int NZW = NA / 4;
-  const float one_col = l16 == 0 ? 1.f : 0.f;
-  f32x4 accz[NZW];
 
   // S^T of the initial state for the first chunk's inter-chunk product
   auto write_st = [&]() {
@@ -504,10 +503,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
   };
   write_st();
   __syncthreads();  // zf holds the initial key sums
-#pragma unroll
-  for (int i = 0; i < NZW; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) accz[i][r] = l16 == 0 ? zf[(wave + 4 * i) * 16 + g * 4 + r] : 0.f;
 
   // K and V pieces: piece tid + 256 p of a chunk is row (tid / PPR) + (256 / PPR) p, columns
   // 4 (tid % PPR) .. + 3.  Rows past the segment end read row t1 - 1 and are zeroed in LDS.
@@ -563,7 +558,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
                  qf[m].z * zf[m * 16 + g * 4 + 2] + qf[m].w * zf[m * 16 + g * 4 + 3];
       }
       f32x4 acco[NC];
-      f32x4 accd = zero4();
 #pragma unroll
       for (int c = 0; c < NC; ++c) acco[c] = zero4();
       // inter-chunk: S^T phi(Q)^T
@@ -578,7 +572,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
           acco[c] = mfma_f32(sv.w, qf[m].w, acco[c]);
         }
       // intra-chunk, one key tile at a time: A^T = phi(K_jt) phi(Q_it)^T (masked on the
-      // diagonal tile), then V^T A^T and the key sums 1^T A^T
+      // diagonal tile), then V^T A^T; the key sums 1^T A^T go into this lane's part of the
+      // denominator (its rows 4g..4g+3 of the tile), summed over the lane groups once per row
       for (int jt = 0; jt <= it; ++jt) {
         f32x4 accA = zero4();
 #pragma unroll
@@ -594,15 +589,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
           for (int r = 0; r < 4; ++r)
             if (g * 4 + r > l16) accA[r] = 0.f;
         }
+        dpart += (accA[0] + accA[1]) + (accA[2] + accA[3]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = jt * 16 + g * 4 + r;
 #pragma unroll
           for (int c = 0; c < NC; ++c) acco[c] = mfma_f32(Vn[j * LD + c * 16 + l16], accA[r], acco[c]);
-          accd = mfma_f32(l16 == 0 ? 1.f : 0.f, accA[r], accd);
         }
       }
-      const float den = sum_over_groups(dpart) + __shfl(accd[0], l16);
+      const float den = sum_over_groups(dpart);
       const int64_t row = c0 + it * 16 + l16;
       if (row < t1) {
         // one IEEE division per row, then products (within 1.5 ulp of a division per element);
@@ -620,6 +615,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
     __syncthreads();  // S^T, z and the tiles are no longer read for outputs
 
     // state update: S[:, own cols] += phi(K)^T V, z[own feature tiles] += phi(K)^T 1
+    float zs[NZW];
+#pragma unroll
+    for (int i = 0; i < NZW; ++i) zs[i] = 0.f;
     for (int ks = 0; ks < C / 4; ++ks) {
 #pragma unroll
       for (int at = 0; at < NA; ++at) {
@@ -629,14 +627,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
           accS[at][p] = mfma_f32(ak, Vn[(ks * 4 + g) * LD + (wave + 4 * p) * 16 + l16], accS[at][p]);
       }
 #pragma unroll
-      for (int i = 0; i < NZW; ++i)
-        accz[i] = mfma_f32(Kn[(ks * 4 + g) * LD + (wave + 4 * i) * 16 + l16], one_col, accz[i]);
+      for (int i = 0; i < NZW; ++i) zs[i] += Kn[(ks * 4 + g) * LD + (wave + 4 * i) * 16 + l16];
     }
-    if (l16 == 0) {
 #pragma unroll
-      for (int i = 0; i < NZW; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) zf[(wave + 4 * i) * 16 + g * 4 + r] = accz[i][r];
+    for (int i = 0; i < NZW; ++i) {
+      const float zc = sum_over_groups(zs[i]);
+      if (g == 0) zf[(wave + 4 * i) * 16 + l16] += zc;
     }
     write_st();
     __syncthreads();  // before the next chunk overwrites the tiles
