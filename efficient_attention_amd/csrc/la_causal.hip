@@ -405,6 +405,10 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
   }
 }
 
+// waves per workgroup of the fp32 kernel: eight at d = 128, whose LDS admits one workgroup per
+// compute unit (four waves would leave one wave per SIMD), four otherwise
+constexpr int f32_waves(int d) { return d == 128 ? 8 : 4; }
+
 // fp32 kernel (no bf16 rounding anywhere).  The fp32 MFMA takes one k value per lane; a lane
 // holds 16-byte pieces of rows, features 16m + 4g .. 16m + 4g + 3, and k-step (m, e) pairs
 // feature 16m + 4g + e on both operands.  Each wave owns query tiles (tiles w and NI - 1 - w when
@@ -415,18 +419,22 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
 // w, w + 4, ...) and written to S^T after each chunk's update.  The next chunk's K and V rows
 // are loaded into registers while the current chunk is computed.
 template <int D, int C, class TB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 4096 ? 3 : 1))) void causal_f32(
+__global__ __launch_bounds__(64 * f32_waves(D)) __attribute__((amdgpu_waves_per_eu(D * C <= 4096 ? 3 : (f32_waves(D) == 8 ? 2 : 1)))) void causal_f32(
     CausalArgs a, TB tb) {  // three workgroups per CU where the LDS allows (d = 64, 64-token chunks)
+  constexpr int NW = f32_waves(D);   // waves: 8 at d = 128 (one workgroup per CU fits the LDS)
+  constexpr int NT = 64 * NW;
   constexpr int LD = D + 4;
   constexpr int NI = C / 16;         // token tiles per chunk
-  constexpr int NCW = D / 64;        // state column tiles per wave
   constexpr int NA = D / 16;         // feature tiles
   constexpr int NC = D / 16;         // output column tiles
+  constexpr int NCW = NC / NW;       // state column tiles per wave
   constexpr int KM = D / 16;         // 16-feature groups of a reduction over features
-  constexpr int TPW = NI / 4;        // query tiles per wave
+  constexpr int SH = NI >= NW ? 1 : NW / NI;  // waves sharing a query tile (splitting its columns)
+  constexpr int TPW = NI >= NW ? NI / NW : 1; // query tiles per wave
+  constexpr int NCO = NC / SH;       // output column tiles per wave
   constexpr int PPR = D / 4;         // 16-byte pieces per row
-  constexpr int NP = C * PPR / 256;  // K (and V) pieces per thread
-  static_assert(NI == 8 || NI == 4, "chunk");
+  constexpr int NP = C * PPR / NT;   // K (and V) pieces per thread
+  static_assert((NI == 8 || NI == 4) && NCW >= 1 && SH <= 2 && NP >= 1, "chunk");
   __shared__ __attribute__((aligned(16))) float Kn[C * LD];
   __shared__ __attribute__((aligned(16))) float Vn[C * LD];
   __shared__ __attribute__((aligned(16))) float St[D * LD];  // S^T of the state before the chunk
@@ -458,7 +466,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
 #pragma unroll
       for (int p = 0; p < NCW; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accS[at][p][r] = s0[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
+        for (int r = 0; r < 4; ++r) accS[at][p][r] = s0[(at * 16 + g * 4 + r) * D + (wave + NW * p) * 16 + l16];
     if (tid < D) zinit = a.z0[bh * D + tid];
   }
   for (int64_t s = 0; s < seg; ++s) {      // same grouping as in the bf16 kernel
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
         for (int p = 0; p < NCW; ++p)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            part[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16];
+            part[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + NW * p) * 16 + l16];
       if (tid < D) zpart += st[D * D + tid];
     }
 #pragma unroll
@@ -488,10 +496,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
   if (tid < D) zf[tid] = zinit;
 
   // The key sums z are added on the vector ALU beside the state update (whose MFMA pipe is the
-  // busy one), each wave for feature tiles wave + 4i: lane (l16, g) sums the keys 4 ks + g of
-  // feature 16 (wave + 4i) + l16 over the chunk, the four lane groups are summed once, and zf
+  // busy one), each wave for feature tiles wave + NW i: lane (l16, g) sums the keys 4 ks + g of
+  // feature 16 (wave + NW i) + l16 over the chunk, the four lane groups are summed once, and zf
   // takes the chunk's sums for the next chunk's normalisers.
-  constexpr int NZW = NA / 4;
+  constexpr int NZW = NA / NW;
 
   // S^T of the initial state for the first chunk's inter-chunk product
   auto write_st = [&]() {
@@ -499,14 +507,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
     for (int at = 0; at < NA; ++at)
 #pragma unroll
       for (int p = 0; p < NCW; ++p)
-        *reinterpret_cast<f32x4*>(&St[((wave + 4 * p) * 16 + l16) * LD + at * 16 + g * 4]) = accS[at][p];
+        *reinterpret_cast<f32x4*>(&St[((wave + NW * p) * 16 + l16) * LD + at * 16 + g * 4]) = accS[at][p];
   };
   write_st();
   __syncthreads();  // zf holds the initial key sums
 
-  // K and V pieces: piece tid + 256 p of a chunk is row (tid / PPR) + (256 / PPR) p, columns
+  // K and V pieces: piece tid + NT p of a chunk is row (tid / PPR) + (NT / PPR) p, columns
   // 4 (tid % PPR) .. + 3.  Rows past the segment end read row t1 - 1 and are zeroed in LDS.
-  auto prow = [&](int p) { return tid / PPR + p * (256 / PPR); };
+  auto prow = [&](int p) { return tid / PPR + p * (NT / PPR); };
+  // the query tile of this wave's tp-th share, and the first of its output column tiles: with
+  // four waves, tiles w and NI - 1 - w (NI = 8) or w (NI = 4), all columns; with eight waves
+  // and four tiles, tile w shared by waves w and 7 - w, which take half the columns each (a SIMD
+  // holds waves s and s + 4, so tiles s and 3 - s: the causal triangle is balanced per SIMD)
+  auto tile_of = [&](int tp) { return SH == 1 ? (tp == 0 ? wave : NI - 1 - wave) : (wave < 4 ? wave : 7 - wave); };
+  const int cb = SH == 1 ? 0 : (wave < 4 ? 0 : NCO);
   const int pcol = (tid % PPR) * 4;
   f32x4 kq[NP], vq[NP];
   auto load_kv = [&](int64_t c0) {
@@ -523,7 +537,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
     f32x4 qv[TPW][KM];
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp) {
-      const int it = tp == 0 ? wave : NI - 1 - wave;
+      const int it = tile_of(tp);
       const int64_t row = c0 + it * 16 + l16;
       const int64_t r = row < t1 ? row : t1 - 1;
 #pragma unroll
@@ -545,7 +559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
 
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp) {
-      const int it = tp == 0 ? wave : NI - 1 - wave;
+      const int it = tile_of(tp);
       f32x4 qf[KM];
       float dpart = 0.f;  // phi(q) . z over this lane's features
 #pragma unroll
@@ -557,15 +571,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
         dpart += qf[m].x * zf[m * 16 + g * 4] + qf[m].y * zf[m * 16 + g * 4 + 1] +
                  qf[m].z * zf[m * 16 + g * 4 + 2] + qf[m].w * zf[m * 16 + g * 4 + 3];
       }
-      f32x4 acco[NC];
+      f32x4 acco[NCO];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acco[c] = zero4();
-      // inter-chunk: S^T phi(Q)^T
+      for (int c = 0; c < NCO; ++c) acco[c] = zero4();
+      // inter-chunk: S^T phi(Q)^T (this wave's output columns)
 #pragma unroll
       for (int m = 0; m < KM; ++m)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(&St[(c * 16 + l16) * LD + m * 16 + g * 4]);
+        for (int c = 0; c < NCO; ++c) {
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(&St[((cb + c) * 16 + l16) * LD + m * 16 + g * 4]);
           acco[c] = mfma_f32(sv.x, qf[m].x, acco[c]);
           acco[c] = mfma_f32(sv.y, qf[m].y, acco[c]);
           acco[c] = mfma_f32(sv.z, qf[m].z, acco[c]);
@@ -594,7 +608,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
         for (int r = 0; r < 4; ++r) {
           const int j = jt * 16 + g * 4 + r;
 #pragma unroll
-          for (int c = 0; c < NC; ++c) acco[c] = mfma_f32(Vn[j * LD + c * 16 + l16], accA[r], acco[c]);
+          for (int c = 0; c < NCO; ++c) acco[c] = mfma_f32(Vn[j * LD + (cb + c) * 16 + l16], accA[r], acco[c]);
         }
       }
       const float den = sum_over_groups(dpart);
@@ -605,10 +619,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
         const float inv = 1.0f / den;
         const bool tiny = !(den >= 0x1p-120f);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+        for (int c = 0; c < NCO; ++c) {
           f32x4 o = {acco[c][0] * inv, acco[c][1] * inv, acco[c][2] * inv, acco[c][3] * inv};
           if (tiny) o = f32x4{acco[c][0] / den, acco[c][1] / den, acco[c][2] / den, acco[c][3] / den};
-          *reinterpret_cast<f32x4*>(O + row * D + c * 16 + g * 4) = o;
+          *reinterpret_cast<f32x4*>(O + row * D + (cb + c) * 16 + g * 4) = o;
         }
       }
     }
@@ -624,15 +638,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
         const float ak = Kn[(ks * 4 + g) * LD + at * 16 + l16];
 #pragma unroll
         for (int p = 0; p < NCW; ++p)
-          accS[at][p] = mfma_f32(ak, Vn[(ks * 4 + g) * LD + (wave + 4 * p) * 16 + l16], accS[at][p]);
+          accS[at][p] = mfma_f32(ak, Vn[(ks * 4 + g) * LD + (wave + NW * p) * 16 + l16], accS[at][p]);
       }
 #pragma unroll
-      for (int i = 0; i < NZW; ++i) zs[i] += Kn[(ks * 4 + g) * LD + (wave + 4 * i) * 16 + l16];
+      for (int i = 0; i < NZW; ++i) zs[i] += Kn[(ks * 4 + g) * LD + (wave + NW * i) * 16 + l16];
     }
 #pragma unroll
     for (int i = 0; i < NZW; ++i) {
       const float zc = sum_over_groups(zs[i]);
-      if (g == 0) zf[(wave + 4 * i) * 16 + l16] += zc;
+      if (g == 0) zf[(wave + NW * i) * 16 + l16] += zc;
     }
     write_st();
     __syncthreads();  // before the next chunk overwrites the tiles
@@ -646,7 +660,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D * C <= 40
 #pragma unroll
       for (int p = 0; p < NCW; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sn[(at * 16 + g * 4 + r) * D + (wave + 4 * p) * 16 + l16] = accS[at][p][r];
+        for (int r = 0; r < 4; ++r) sn[(at * 16 + g * 4 + r) * D + (wave + NW * p) * 16 + l16] = accS[at][p][r];
     if (tid < D) a.zn[bh * D + tid] = zf[tid];
   }
 }
@@ -684,7 +698,7 @@ static hipError_t launch_causal_tb(const CausalArgs& a, int dtype, hipStream_t s
     hipLaunchKernelGGL((causal_bf16<D, C, TB>), dim3(blocks), dim3(512), 0, s, a, tb);
   } else {
     if constexpr (D * C <= 8192)
-      hipLaunchKernelGGL((causal_f32<D, C, TB>), dim3(blocks), dim3(256), 0, s, a, tb);
+      hipLaunchKernelGGL((causal_f32<D, C, TB>), dim3(blocks), dim3(64 * f32_waves(D)), 0, s, a, tb);
     else
       return hipErrorInvalidValue;
   }
