@@ -411,13 +411,15 @@ constexpr int f32_waves(int d) { return d == 128 ? 8 : 4; }
 
 // fp32 kernel (no bf16 rounding anywhere).  The fp32 MFMA takes one k value per lane; a lane
 // holds 16-byte pieces of rows, features 16m + 4g .. 16m + 4g + 3, and k-step (m, e) pairs
-// feature 16m + 4g + e on both operands.  Each wave owns query tiles (tiles w and NI - 1 - w when
-// a chunk has 8, tile w when it has 4) and produces all output columns of them: the masked tile
-// A^T = phi(K) phi(Q)^T of each (key tile, query tile) pair is computed once, by its owner, and
-// fed back as an operand with permuted k, as in the bf16 kernel.  The inter-chunk product reads
-// S^T from LDS; the state accumulators are split by value columns (wave w owns column tiles
-// w, w + 4, ...) and written to S^T after each chunk's update.  The next chunk's K and V rows
-// are loaded into registers while the current chunk is computed.
+// feature 16m + 4g + e on both operands.  With four waves, each wave owns query tiles (tiles w
+// and NI - 1 - w when a chunk has 8, tile w when it has 4) and produces all output columns of
+// them: the masked tile A^T = phi(K) phi(Q)^T of each (key tile, query tile) pair is computed
+// once, by its owner, and fed back as an operand with permuted k, as in the bf16 kernel.  With
+// eight waves (d = 128) waves w and 7 - w share tile w and produce half the columns each, both
+// computing its masked tiles.  The inter-chunk product reads S^T from LDS; the state
+// accumulators are split by value columns (wave w owns column tiles w, w + NW, ...) and written
+// to S^T after each chunk's update.  The next chunk's K and V rows are loaded into registers
+// while the current chunk is computed.
 template <int D, int C, class TB>
 __global__ __launch_bounds__(64 * f32_waves(D)) __attribute__((amdgpu_waves_per_eu(D * C <= 4096 ? 3 : (f32_waves(D) == 8 ? 2 : 1)))) void causal_f32(
     CausalArgs a, TB tb) {  // three workgroups per CU where the LDS allows (d = 64, 64-token chunks)

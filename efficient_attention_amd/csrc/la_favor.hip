@@ -633,7 +633,9 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 // chunk's keys j <= i), the largest exponent among the keys it attends to: every weight is then
 // at most 1 and the largest one is not below fp32's range, however far apart the exponents of
 // different tokens are.  So A_ij enters as (f(q_i) . phi~(k_j)) exp(m_j - P_i), the carried state
-// as exp(c_prev - P_i) S, and the state update as phi~(K)^T (exp(m_j - c) V).
+// as exp(c_prev - P_i) S, and the state update as (exp(m_j - c) phi~(K))^T V: a second copy of the
+// chunk's key features, Kc, is written already on the state's scale (where LDS has room for it;
+// otherwise the factors go on the V operand).
 //
 // Feature order.  Features are stored in "operand order": stored feature q = 32 j + 8 g + 4 h + r
 // is feature p = 32 j + 16 h + 4 g + r.  An MFMA result lane (g, r) of feature tiles 2j and
@@ -644,7 +646,8 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 // where it crosses the kernel's boundary.
 //
 // LDS (bf16 unless noted): Kf[C][M+16] phi(K_c) token-major (rows of M with pieces permuted by
-// pswz where Kc exists); Vs[2][C][D] V of this chunk and the next; St[D][M] the state
+// pswz where Kc exists); Kc[C][M+16] the same features on the state's scale (read by transpose
+// reads, so padded); Vs[2][C][D] V of this chunk and the next; St[D][M] the state
 // transposed, St[c][q] = S[q][c], pieces permuted by pswz; Zr[16][M+16] rows bf16(z) and
 // bf16(z - bf16(z)); Ws[M][D+16] the projection.  Work per wave: one query tile, shared by
 // waves w and 7 - w when C = 64 (they split the value columns), or its own when C = 128 (tiles
@@ -656,7 +659,7 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 template <int D, int M, int C>
 __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   constexpr int NT = 512;
-  constexpr int LDF = M + 16;      // 8 (mod 64) dwords
+  constexpr int LDF = M + 16;      // padded rows: conflict-free 16-row operand and transpose reads
   constexpr int LDW = D + 16;
   constexpr int KA = D / 32;
   constexpr int MT = M / 16;       // feature tiles
