@@ -39,6 +39,13 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+// the largest spread (natural-log units) between a chunk's key maxima and its state's scale for
+// which the causal kernel evaluates the whole chunk on the state's scale
+constexpr float kSameScale = 40.f;
 // exp(a (u - m)) as one FMA and the base-2 exponential: al2 = a log2(e), ml2 = m a log2(e)
 __device__ __forceinline__ float fexp_shift(float u, float al2, float ml2) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(u, al2, -ml2));
@@ -681,6 +688,9 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   constexpr int kLdsBase = 2 * (C * LDF + NVB * C * D + D * LDF + 16 * LDF + M * LDW) +
                            4 * (8 + NQW * C + C);
   constexpr bool KCS = kLdsBase + 2 * C * LDF <= 160 * 1024;
+  // chunks evaluated on the state's scale where the copy exists (64-token chunks: with 128 the
+  // second path does not fit the registers)
+  constexpr bool SAME = KCS && C == 64;
 
   __shared__ __attribute__((aligned(16))) uint16_t Kf[C * LDF];
   __shared__ __attribute__((aligned(16))) uint16_t Kc[KCS ? C * LDF : 8];  // phi(K_c), state's scale
@@ -1007,9 +1017,17 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
         acco[ct] = mfma_bf16(ld16(&St[pswz<M>((oc0 + ct) * 16 + l16, 32 * j + 8 * g)]), fq[j], acco[ct]);
       accd = mfma_bf16(ld16(&Zr[l16 * LDF + 32 * j + 8 * g]), fq[j], accd);
     }
-    const float pq_l2 = pq * kLog2e;
+    // A chunk whose key maxima lie within kSameScale of its state's scale evaluates every query
+    // on that scale c_cur instead of its own P_i (every weight still at most 1, the smallest
+    // shrunk by at most e^-kSameScale, far inside the bf16 / fp32 range): the key features
+    // already written on c_cur (Kc) are then the masked product's operand as they are, and the
+    // carried state takes one factor for all queries.  Other chunks use P_i.
+    const bool same = SAME && __builtin_amdgcn_readfirstlane(
+                                  (int)(c_cur - fmaxf(c_prev, mk[0]) <= kSameScale));
+    const float pe = same ? c_cur : pq;  // the scale of this lane's query in this chunk
+    const float pq_l2 = pe * kLog2e;
     {
-      const float sc = fexp(c_prev - pq);
+      const float sc = fexp(c_prev - pe);
       if (sc != 1.f) {
 #pragma unroll
         for (int ct = 0; ct < OCT; ++ct) acco[ct] *= sc;
@@ -1018,22 +1036,32 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     }
 
     // (iii) this chunk: A^T = phi(K_c) f^T masked to key <= query, then V^T A^T and ones A^T
-    auto a_tiles = [&](int m, f32x4& a0, f32x4& a1) {
+    auto a_tiles = [&](int m, f32x4& a0, f32x4& a1, auto samec) {
       a0 = zero4();
       a1 = zero4();
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
-        a0 = mfma_bf16(ld16(&Kf[kfo(2 * m * 16 + l16, 32 * j + 8 * g)]), fq[j], a0);
-        a1 = mfma_bf16(ld16(&Kf[kfo((2 * m + 1) * 16 + l16, 32 * j + 8 * g)]), fq[j], a1);
+        if constexpr (decltype(samec)::value) {
+          a0 = mfma_bf16(ld16(&Kc[(2 * m * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], a0);
+          a1 = mfma_bf16(ld16(&Kc[((2 * m + 1) * 16 + l16) * LDF + 32 * j + 8 * g]), fq[j], a1);
+        } else {
+          a0 = mfma_bf16(ld16(&Kf[kfo(2 * m * 16 + l16, 32 * j + 8 * g)]), fq[j], a0);
+          a1 = mfma_bf16(ld16(&Kf[kfo((2 * m + 1) * 16 + l16, 32 * j + 8 * g)]), fq[j], a1);
+        }
       }
     };
-    auto pack_a = [&](int m, f32x4 a0, f32x4 a1) {
-      const f32x4 m0 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 4 * g]);
-      const f32x4 m1 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 16 + 4 * g]);
+    auto pack_a = [&](int m, f32x4 a0, f32x4 a1, auto samec) {
+      if constexpr (!decltype(samec)::value) {
+        const f32x4 m0 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 4 * g]);
+        const f32x4 m1 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 16 + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          a0[r] *= fexp_shift(m0[r], kLog2e, pq_l2);
+          a1[r] *= fexp_shift(m1[r], kLog2e, pq_l2);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        a0[r] *= fexp_shift(m0[r], kLog2e, pq_l2);
-        a1[r] *= fexp_shift(m1[r], kLog2e, pq_l2);
         if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
         if (2 * m + 1 > it || (2 * m + 1 == it && g * 4 + r > l16)) a1[r] = 0.f;
       }
@@ -1049,21 +1077,29 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
       for (int ct = 0; ct < OCT; ++ct) acco[ct] = mfma_bf16(ld_v_rows<D>(Vc, m * 32, (oc0 + ct) * 16, l16, g), af, acco[ct]);
       accd = mfma_bf16(ones, af, accd);
     };
-    {
-      // step m covers key tiles 2m and 2m + 1; the A products of step m + 1 are issued before
-      // the V products of step m so that the two overlap
+    // step m covers key tiles 2m and 2m + 1; the A products of step m + 1 are issued before the
+    // V products of step m so that the two overlap
+    auto intra = [&](auto samec) {
       const int mlast = it >> 1;
       f32x4 a0, a1;
-      a_tiles(0, a0, a1);
+      a_tiles(0, a0, a1, samec);
 #pragma unroll
       for (int m = 0; m < NI / 2 - 1; ++m) {
         if (m < mlast) {
-          const u32x4 af = pack_a(m, a0, a1);
-          a_tiles(m + 1, a0, a1);
+          const u32x4 af = pack_a(m, a0, a1, samec);
+          a_tiles(m + 1, a0, a1, samec);
           av_step(m, af);
         }
       }
-      av_step(mlast, pack_a(mlast, a0, a1));
+      av_step(mlast, pack_a(mlast, a0, a1, samec));
+    };
+    if constexpr (SAME) {
+      if (same)
+        intra(BoolC<true>{});
+      else
+        intra(BoolC<false>{});
+    } else {
+      intra(BoolC<false>{});
     }
 
     const float den = from_row0(accd[0] + accd[1]);
