@@ -847,8 +847,24 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   // exp(u - m_j) exp(m_j - c), so that the state update takes V as it is; a token past the end
   // (all exponents -inf) gets zero features in both
   auto token_max = [&](int t) { return NQW == 2 ? fmaxf(tm[0][t], tm[NQW - 1][t]) : tm[0][t]; };
-  auto store_kf = [&](float c_state) {
+  // A chunk evaluated on its state's scale (same_scale) reads only Kc: Kf is not written, and
+  // Kc is exp(u - c) directly.
+  auto store_kf = [&](float c_state, bool same_scale) {
     const int t = it * 16 + l16;
+    if constexpr (SAME) {
+      if (same_scale) {
+        const float c_l2 = c_state * kLog2e;
+#pragma unroll
+        for (int ft = 0; ft < HF; ++ft) {
+          const int f = hf0 + ft;
+          u32x2 c2;
+          c2.x = pack_bf16(fexp_shift(uk[ft][0], kLog2e, c_l2), fexp_shift(uk[ft][1], kLog2e, c_l2));
+          c2.y = pack_bf16(fexp_shift(uk[ft][2], kLog2e, c_l2), fexp_shift(uk[ft][3], kLog2e, c_l2));
+          *reinterpret_cast<u32x2*>(&Kc[t * LDF + 32 * (f >> 1) + 8 * g + 4 * (f & 1)]) = c2;
+        }
+        return;
+      }
+    }
     const float mt = token_max(t);
     const float sh_l2 = mt == kNegInf ? 0.f : mt * kLog2e;
     const float et = (mt == kNegInf || c_state == kNegInf) ? 0.f : fexp(mt - c_state);
@@ -899,11 +915,16 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
   float al = c_cur == kNegInf ? 0.f : fexp(c_cur - c_next);
-  store_kf(c_next);
+  // whether the coming chunk is evaluated on its state's scale: its key maxima (token 0's is
+  // the smallest P_i) within kSameScale of c_next
+  bool same_next = SAME && __builtin_amdgcn_readfirstlane(
+                               (int)(c_next - fmaxf(c_cur, token_max(0)) <= kSameScale));
+  store_kf(c_next, same_next);
   float pq = chunk_maxima(c_cur);  // P_i of this lane's query in the coming chunk
   write_state();  // the initial state, on scale c_cur
   float c_prev = c_cur;  // scale of the state in St
   c_cur = c_next;        // scale of the state after this chunk
+  bool same_cur = same_next;
 
   int buf = 0;
   for (int64_t c0 = t0; c0 < t1; c0 += C, buf ^= (NVB - 1)) {
@@ -1022,8 +1043,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     // shrunk by at most e^-kSameScale, far inside the bf16 / fp32 range): the key features
     // already written on c_cur (Kc) are then the masked product's operand as they are, and the
     // carried state takes one factor for all queries.  Other chunks use P_i.
-    const bool same = SAME && __builtin_amdgcn_readfirstlane(
-                                  (int)(c_cur - fmaxf(c_prev, mk[0]) <= kSameScale));
+    const bool same = same_cur;
     const float pe = same ? c_cur : pq;  // the scale of this lane's query in this chunk
     const float pq_l2 = pe * kLog2e;
     {
@@ -1050,7 +1070,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
         }
       }
     };
-    auto pack_a = [&](int m, f32x4 a0, f32x4 a1, auto samec) {
+    auto pack_a = [&](int m, f32x4 a0, f32x4 a1, auto samec, auto maskc) {
       if constexpr (!decltype(samec)::value) {
         const f32x4 m0 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 4 * g]);
         const f32x4 m1 = *reinterpret_cast<const f32x4*>(&mk[32 * m + 16 + 4 * g]);
@@ -1060,10 +1080,12 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
           a1[r] *= fexp_shift(m1[r], kLog2e, pq_l2);
         }
       }
+      if constexpr (decltype(maskc)::value) {  // the last step holds the diagonal tile
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
-        if (2 * m + 1 > it || (2 * m + 1 == it && g * 4 + r > l16)) a1[r] = 0.f;
+        for (int r = 0; r < 4; ++r) {
+          if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
+          if (2 * m + 1 > it || (2 * m + 1 == it && g * 4 + r > l16)) a1[r] = 0.f;
+        }
       }
       u32x4 af;
       af.x = pack_bf16(a0[0], a0[1]);
@@ -1086,12 +1108,12 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
 #pragma unroll
       for (int m = 0; m < NI / 2 - 1; ++m) {
         if (m < mlast) {
-          const u32x4 af = pack_a(m, a0, a1, samec);
+          const u32x4 af = pack_a(m, a0, a1, samec, BoolC<false>{});  // below the diagonal
           a_tiles(m + 1, a0, a1, samec);
           av_step(m, af);
         }
       }
-      av_step(mlast, pack_a(mlast, a0, a1, samec));
+      av_step(mlast, pack_a(mlast, a0, a1, samec, BoolC<true>{}));
     };
     if constexpr (SAME) {
       if (same)
@@ -1133,11 +1155,14 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     for (int w = 0; w < 8; ++w) c_next = fmaxf(c_next, wmax[w]);
     al = fexp(c_cur - c_next);
     if (NVB == 1) store_v(Vs[0], c0 + C);
-    store_kf(c_next);
+    same_next = SAME && __builtin_amdgcn_readfirstlane(
+                            (int)(c_next - fmaxf(c_cur, token_max(0)) <= kSameScale));
+    store_kf(c_next, same_next);
     pq = chunk_maxima(c_cur);
     write_state();  // the state after this chunk, on scale c_cur
     c_prev = c_cur;
     c_cur = c_next;
+    same_cur = same_next;
   }
 
   // the state after the last token (scale c_cur), in feature order, from the last segment
