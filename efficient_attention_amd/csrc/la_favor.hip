@@ -920,7 +920,9 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
   bool same_next = SAME && __builtin_amdgcn_readfirstlane(
                                (int)(c_next - fmaxf(c_cur, token_max(0)) <= kSameScale));
   store_kf(c_next, same_next);
-  float pq = chunk_maxima(c_cur);  // P_i of this lane's query in the coming chunk
+  // P_i of this lane's query in the coming chunk (and the chunk's key maxima mk), which a chunk
+  // evaluated on its state's scale does not use
+  float pq = same_next ? 0.f : chunk_maxima(c_cur);
   write_state();  // the initial state, on scale c_cur
   float c_prev = c_cur;  // scale of the state in St
   c_cur = c_next;        // scale of the state after this chunk
@@ -1158,7 +1160,7 @@ __global__ __launch_bounds__(512) void favor_causal(FavorCausalArgs a) {
     same_next = SAME && __builtin_amdgcn_readfirstlane(
                             (int)(c_next - fmaxf(c_cur, token_max(0)) <= kSameScale));
     store_kf(c_next, same_next);
-    pq = chunk_maxima(c_cur);
+    pq = same_next ? 0.f : chunk_maxima(c_cur);
     write_state();  // the state after this chunk, on scale c_cur
     c_prev = c_cur;
     c_cur = c_next;
