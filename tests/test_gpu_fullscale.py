@@ -1,12 +1,17 @@
 """GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
 
-The oracle cannot redo a whole 16K/64K-token batch in seconds, so each test checks:
-  * whole heads (sampled) against the oracle's full computation,
+The oracle cannot redo every full-size workload in seconds on one core, so the tests check:
+  * for C3 and C4, every head against the oracle's full computation (non-causal form, causal
+    recurrence), one head per host thread (about 20 s for C4's 128 heads on 16 cores); for the
+    grid points and FAVOR+, whole heads (sampled),
   * single rows (sampled, incl. segment and chunk boundaries and the last row) against the
     quadratic definition at O(n d) per row,
   * for decode, every step's output of sampled heads, and the final state of EVERY head
     against the fp64 sum of all tokens it has seen.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -43,15 +48,22 @@ def _check_forward(ea, name, form):
         out = ea.la_forward_causal(tq, tk, tv, chunk=w.chunk)
     g = from_dev(out, w.dtype)
     assert np.all(np.isfinite(g))
-    # whole heads
-    heads = [(0, 0), (w.B - 1, w.H - 1)]
-    for (b, h) in heads:
-        say(name, "oracle head", b, h)
+    # every head against the oracle's full computation; the heads are independent, and the C
+    # oracle (called through ctypes, which releases the interpreter lock) runs one per thread
+
+    def head_err(bh):
+        b, h = divmod(bh, w.H)
         Q, K, V = (f64(x[b, h], w.dtype) for x in (q, k, v))
         ref = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
-        e = form_err(form, g[b, h], ref)
-        print("%s head (%d,%d) err %.3e" % (name, b, h, e))
-        assert e <= TOL_BF16
+        return form_err(form, g[b, h], ref)
+
+    say(name, "oracle on all", w.B * w.H, "heads")
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        errs = np.array(list(ex.map(head_err, range(w.B * w.H))))
+    worst = int(np.argmax(errs))
+    print("%s all %d heads: worst err %.3e (head %d), median %.3e" % (name, errs.size, errs[worst], worst,
+                                                                    float(np.median(errs))))
+    assert errs.max() <= TOL_BF16, (worst, errs[worst])
     # sampled rows of other heads, by the quadratic definition
     rng = np.random.default_rng(7)
     seg_len = ea.la_causal_plan(w.B, w.H, w.n, w.d, w.chunk or 128, tq.dtype) if form == "causal" else w.n
@@ -177,8 +189,9 @@ GRID = [(form, dtype, n, d) for dtype in ("bf16", "f32") for form in ("noncausal
 @pytest.mark.parametrize("form,dtype,n,d", GRID)
 def test_grid_point_full_size(ea, form, dtype, n, d):
     # every shape of the metric's grid, in the launch configuration `bench.py --grid` times
-    # (128 heads, inputs drawn on the device from a seeded generator): sampled rows of two heads
-    # against the quadratic definition, and one whole head against the oracle at n = 16K
+    # (128 heads, inputs drawn on the device from a seeded generator): every head against the
+    # oracle's full computation (one head per host thread, heads fetched in batches), and
+    # sampled rows of two heads against the quadratic definition
     import zlib
 
     import torch
@@ -206,10 +219,22 @@ def test_grid_point_full_size(ea, form, dtype, n, d):
         say("grid", form, dtype, n, d, "oracle rows", b, h)
         ref = oracle.rows(Q, K, V, rows, causal=(form == "causal"))
         assert form_err(form, G[rows][None], ref[None]) <= tol, (b, h)
-        if n == 16384 and (b, h) == (0, 0):
-            say("grid", form, dtype, n, d, "oracle head")
-            whole = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
-            assert form_err(form, G, whole) <= tol
+
+    def head_err(Q, K, V, G):
+        whole = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
+        return form_err(form, G, whole)
+
+    say("grid", form, dtype, n, d, "oracle on all", B * H, "heads")
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    errs = []
+    with ThreadPoolExecutor(nthreads) as ex:
+        for h0 in range(0, B * H, nthreads):
+            batch = [divmod(bh, H) for bh in range(h0, min(B * H, h0 + nthreads))]
+            data = [(host(q[b, h]), host(k[b, h]), host(v[b, h]), host(out[b, h])) for (b, h) in batch]
+            errs += list(ex.map(lambda a: head_err(*a), data))
+    errs = np.array(errs)
+    print("grid %s %s n=%d d=%d all %d heads: worst err %.3e" % (form, dtype, n, d, errs.size, errs.max()))
+    assert errs.max() <= tol, (int(np.argmax(errs)), errs.max())
 
 
 
