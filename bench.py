@@ -107,33 +107,39 @@ def cpu_baseline(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec):
 
 def _cpu_baseline_pinned(C3, C4, C5, q3, k3, v3, q4, k4, v4, dec, f64, core):
     import oracle
-    # non-causal: 2 heads of n = 16384
-    Q, K, V = f64(q3[0, :2]), f64(k3[0, :2]), f64(v3[0, :2])
+    # non-causal: the 16 heads of the first sequence, n = 16384
+    nh3 = min(16, C3.H)
+    Q, K, V = f64(q3[0, :nh3]), f64(k3[0, :nh3]), f64(v3[0, :nh3])
     t = time.perf_counter()
     oracle.noncausal_linear(Q, K, V)
-    t_nc = (time.perf_counter() - t) / 2 * (C3.B * C3.H)
-    # causal: 1 head of n = 65536 by the recurrence
-    Q, K, V = f64(q4[0, :1]), f64(k4[0, :1]), f64(v4[0, :1])
+    t_nc = (time.perf_counter() - t) / nh3 * (C3.B * C3.H)
+    # causal: 8 heads of n = 65536 by the recurrence
+    nh4 = min(8, C4.H)
+    Q, K, V = f64(q4[0, :nh4]), f64(k4[0, :nh4]), f64(v4[0, :nh4])
     t = time.perf_counter()
     oracle.causal_recurrent(Q, K, V)
-    t_c = (time.perf_counter() - t) * (C4.B * C4.H)
-    # decode: one step for 128 of the 8192 heads (4 sequences x 32 heads)
+    t_c = (time.perf_counter() - t) / nh4 * (C4.B * C4.H)
+    # decode: one step for 1024 of the 8192 heads (32 sequences x 32 heads)
+    ns5 = min(32, C5.B)
     dq, dk, dv, S0, z0 = dec
-    dq, dk, dv = f64(dq[:4]), f64(dk[:4]), f64(dv[:4])
+    dq, dk, dv = f64(dq[:ns5]), f64(dk[:ns5]), f64(dv[:ns5])
     t = time.perf_counter()
-    oracle.decode_step(dq, dk, dv, S0[:4], z0[:4])
-    t_d = (time.perf_counter() - t) * (C5.B * C5.H) / (4 * C5.H)
+    oracle.decode_step(dq, dk, dv, S0[:ns5], z0[:ns5])
+    t_d = (time.perf_counter() - t) * C5.B / ns5
     step_s = t_nc + t_c + t_d
+    sample_s = t_nc * nh3 / (C3.B * C3.H) + t_c * nh4 / (C4.B * C4.H) + t_d * ns5 / C5.B
     tokens = C3.B * C3.n + C4.B * C4.n + C5.B
     return {
         "value": tokens / step_s,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": ("fp64 C oracle, 1 thread: non-causal 2 of 128 heads (n=16384), causal 1 of 128 "
-                   "heads (n=65536, recurrence), decode 1 step of 128 of 8192 heads; each scaled by "
-                   "its head count to one step of %d tokens; step time %.1f s; process pinned to one core"
-                   % (tokens, step_s)),
+        "sample": ("fp64 C oracle, 1 thread: non-causal %d of %d heads (n=%d), causal %d of %d "
+                   "heads (n=%d, recurrence), decode 1 step of %d of %d heads; each scaled by its head "
+                   "count to one step of %d tokens; sample %.1f s of CPU work, step time %.1f s; "
+                   "process pinned to one core"
+                   % (nh3, C3.B * C3.H, C3.n, nh4, C4.B * C4.H, C4.n, ns5 * C5.H, C5.B * C5.H, tokens,
+                      sample_s, step_s)),
         "host_cores": os.cpu_count(),
         "pinned_core": core,
         "cpu_model": cpu_model(),
