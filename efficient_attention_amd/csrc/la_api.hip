@@ -15,7 +15,11 @@ static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES]
 
 namespace {
 
-constexpr int64_t kTargetStateBlocks = 512;  // stage-1 workgroups to aim for (2 per CU)
+// Stage-1 workgroups to aim for: the stage-1 kernel's workgroup slots on 256 compute units.  Its
+// four-wave workgroups fit two per CU (registers or LDS), four for the fp32 kernel at d = 64
+// (84 registers, 34 KB of LDS).
+constexpr int64_t state_blocks_target(int d, int dtype) { return (dtype == LA_DTYPE_F32 && d == 64) ? 1024 : 512; }
+constexpr int64_t kTargetFavorStateBlocks = 512;  // FAVOR+ stage-1 workgroups to aim for (2 per CU)
 constexpr int64_t kTargetCausalBlocks = 256;  // one causal workgroup per compute unit
 constexpr int64_t kMaxSegments = 16;
 
@@ -61,7 +65,7 @@ StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
   p.groups = groups;
   const int64_t tile = la::kv_state_tile(d, dtype);
   const int64_t tiles = cdiv(group_len, tile);
-  int64_t slices = clamp64(cdiv(kTargetStateBlocks, groups), 1, tiles);
+  int64_t slices = clamp64(cdiv(state_blocks_target(d, dtype), groups), 1, tiles);
   p.slice_len = cdiv(tiles, slices) * tile;
   p.slices = cdiv(group_len, p.slice_len);
   const size_t E = (size_t)(d * d + d) * sizeof(float);
@@ -175,7 +179,7 @@ StatePlan plan_favor_state(int64_t groups, int64_t group_len, int d, int m) {
   StatePlan p;
   p.groups = groups;
   const int64_t tiles = cdiv(group_len, la::kFavorTile);
-  const int64_t slices = clamp64(cdiv(kTargetStateBlocks, groups), 1, tiles < 64 ? tiles : 64);
+  const int64_t slices = clamp64(cdiv(kTargetFavorStateBlocks, groups), 1, tiles < 64 ? tiles : 64);
   p.slice_len = cdiv(tiles, slices) * la::kFavorTile;
   p.slices = cdiv(group_len, p.slice_len);
   p.scratch_bytes = (size_t)groups * (size_t)p.slices * (size_t)la::favor_rec(d, m) * sizeof(float);
