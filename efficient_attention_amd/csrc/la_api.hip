@@ -75,10 +75,18 @@ StatePlan plan_state(int64_t groups, int64_t group_len, int d, int dtype) {
 
 size_t state_bytes(int64_t groups, int d) { return (size_t)groups * (size_t)(d * d + d) * sizeof(float); }
 
-// Non-causal workspace: the per-slice partials (summed by the output kernel), or the states
-// themselves when every head has one slice.
-size_t nc_ws_bytes(const StatePlan& p, int d) {
-  return p.slices > 1 ? p.scratch_bytes : state_bytes(p.groups, d);
+// Stage 2 of the non-causal form.  The bf16 output kernel at d = 64 takes 256 queries per
+// workgroup (la::nc_queries): adding a head's slice partials in every one of its workgroups would
+// re-read them for every 32 KB of queries, so state_reduce adds them once per head, in slice
+// order (the same sums, bit for bit), and the output kernel reads one state.  The other output
+// kernels take 2048 or 4096 queries and add the partials themselves.
+constexpr bool nc_reduce_first(int d, int dtype) { return dtype == LA_DTYPE_BF16 && d == 64; }
+
+// Non-causal workspace: the per-slice partials (and the summed states where they are reduced
+// first), or the states themselves when every head has one slice.
+size_t nc_ws_bytes(const StatePlan& p, int d, int dtype) {
+  if (p.slices == 1) return state_bytes(p.groups, d);
+  return p.scratch_bytes + (nc_reduce_first(d, dtype) ? state_bytes(p.groups, d) : 0);
 }
 
 // Causal workspace: the leading segments' partials (or their sums when one slice each).
@@ -227,7 +235,7 @@ int check_noncausal(const void* q, const void* k, const void* v, void* out, int6
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   c->plan = plan_state(c->bh, n, (int)d, dtype);
-  c->need = nc_ws_bytes(c->plan, (int)d);
+  c->need = nc_ws_bytes(c->plan, (int)d, dtype);
   if (overlaps(out, c->bytes, q, c->bytes) || overlaps(out, c->bytes, k, c->bytes) ||
       overlaps(out, c->bytes, v, c->bytes))
     return LA_ERR_ALIAS;
@@ -236,22 +244,33 @@ int check_noncausal(const void* q, const void* k, const void* v, void* out, int6
   return LA_OK;
 }
 
-// Both stages on `stream`, the slice partials in `ws` (c.need bytes, validated by the caller).
-int run_noncausal(const NcCall& c, const void* q, const void* k, const void* v, void* out, int64_t n,
-                  int d, int dtype, void* ws, void* stream) {
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+// Stage 1, the reduction where it applies, and the output kernel on `s`, with the workspace `ws`
+// (nc_ws_bytes(p, d, dtype) bytes, validated by the caller): partials first, then the summed
+// states.  n is the (longest) sequence length; tab the variable-length table or null.
+int run_nc_stages(const StatePlan& p, const void* q, const void* k, const void* v, void* out, int64_t n,
+                  int64_t bh, int d, int dtype, void* ws, hipStream_t s, const la::SeqTable* tab) {
   float* parts = reinterpret_cast<float*>(ws);
-  la::KvStateArgs ka = state_args(c.plan, k, v, parts, parts, n, n, 1);
-  if (la::launch_kv_state(ka, d, dtype, s) != hipSuccess) return LA_ERR_HIP;
-  la::NcOutArgs oa;  // the output kernel adds each head's slices itself
+  const bool reduce = p.slices > 1 && nc_reduce_first(d, dtype);
+  float* states = reduce ? parts + p.scratch_bytes / sizeof(float) : parts;
+  la::KvStateArgs ka = state_args(p, k, v, parts, states, n, n, 1);
+  if (la::launch_kv_state(ka, d, dtype, s, tab) != hipSuccess) return LA_ERR_HIP;
+  if (reduce && la::launch_state_reduce(ka, d, s) != hipSuccess) return LA_ERR_HIP;
+  la::NcOutArgs oa;  // otherwise the output kernel adds each head's slices itself
   oa.q = q;
   oa.out = out;
-  oa.state = parts;
-  oa.slices = c.plan.slices;
+  oa.state = states;
+  oa.slices = reduce ? 1 : p.slices;
   oa.n = n;
-  oa.bh = c.bh;
-  if (la::launch_nc_out(oa, d, dtype, s) != hipSuccess) return LA_ERR_HIP;
+  oa.bh = bh;
+  if (la::launch_nc_out(oa, d, dtype, s, tab) != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
+}
+
+// Both stages on `stream` (c.need bytes of workspace, validated by the caller).
+int run_noncausal(const NcCall& c, const void* q, const void* k, const void* v, void* out, int64_t n,
+                  int d, int dtype, void* ws, void* stream) {
+  return run_nc_stages(c.plan, q, k, v, out, n, c.bh, d, dtype, ws, reinterpret_cast<hipStream_t>(stream),
+                       nullptr);
 }
 
 // ---- scratch of la_forward_noncausal_noalloc
@@ -304,7 +323,7 @@ size_t la_noncausal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, 
   size_t bytes = 0;
   if (check_shape(B, H, n, d, dtype, &bh, &bytes) != LA_OK) return 0;
   if (bh == 0 || n == 0) return 0;
-  return nc_ws_bytes(plan_state(bh, n, (int)d, dtype), (int)d);
+  return nc_ws_bytes(plan_state(bh, n, (int)d, dtype), (int)d, dtype);
 }
 
 int la_forward_noncausal(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -574,7 +593,7 @@ size_t la_noncausal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t ns
                                            int64_t d, la_dtype_t dtype) {
   Varlen vl;
   if (make_varlen(cu_seqlens, nseq, H, d, dtype, &vl) != LA_OK || vl.bh == 0 || vl.maxn == 0) return 0;
-  return nc_ws_bytes(plan_state(vl.bh, vl.maxn, (int)d, dtype), (int)d);
+  return nc_ws_bytes(plan_state(vl.bh, vl.maxn, (int)d, dtype), (int)d, dtype);
 }
 
 int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, void* out,
@@ -587,7 +606,7 @@ int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, voi
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   const StatePlan p = plan_state(vl.bh, vl.maxn, (int)d, dtype);
-  const size_t need = nc_ws_bytes(p, (int)d);
+  const size_t need = nc_ws_bytes(p, (int)d, dtype);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LA_ERR_ALIGN;
   const size_t bytes = vl.bytes;
@@ -596,19 +615,8 @@ int la_forward_noncausal_varlen(const void* q, const void* k, const void* v, voi
     return LA_ERR_ALIAS;
   if (!grid_ok(p.groups * p.slices) || !grid_ok(vl.bh * cdiv(vl.maxn, la::nc_queries((int)d, dtype))))
     return LA_ERR_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  float* parts = reinterpret_cast<float*>(workspace);
-  la::KvStateArgs ka = state_args(p, k, v, parts, parts, vl.maxn, vl.maxn, 1);
-  if (la::launch_kv_state(ka, (int)d, dtype, s, &vl.tab) != hipSuccess) return LA_ERR_HIP;
-  la::NcOutArgs oa;
-  oa.q = q;
-  oa.out = out;
-  oa.state = parts;
-  oa.slices = p.slices;
-  oa.n = vl.maxn;
-  oa.bh = vl.bh;
-  if (la::launch_nc_out(oa, (int)d, dtype, s, &vl.tab) != hipSuccess) return LA_ERR_HIP;
-  return LA_OK;
+  return run_nc_stages(p, q, k, v, out, vl.maxn, vl.bh, (int)d, dtype, workspace,
+                       reinterpret_cast<hipStream_t>(stream), &vl.tab);
 }
 
 size_t la_causal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq, int64_t H,

@@ -799,9 +799,9 @@ hipError_t launch_state_reduce(const KvStateArgs& a, int d, hipStream_t s) {
   return d == 64 ? launch_state_reduce_t<64>(a, s) : launch_state_reduce_t<128>(a, s);
 }
 
-// bf16 output tiles: nc_queries(D, 1) queries per workgroup, halved (down to 512 at D = 64,
-// 2048 at D = 128, where smaller tiles spill registers) while the launch would leave compute
-// units idle (fewer than 256 workgroups, e.g. a few heads)
+// bf16 output tiles: nc_queries(D, 1) queries per workgroup (256 at D = 64); at D = 128 halved,
+// down to 2048, while the launch would leave compute units idle (fewer than 256 workgroups, e.g.
+// a few heads)
 template <int D, class TB, int QTV>
 static void launch_nc_out_bf16(const NcOutArgs& a, hipStream_t s, const TB& tb) {
   const int64_t tiles = (a.n + QTV - 1) / QTV;
