@@ -24,16 +24,18 @@ extern "C" {
 #endif
 
 /*
- * Plain device copy of `bytes` (a positive multiple of 16): dst = src.  Each thread moves four
- * 16-byte pieces per step (loads first, then stores), non-temporal both ways; 2048 workgroups of
- * 256 threads stride over the buffers.  src and dst must not overlap.
+ * Plain device copy of `bytes` (a positive multiple of 16): dst = src.  One 16-byte piece per
+ * thread, non-temporal both ways, one 256-thread workgroup per 4 KB of the buffer (the fastest
+ * copy pattern measured on the device).  src and dst must not overlap; a buffer of more than
+ * INT_MAX * 4 KB is LA_ERR_SHAPE.
  */
 int la_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /*
  * Read-only stream over `bytes` (a positive multiple of 16): every 16-byte piece of src is read
- * once; sink[w] (uint32, la_ceiling_read_sink_words() of them) receives the XOR of the 32-bit
- * words workgroup w read, so the result is checkable.  sink must not overlap src.
+ * once, non-temporally, each of la_ceiling_read_sink_words() workgroups streaming one contiguous
+ * range; sink[w] (uint32) receives the XOR of the 32-bit words workgroup w read, so the result is
+ * checkable.  sink must not overlap src.
  */
 size_t la_ceiling_read_sink_words(void);
 int la_ceiling_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
