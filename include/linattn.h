@@ -101,8 +101,8 @@ int la_forward_noncausal(const void* q, const void* k, const void* v, void* out,
 /*
  * la_forward_noncausal for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and the
- * same results (bit for bit), with the slice partials kept in a device array of the library
- * instead of a caller's workspace.  The call allocates nothing and frees nothing.
+ * same results (bit for bit), with the slice partials (and their per-head sums) kept in a device
+ * array of the library instead of a caller's workspace.  The call allocates nothing and frees nothing.
  *   q, k, v, out, B, H, n, d, dtype, stream : as for la_forward_noncausal
  * The array holds LA_NOALLOC_SCRATCH_BYTES bytes per GPU; it is reserved when the library's code
  * is loaded on a GPU and held until the process ends.  A shape whose partials need more
