@@ -542,6 +542,9 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
 #pragma unroll
   for (int r = 0; r < RPT; ++r)  // non-temporal, as in decode_step_kernel: read once per step
     sv[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (int64_t)(rg + RG * r) * D + cg * 4));
+  // the scale and z of the state, loaded with S (only this workgroup writes them, at the end)
+  const float c_old = a.c[h];
+  const float z_old = tid < M ? a.z[h * M + tid] : 0.f;
 
   const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + h * D;
   const uint16_t* k = reinterpret_cast<const uint16_t*>(a.k) + h * D;
@@ -585,7 +588,6 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
     wmq[wave] = mq;
   }
   __syncthreads();
-  const float c_old = a.c[h];
   const float umax = fmaxf(fmaxf(wmk[0], wmk[1]), fmaxf(wmk[2], wmk[3]));
   const float qmax = fmaxf(fmaxf(wmq[0], wmq[1]), fmaxf(wmq[2], wmq[3]));
   const float c_new = fmaxf(c_old, umax);
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(256) void favor_decode(FavorDecodeArgs a) {
     const float eq = fexp(s * (uq - qmax));
     fk[tid] = ek;
     fq[tid] = eq;
-    const float znew = al * a.z[h * M + tid] + ek;
+    const float znew = al * z_old + ek;
     a.z[h * M + tid] = znew;
     dpart = eq * znew;
   }
