@@ -68,6 +68,21 @@ def test_workspace_sizes():
     assert ea.la_causal_workspace_bytes(1, 1, 4096, 64, 64, 0) > 0
 
 
+def test_noncausal_plans_of_the_workload_shapes():
+    # The stage-1 plan aims at the stage-1 kernel's workgroup slots on 256 compute units: 512
+    # workgroups, 1024 for the fp32 kernel at d = 64.  128 heads therefore take 4 (or 8) slices
+    # each, and each slice writes one fp32 [KV | z] partial; for bf16 at d = 64 each head's
+    # partials are then added into one more state.
+    E64, E128 = (64 * 64 + 64) * 4, (128 * 128 + 128) * 4
+    assert ea.la_noncausal_workspace_bytes(8, 16, 16384, 64, 1) == 128 * 4 * E64 + 128 * E64
+    assert ea.la_noncausal_workspace_bytes(8, 16, 16384, 64, 0) == 128 * 8 * E64
+    assert ea.la_noncausal_workspace_bytes(8, 16, 16384, 128, 1) == 128 * 4 * E128
+    assert ea.la_noncausal_workspace_bytes(8, 16, 16384, 128, 0) == 128 * 4 * E128
+    # enough heads for one slice each: the states themselves, nothing added afterwards
+    assert ea.la_noncausal_workspace_bytes(64, 16, 4096, 64, 1) == 1024 * E64
+    assert ea.la_noncausal_workspace_bytes(64, 32, 4096, 64, 0) == 2048 * E64
+
+
 P = ctypes.c_void_p
 
 
