@@ -180,14 +180,13 @@ hipError_t launch_favor_causal(const FavorCausalArgs& a, int d, int m, int chunk
 // sn, zn, cn = the empty state (zeros, c = -inf) for every head
 hipError_t launch_favor_empty_state(const FavorCausalArgs& a, int d, int m, hipStream_t s);
 
-// Queries per workgroup of the non-causal output kernel: 4 waves x 512, or 4 waves x 1024 for
-// bf16 with d = 128, whose workgroups fit only two per compute unit (LDS): 128 heads x 16K
-// queries are then one round of workgroups.
-// Queries per workgroup of the non-causal output kernels.  The bf16 kernel at d = 64 takes 256:
-// its workgroups are then short and start in address order, so the rows being written at any
-// moment lie close together, which this device's HBM absorbed faster than a thousand long-lived
-// workgroups each writing its own 256 KB (128 heads of 16K tokens: 105 -> 93 us).  The fp32 and
-// d = 128 kernels measured no gain from smaller tiles.
+// Queries per workgroup of the non-causal output kernels.  fp32: 4 waves x 512.  bf16 at
+// d = 128: 4 waves x 1024; its workgroups fit only two per compute unit (LDS), so 128 heads x
+// 16K queries are one round of workgroups.  bf16 at d = 64: 256.  Its workgroups are then short
+// and start in address order, so the rows being written at any moment lie close together, which
+// this device's HBM absorbed faster than a thousand long-lived workgroups each writing its own
+// 256 KB (128 heads of 16K tokens: 105 -> 93 us).  The fp32 and d = 128 kernels measured no gain
+// from smaller tiles.
 constexpr int64_t nc_queries(int d, int dtype) { return dtype == 1 ? (d == 128 ? 4096 : 256) : 2048; }
 
 // Tile sizes the host needs for workspace planning.
