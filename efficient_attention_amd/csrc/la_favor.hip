@@ -147,11 +147,11 @@ __device__ __forceinline__ int favor_p_of_q(int q) {
 #define FAVOR_NW(D, M) ((M) >= 256 && (D) == 64 ? 16 : (M) >= 128 ? 8 : 4)
 // One workgroup (NW waves) sums the features of one token slice:
 // S_p = sum_j phi(k_j) v_j^T, z_p = sum_j phi(k_j), with log-scale c_p.  The slice streams
-// through LDS in tiles of 64 tokens (128 with 16 waves; double-buffered, one barrier per tile);
-// wave w owns the 16 FT features from w M / NW:
+// through LDS in tiles of 64 tokens (128 with 16 waves, 32 at D = M = 128; double-buffered, one
+// barrier per tile); wave w owns the 16 FT features from w M / NW:
 //   U = K_tile W_w^T on MFMA (A = token rows of K from LDS, B = this wave's rows of W, held in
 //       registers for the whole slice) -> lane holds u for feature l16 of each of its feature
-//       tiles and tokens 16 tt + 4 g + r of the four token tiles tt;
+//       tiles and tokens 16 tt + 4 g + r of the tile's token tiles tt;
 //   u = (scale U - (scale^2 |k|^2 / 2 + ln(M) / 2)) log2(e) per token, i.e. the exponent in
 //       base-2 units (one FMA per element); the wave's running maximum c_w;
 //   S_w += 2^(u - c_w)^T V_tile and z_w += 2^(u - c_w)^T 1 on MFMA, the exp values packed to
@@ -159,11 +159,19 @@ __device__ __forceinline__ int favor_p_of_q(int q) {
 //       V read transposed from LDS in the same token order.
 // At the end the waves' blocks are brought to the workgroup maximum and written, the log-scale
 // converted back to natural-log units.
+// At D = M = 128 the kernel fits 128 VGPRs, so two workgroups share a compute unit: 32-token
+// tiles, the next tile's loads issued after the projection, and V operands read in two halves.
+// That took the non-causal forward at d = m = 128 (128 heads of 65,536 tokens) from 1.93 to
+// 1.86 ms; the other shapes keep 64-token tiles and the early loads, which measured 1-2% faster
+// for them.
+#define FAVOR_STATE_WIDE(D, M) ((D) == 128 && (M) == 128)
 template <int D, int M>
-__global__ __launch_bounds__(FAVOR_NW(D, M) * 64) void favor_kv_state(FavorStateArgs a) {
+__global__ __launch_bounds__(FAVOR_NW(D, M) * 64) __attribute__((amdgpu_waves_per_eu(FAVOR_STATE_WIDE(D, M) ? 4 : 1)))
+void favor_kv_state(FavorStateArgs a) {
   constexpr int NW = FAVOR_NW(D, M);
   constexpr int NT = 64 * NW;
-  constexpr int T = NW == 16 ? 2 * kFavorTile : kFavorTile;
+  constexpr bool kWide = FAVOR_STATE_WIDE(D, M);
+  constexpr int T = NW == 16 ? 2 * kFavorTile : (kWide ? kFavorTile / 2 : kFavorTile);
   constexpr int TT = T / 16;        // token tiles per tile
   constexpr int LDK = D + 16;
   constexpr int KA = D / 32;        // k-steps of the projection
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(FAVOR_NW(D, M) * 64) void favor_kv_state(FavorState
   __syncthreads();
   int b = 0;
   for (int64_t tt = t0; tt < t1; tt += T, b ^= 1) {
-    load(tt + T);  // next tile (clamped rows past the end; stored but never counted)
+    if constexpr (!kWide) load(tt + T);  // next tile (clamped rows past the end; stored but never counted)
     f32x4 u[FT][TT];
     float tmax = kNegInf;
 #pragma unroll
@@ -275,6 +283,7 @@ __global__ __launch_bounds__(FAVOR_NW(D, M) * 64) void favor_kv_state(FavorState
         }
       }
     }
+    if constexpr (kWide) load(tt + T);
     tmax = wave_max(tmax);
     if (tmax > cw) {  // wave-uniform: rescale what this wave has summed to the new maximum
       const float al = __builtin_amdgcn_exp2f(cw - tmax);
@@ -286,22 +295,41 @@ __global__ __launch_bounds__(FAVOR_NW(D, M) * 64) void favor_kv_state(FavorState
       }
       cw = tmax;
     }
+    auto pack_exp = [&](const f32x4& u0, const f32x4& u1) {  // 2^(u - c_w) of two token tiles, bf16
+      u32x4 r;
+      r.x = pack_bf16(__builtin_amdgcn_exp2f(u0[0] - cw), __builtin_amdgcn_exp2f(u0[1] - cw));
+      r.y = pack_bf16(__builtin_amdgcn_exp2f(u0[2] - cw), __builtin_amdgcn_exp2f(u0[3] - cw));
+      r.z = pack_bf16(__builtin_amdgcn_exp2f(u1[0] - cw), __builtin_amdgcn_exp2f(u1[1] - cw));
+      r.w = pack_bf16(__builtin_amdgcn_exp2f(u1[2] - cw), __builtin_amdgcn_exp2f(u1[3] - cw));
+      return r;
+    };
 #pragma unroll
     for (int st = 0; st < TT / 2; ++st) {
-      u32x4 bv[DC];
+      if constexpr (!kWide) {
+        u32x4 bv[DC];
 #pragma unroll
-      for (int ct = 0; ct < DC; ++ct) bv[ct] = ld_v_rows<D>(Vs[b], st * 32, ct * 16, l16, g);
+        for (int ct = 0; ct < DC; ++ct) bv[ct] = ld_v_rows<D>(Vs[b], st * 32, ct * 16, l16, g);
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        const f32x4 u0 = u[ft][2 * st], u1 = u[ft][2 * st + 1];
-        u32x4 af;
-        af.x = pack_bf16(__builtin_amdgcn_exp2f(u0[0] - cw), __builtin_amdgcn_exp2f(u0[1] - cw));
-        af.y = pack_bf16(__builtin_amdgcn_exp2f(u0[2] - cw), __builtin_amdgcn_exp2f(u0[3] - cw));
-        af.z = pack_bf16(__builtin_amdgcn_exp2f(u1[0] - cw), __builtin_amdgcn_exp2f(u1[1] - cw));
-        af.w = pack_bf16(__builtin_amdgcn_exp2f(u1[2] - cw), __builtin_amdgcn_exp2f(u1[3] - cw));
-        accz[ft] = mfma_bf16(af, ones, accz[ft]);
+        for (int ft = 0; ft < FT; ++ft) {
+          const u32x4 af = pack_exp(u[ft][2 * st], u[ft][2 * st + 1]);
+          accz[ft] = mfma_bf16(af, ones, accz[ft]);
 #pragma unroll
-        for (int ct = 0; ct < DC; ++ct) acc[ft][ct] = mfma_bf16(af, bv[ct], acc[ft][ct]);
+          for (int ct = 0; ct < DC; ++ct) acc[ft][ct] = mfma_bf16(af, bv[ct], acc[ft][ct]);
+        }
+      } else {  // one feature tile per wave; V operands in two halves of the value columns
+        static_assert(FT == 1 && DC % 2 == 0, "shape");
+        constexpr int CG = DC / 2;
+        u32x4 bv[CG];
+#pragma unroll
+        for (int c = 0; c < CG; ++c) bv[c] = ld_v_rows<D>(Vs[b], st * 32, c * 16, l16, g);
+        const u32x4 af = pack_exp(u[0][2 * st], u[0][2 * st + 1]);
+        accz[0] = mfma_bf16(af, ones, accz[0]);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) acc[0][c] = mfma_bf16(af, bv[c], acc[0][c]);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) bv[c] = ld_v_rows<D>(Vs[b], st * 32, (CG + c) * 16, l16, g);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) acc[0][CG + c] = mfma_bf16(af, bv[c], acc[0][CG + c]);
       }
     }
     store(b ^ 1, tt + T);
