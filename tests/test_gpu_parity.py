@@ -692,3 +692,24 @@ def test_workspace_contents_do_not_matter(ea, fill):
         gc2 = from_dev(ea.la_forward_causal(tq, tk, tv, chunk=chunk,
                                             ws=torch.zeros(big, dtype=torch.uint8, device="cuda")), dtype)
         assert np.array_equal(gc, gc2)
+
+
+def test_release_workspaces_drops_the_cached_buffers(ea):
+    # calls given no workspace share one per (device, stream); release_workspaces hands them back
+    import torch
+    from efficient_attention_amd import _binding
+    dtype = "bf16"
+    q, k, v = (to_dev(x, dtype) for x in random_inputs(81, (2, 4, 3000, 64), dtype, 0.125))
+    _binding.release_workspaces()
+    say("workspace cache")
+    a = ea.la_forward_noncausal(q, k, v)
+    torch.cuda.synchronize()
+    need = ea.la_noncausal_workspace_bytes(2, 4, 3000, 64, torch.bfloat16)
+    assert need > 0
+    assert _binding.release_workspaces(device=q.device) >= need
+    assert _binding.release_workspaces() == 0
+    assert _binding.release_workspaces(device=q.device) == 0
+    b = ea.la_forward_noncausal(q, k, v)  # a new cached workspace, the same result
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert _binding.release_workspaces() >= need
