@@ -237,7 +237,7 @@ def run_grid():
                 for d in (64, 128):
                     # bf16: chunk 128; fp32: chunk 64 (d*chunk <= 8192 at d = 128; at d = 64 it fits three
                     # workgroups per compute unit, measured faster than chunk 128)
-                    chunk = 128 if dtype == "bf16" else 64
+                    chunk = 64 if (dtype == "f32" and d == 128) else 128  # the largest the kernel takes
                     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
                     gen = torch.Generator(device=dev)
                     gen.manual_seed(zlib.crc32(repr((form, dtype, n, d)).encode()))

@@ -17,7 +17,7 @@ namespace {
 
 // Stage-1 workgroups to aim for: the stage-1 kernel's workgroup slots on 256 compute units.  Its
 // four-wave workgroups fit two per CU (registers or LDS), four for the fp32 kernel at d = 64
-// (84 registers, 34 KB of LDS).
+// (90 registers, 40 KB of LDS).
 constexpr int64_t state_blocks_target(int d, int dtype) { return (dtype == LA_DTYPE_F32 && d == 64) ? 1024 : 512; }
 constexpr int64_t kTargetFavorStateBlocks = 512;  // FAVOR+ stage-1 workgroups to aim for (2 per CU)
 constexpr int64_t kTargetCausalBlocks = 256;  // one causal workgroup per compute unit
@@ -94,17 +94,12 @@ size_t causal_ws_bytes(const StatePlan& p, int d) {
   return p.slices > 1 ? p.scratch_bytes : state_bytes(p.groups, d);
 }
 
-// Chunked causal workgroups that fit on one compute unit: the fp32 kernel at d = 64 with
-// 64-token chunks uses 52 KB of LDS (three per CU); the others one per CU.
-int64_t causal_wgs_per_cu(int64_t d, int64_t chunk, int dtype) {
-  return (dtype == LA_DTYPE_F32 && d * chunk <= 4096) ? 3 : 1;
-}
-
 // Tokens per segment: enough segments that the (head, segment) workgroups fill every compute
-// unit's workgroup slots (at most kMaxSegments per head).
-int64_t causal_seg_len(int64_t bh, int64_t n, int64_t chunk, int64_t wgs_per_cu = 1) {
+// unit (at most kMaxSegments per head).  Every chunked causal kernel, bf16 or fp32, runs one
+// eight-wave workgroup per CU (registers and LDS).
+int64_t causal_seg_len(int64_t bh, int64_t n, int64_t chunk) {
   const int64_t nchunks = cdiv(n, chunk);
-  int64_t segs = clamp64(cdiv(kTargetCausalBlocks * wgs_per_cu, bh), 1, kMaxSegments);
+  int64_t segs = clamp64(cdiv(kTargetCausalBlocks, bh), 1, kMaxSegments);
   segs = clamp64(segs, 1, nchunks);
   return cdiv(nchunks, segs) * chunk;
 }
@@ -357,7 +352,7 @@ size_t la_causal_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
   size_t bytes = 0;
   if (check_causal(B, H, n, d, chunk, dtype, &bh, &bytes) != LA_OK) return 0;
   if (bh == 0 || n == 0) return 0;
-  const int64_t seg_len = causal_seg_len(bh, n, chunk, causal_wgs_per_cu(d, chunk, dtype));
+  const int64_t seg_len = causal_seg_len(bh, n, chunk);
   const int64_t segs = cdiv(n, seg_len);
   if (segs == 1) return 0;
   return causal_ws_bytes(plan_state(bh * (segs - 1), seg_len, (int)d, dtype), (int)d);
@@ -370,7 +365,7 @@ int la_causal_plan(int64_t B, int64_t H, int64_t n, int64_t d, int64_t chunk, la
   int st = check_causal(B, H, n, d, chunk, dtype, &bh, &bytes);
   if (st != LA_OK) return st;
   if (!seg_len) return LA_ERR_NULL;
-  *seg_len = (bh == 0 || n == 0) ? chunk : causal_seg_len(bh, n, chunk, causal_wgs_per_cu(d, chunk, dtype));
+  *seg_len = (bh == 0 || n == 0) ? chunk : causal_seg_len(bh, n, chunk);
   return LA_OK;
 }
 
@@ -496,7 +491,7 @@ int la_forward_causal_state(const void* q, const void* k, const void* v, void* o
   }
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
-  const int64_t seg_len = causal_seg_len(bh, n, chunk, causal_wgs_per_cu(d, chunk, dtype));
+  const int64_t seg_len = causal_seg_len(bh, n, chunk);
   const int64_t segs = cdiv(n, seg_len);
   StatePlan p;
   size_t need = 0;
@@ -624,7 +619,7 @@ size_t la_causal_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t nseq,
   Varlen vl;
   if (make_varlen(cu_seqlens, nseq, H, d, dtype, &vl) != LA_OK || vl.bh == 0 || vl.maxn == 0) return 0;
   if (chunk != 64 && chunk != 128) return 0;
-  const int64_t seg_len = causal_seg_len(vl.bh, vl.maxn, chunk, causal_wgs_per_cu(d, chunk, dtype));
+  const int64_t seg_len = causal_seg_len(vl.bh, vl.maxn, chunk);
   const int64_t segs = cdiv(vl.maxn, seg_len);
   if (segs == 1) return 0;
   return causal_ws_bytes(plan_state(vl.bh * (segs - 1), seg_len, (int)d, dtype), (int)d);
@@ -642,7 +637,7 @@ int la_forward_causal_varlen(const void* q, const void* k, const void* v, void* 
   if (vl.bh == 0 || vl.maxn == 0) return LA_OK;
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
-  const int64_t seg_len = causal_seg_len(vl.bh, vl.maxn, chunk, causal_wgs_per_cu(d, chunk, dtype));
+  const int64_t seg_len = causal_seg_len(vl.bh, vl.maxn, chunk);
   const int64_t segs = cdiv(vl.maxn, seg_len);
   StatePlan p;
   size_t need = 0;

@@ -405,45 +405,47 @@ __global__ __launch_bounds__(512) void causal_bf16(CausalArgs a, TB tb) {
   }
 }
 
-// waves per workgroup of the fp32 kernel: eight at d = 128, whose LDS admits one workgroup per
-// compute unit (four waves would leave one wave per SIMD), four otherwise
-constexpr int f32_waves(int d) { return d == 128 ? 8 : 4; }
-
-// fp32 kernel (no bf16 rounding anywhere).  The fp32 MFMA takes one k value per lane; a lane
-// holds 16-byte pieces of rows, features 16m + 4g .. 16m + 4g + 3, and k-step (m, e) pairs
-// feature 16m + 4g + e on both operands.  With four waves, each wave owns query tiles (tiles w
-// and NI - 1 - w when a chunk has 8, tile w when it has 4) and produces all output columns of
-// them: the masked tile A^T = phi(K) phi(Q)^T of each (key tile, query tile) pair is computed
-// once, by its owner, and fed back as an operand with permuted k, as in the bf16 kernel.  With
-// eight waves (d = 128) waves w and 7 - w share tile w and produce half the columns each, both
-// computing its masked tiles.  The inter-chunk product reads S^T from LDS; the state
-// accumulators are split by value columns (wave w owns column tiles w, w + NW, ...) and written
-// to S^T after each chunk's update.  The next chunk's K and V rows are loaded into registers
-// while the current chunk is computed.
+// fp32 kernel: the bf16 kernel's schedule, tiles and operand layouts, with every product of fp32
+// values taken on the bf16 MFMA from two-term splits (split4 / split8 / mfma_split in
+// la_common.h): phi(K), V, the state S^T and z are held in LDS as two bf16 planes (hi, lo),
+// phi(Q) and the masked weights A as hi and lo operands in registers, and each 16x16x32 product
+// becomes four.  The running state, z, every accumulation and the output division stay fp32.
+// (The fp32 MFMA, 16x16x4, does the same work at 1/16 of the bf16 rate; four terms cost 1/4 plus
+// the vector work of splitting, which leaves the kernel bound by memory, not the matrix pipe.)
+//
+// LDS, bf16 planes: KnH/KnL [C][D + 16] phi(K); VnH/VnL [C][D] V, pieces permuted as in the bf16
+// kernel (one buffer: the next chunk's V is stored after the chunk's second barrier, with K);
+// StH/StL [D][D] S^T (pswz); Zr [16][D + 16], rows 0 and 1 the hi and lo of z.  d = 128 with
+// 64-token chunks takes 137 KB (one workgroup per CU); d = 64 takes 55 KB with 64-token chunks
+// (two per CU) and 91 KB with 128.
 template <int D, int C, class TB>
-__global__ __launch_bounds__(64 * f32_waves(D)) __attribute__((amdgpu_waves_per_eu(D * C <= 4096 ? 3 : (f32_waves(D) == 8 ? 2 : 1)))) void causal_f32(
-    CausalArgs a, TB tb) {  // three workgroups per CU where the LDS allows (d = 64, 64-token chunks)
-  constexpr int NW = f32_waves(D);   // waves: 8 at d = 128 (one workgroup per CU fits the LDS)
-  constexpr int NT = 64 * NW;
-  constexpr int LD = D + 4;
-  constexpr int NI = C / 16;         // token tiles per chunk
-  constexpr int NA = D / 16;         // feature tiles
-  constexpr int NC = D / 16;         // output column tiles
-  constexpr int NCW = NC / NW;       // state column tiles per wave
-  constexpr int KM = D / 16;         // 16-feature groups of a reduction over features
-  constexpr int SH = NI >= NW ? 1 : NW / NI;  // waves sharing a query tile (splitting its columns)
-  constexpr int TPW = NI >= NW ? NI / NW : 1; // query tiles per wave
-  constexpr int NCO = NC / SH;       // output column tiles per wave
-  constexpr int PPR = D / 4;         // 16-byte pieces per row
-  constexpr int NP = C * PPR / NT;   // K (and V) pieces per thread
-  static_assert((NI == 8 || NI == 4) && NCW >= 1 && SH <= 2 && NP >= 1, "chunk");
-  __shared__ __attribute__((aligned(16))) float Kn[C * LD];
-  __shared__ __attribute__((aligned(16))) float Vn[C * LD];
-  __shared__ __attribute__((aligned(16))) float St[D * LD];  // S^T of the state before the chunk
+__global__ __launch_bounds__(512) void causal_f32(
+    CausalArgs a, TB tb) {
+  constexpr int NT = 512;
+  constexpr int LDK = D + 16;
+  constexpr int NI = C / 16;
+  constexpr int NC = D / 16;
+  constexpr int NA = D / 16;
+  constexpr int NAW = NA / 4;
+  constexpr int NCW = NC / 2;
+  constexpr int OCT = NI == 8 ? NC : NC / 2;
+  constexpr int KA = D / 32;
+  constexpr int KJ = C / 32;
+  constexpr int PPR = D / 4;          // 16-byte fp32 pieces per row
+  constexpr int RPK = C * PPR / NT;   // K (and V) pieces per thread
+  static_assert(NI == 8 || NI == 4, "chunk");
+  static_assert(RPK >= 1, "tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t KnH[C * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t KnL[C * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t VnH[C * D];
+  __shared__ __attribute__((aligned(16))) uint16_t VnL[C * D];
+  __shared__ __attribute__((aligned(16))) uint16_t StH[D * D];
+  __shared__ __attribute__((aligned(16))) uint16_t StL[D * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Zr[16 * LDK];
   __shared__ float zf[D];
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
   const HeadSpan sp = head_span(tb, a.n, bh);
@@ -455,215 +457,320 @@ __global__ __launch_bounds__(64 * f32_waves(D)) __attribute__((amdgpu_waves_per_
   const float* V = reinterpret_cast<const float*>(a.v) + sp.row0 * D;
   float* O = reinterpret_cast<float*>(a.out) + sp.row0 * D;
 
-  f32x4 accS[NA][NCW];
+  const int it = wave < 4 ? wave : (NI == 8 ? 11 - wave : 7 - wave);   // this wave's query tile
+  const int oc0 = (NI == 8 || wave < 4) ? 0 : NC / 2;                 // its first output column tile
+  const int sa0 = NAW * (wave & 3), sc0 = NCW * (wave >> 2);           // its state block
+  const bool zown = wave < 4;                                          // keeps z of tiles sa0..
+
+  // ---- initial state: sum of the leading segments' sums (the bf16 kernel's grouping)
+  f32x4 accS[NAW][NCW];
 #pragma unroll
-  for (int at = 0; at < NA; ++at)
+  for (int i = 0; i < NAW; ++i)
 #pragma unroll
-    for (int p = 0; p < NCW; ++p) accS[at][p] = zero4();
+    for (int j = 0; j < NCW; ++j) accS[i][j] = zero4();
   float zinit = 0.f;
   if (a.s0) {  // the state before the sequence
     const float* s0 = a.s0 + bh * D * D;
 #pragma unroll
-    for (int at = 0; at < NA; ++at)
+    for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p)
+      for (int j = 0; j < NCW; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accS[at][p][r] = s0[(at * 16 + g * 4 + r) * D + (wave + NW * p) * 16 + l16];
+        for (int r = 0; r < 4; ++r) accS[i][j][r] = s0[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16];
     if (tid < D) zinit = a.z0[bh * D + tid];
   }
-  for (int64_t s = 0; s < seg; ++s) {      // same grouping as in the bf16 kernel
-    f32x4 part[NA][NCW];
+  for (int64_t s = 0; s < seg; ++s) {
+    f32x4 part[NAW][NCW];
     float zpart = 0.f;
 #pragma unroll
-    for (int at = 0; at < NA; ++at)
+    for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p) part[at][p] = zero4();
-    for (int64_t q = 0; q < a.seg_parts; ++q) {
-      const float* st = seg_state_ptr(a, bh, s * a.seg_parts + q, D);
+      for (int j = 0; j < NCW; ++j) part[i][j] = zero4();
+    for (int64_t p = 0; p < a.seg_parts; ++p) {
+      const float* st = seg_state_ptr(a, bh, s * a.seg_parts + p, D);
 #pragma unroll
-      for (int at = 0; at < NA; ++at)
+      for (int i = 0; i < NAW; ++i)
 #pragma unroll
-        for (int p = 0; p < NCW; ++p)
+        for (int j = 0; j < NCW; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            part[at][p][r] += st[(at * 16 + g * 4 + r) * D + (wave + NW * p) * 16 + l16];
+            part[i][j][r] += st[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16];
       if (tid < D) zpart += st[D * D + tid];
     }
 #pragma unroll
-    for (int at = 0; at < NA; ++at)
+    for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p) accS[at][p] += part[at][p];
+      for (int j = 0; j < NCW; ++j) accS[i][j] += part[i][j];
     zinit += zpart;
   }
   if (tid < D) zf[tid] = zinit;
-
-  // The key sums z are added on the vector ALU beside the state update (whose MFMA pipe is the
-  // busy one), each wave for feature tiles wave + NW i: lane (l16, g) sums the keys 4 ks + g of
-  // feature 16 (wave + NW i) + l16 over the chunk, the four lane groups are summed once, and zf
-  // takes the chunk's sums for the next chunk's normalisers.
-  constexpr int NZW = NA / NW;
-
-  // S^T of the initial state for the first chunk's inter-chunk product
-  auto write_st = [&]() {
+  auto write_state = [&]() {
 #pragma unroll
-    for (int at = 0; at < NA; ++at)
+    for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p)
-        *reinterpret_cast<f32x4*>(&St[((wave + NW * p) * 16 + l16) * LD + at * 16 + g * 4]) = accS[at][p];
+      for (int j = 0; j < NCW; ++j) {
+        u32x2 h, l;
+        split4(accS[i][j], h, l);
+        const int o = pswz<D>((sc0 + j) * 16 + l16, (sa0 + i) * 16 + g * 4);
+        *reinterpret_cast<u32x2*>(&StH[o]) = h;
+        *reinterpret_cast<u32x2*>(&StL[o]) = l;
+      }
   };
-  write_st();
-  __syncthreads();  // zf holds the initial key sums
+  write_state();
+  __syncthreads();
+  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
+  u32x4 ones;                          // A operand with a row of ones (row 0)
+  ones.x = ones.y = ones.z = ones.w = (l16 == 0) ? one2 : 0u;
+  f32x4 accz[NAW];                     // z of this wave's feature tiles (column 0 of phi(K)^T ones)
+  const u32x4 zones = zown ? ones : zero_u4();
+#pragma unroll
+  for (int i = 0; i < NAW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accz[i][r] = (zown && l16 == 0) ? zf[(sa0 + i) * 16 + g * 4 + r] : 0.f;
+  for (int e = tid; e < 16 * D; e += NT) {
+    const int row = e / D, c = e % D;
+    uint16_t val = 0;
+    if (row == 0) val = (uint16_t)(__float_as_uint(zf[c]) >> 16);
+    if (row == 1) val = __builtin_bit_cast(uint16_t, (__bf16)split_rest(zf[c]));
+    Zr[row * LDK + c] = val;
+  }
 
-  // K and V pieces: piece tid + NT p of a chunk is row (tid / PPR) + (NT / PPR) p, columns
-  // 4 (tid % PPR) .. + 3.  Rows past the segment end read row t1 - 1 and are zeroed in LDS.
+  // ---- K and V tiles: fp32 piece tid + 512 p of each (16-byte pieces, row-major)
+  f32x4 kq[RPK], vq[RPK];
+  f32x4 qr[KA][2];  // this wave's query rows (raw): features 32 ks + 8 g .. + 7
+  u32x2 khi[RPK], klo[RPK], vhi[RPK], vlo[RPK];
   auto prow = [&](int p) { return tid / PPR + p * (NT / PPR); };
-  // the query tile of this wave's tp-th share, and the first of its output column tiles: with
-  // four waves, tiles w and NI - 1 - w (NI = 8) or w (NI = 4), all columns; with eight waves
-  // and four tiles, tile w shared by waves w and 7 - w, which take half the columns each (a SIMD
-  // holds waves s and s + 4, so tiles s and 3 - s: the causal triangle is balanced per SIMD)
-  auto tile_of = [&](int tp) { return SH == 1 ? (tp == 0 ? wave : NI - 1 - wave) : (wave < 4 ? wave : 7 - wave); };
-  const int cb = SH == 1 ? 0 : (wave < 4 ? 0 : NCO);
   const int pcol = (tid % PPR) * 4;
-  f32x4 kq[NP], vq[NP];
-  auto load_kv = [&](int64_t c0) {
+  auto ldf = [&](const float* base, int64_t row, int col) {  // rows past the end read row t1 - 1
+    const int64_t r = row < t1 ? row : t1 - 1;
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + r * D + col));
+  };
+  auto load_k = [&](int64_t c0) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int64_t r = c0 + prow(p) < t1 ? c0 + prow(p) : t1 - 1;
-      kq[p] = *reinterpret_cast<const f32x4*>(K + r * D + pcol);
-      vq[p] = *reinterpret_cast<const f32x4*>(V + r * D + pcol);
+    for (int p = 0; p < RPK; ++p) kq[p] = ldf(K, c0 + prow(p), pcol);
+  };
+  auto load_v = [&](int64_t c0) {
+#pragma unroll
+    for (int p = 0; p < RPK; ++p) vq[p] = ldf(V, c0 + prow(p), pcol);
+  };
+  auto load_q = [&](int64_t c0) {  // rows >= t1 are never stored
+    const int64_t row = c0 + it * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) {
+      qr[ks][0] = ldf(Q, row, ks * 32 + g * 8);
+      qr[ks][1] = ldf(Q, row, ks * 32 + g * 8 + 4);
     }
   };
-  load_kv(t0);
-  for (int64_t c0 = t0; c0 < t1; c0 += C) {
-    // this wave's query rows (rows past the end read row t1 - 1; their outputs are not stored)
-    f32x4 qv[TPW][KM];
+  // feature map on K, then both tiles split; rows past the segment end become zero.  V is
+  // canonicalised first so that a signalling NaN stays NaN in hi.
+  auto prep_kv = [&](int64_t c0) {
 #pragma unroll
-    for (int tp = 0; tp < TPW; ++tp) {
-      const int it = tile_of(tp);
-      const int64_t row = c0 + it * 16 + l16;
-      const int64_t r = row < t1 ? row : t1 - 1;
-#pragma unroll
-      for (int m = 0; m < KM; ++m) qv[tp][m] = *reinterpret_cast<const f32x4*>(Q + r * D + m * 16 + g * 4);
-    }
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {  // phi on K; rows past the end are zero in both tiles
-      const bool ok = c0 + prow(p) < t1;
-      f32x4 kk = kq[p];
+    for (int p = 0; p < RPK; ++p) {
+      const uint32_t m = 0u - (uint32_t)(c0 + prow(p) < t1);
+      f32x4 kk = kq[p], vv = vq[p];
       kk.x = phi(kk.x);
       kk.y = phi(kk.y);
       kk.z = phi(kk.z);
       kk.w = phi(kk.w);
-      *reinterpret_cast<u32x4*>(&Kn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, kk), ok);
-      *reinterpret_cast<u32x4*>(&Vn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, vq[p]), ok);
+      vv.x = __builtin_canonicalizef(vv.x);
+      vv.y = __builtin_canonicalizef(vv.y);
+      vv.z = __builtin_canonicalizef(vv.z);
+      vv.w = __builtin_canonicalizef(vv.w);
+      split4(kk, khi[p], klo[p]);
+      split4(vv, vhi[p], vlo[p]);
+      khi[p].x &= m;
+      khi[p].y &= m;
+      klo[p].x &= m;
+      klo[p].y &= m;
+      vhi[p].x &= m;
+      vhi[p].y &= m;
+      vlo[p].x &= m;
+      vlo[p].y &= m;
     }
-    __syncthreads();  // tiles, S^T and z of this chunk ready
-    load_kv(c0 + C);  // the next chunk's rows arrive while this one is computed
+  };
 
+  // V pieces permuted by the row as in the bf16 kernel (conflict-free transpose reads)
+  constexpr int VRL = 128 / D;
+  auto vofs = [&](int r, int c) { return r * D + ((((c >> 3) ^ (2 * ((r / VRL) % (D / 16))))) << 3) + (c & 7); };
+  auto ld_v_operand = [&](const uint16_t* Vt, int row0, int col0) {
+    const uint16_t* p0 = Vt + vofs(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3));
+    const u32x2 lo = ld_tr16(p0), hi = ld_tr16(p0 + 16 * D);
+    u32x4 r;
+    r.x = lo.x;
+    r.y = lo.y;
+    r.z = hi.x;
+    r.w = hi.y;
+    return r;
+  };
+  auto store_kv = [&]() {
 #pragma unroll
-    for (int tp = 0; tp < TPW; ++tp) {
-      const int it = tile_of(tp);
-      f32x4 qf[KM];
-      float dpart = 0.f;  // phi(q) . z over this lane's features
-#pragma unroll
-      for (int m = 0; m < KM; ++m) {
-        qf[m].x = phi(qv[tp][m].x);
-        qf[m].y = phi(qv[tp][m].y);
-        qf[m].z = phi(qv[tp][m].z);
-        qf[m].w = phi(qv[tp][m].w);
-        dpart += qf[m].x * zf[m * 16 + g * 4] + qf[m].y * zf[m * 16 + g * 4 + 1] +
-                 qf[m].z * zf[m * 16 + g * 4 + 2] + qf[m].w * zf[m * 16 + g * 4 + 3];
-      }
-      f32x4 acco[NCO];
-#pragma unroll
-      for (int c = 0; c < NCO; ++c) acco[c] = zero4();
-      // inter-chunk: S^T phi(Q)^T (this wave's output columns)
-#pragma unroll
-      for (int m = 0; m < KM; ++m)
-#pragma unroll
-        for (int c = 0; c < NCO; ++c) {
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(&St[((cb + c) * 16 + l16) * LD + m * 16 + g * 4]);
-          acco[c] = mfma_f32(sv.x, qf[m].x, acco[c]);
-          acco[c] = mfma_f32(sv.y, qf[m].y, acco[c]);
-          acco[c] = mfma_f32(sv.z, qf[m].z, acco[c]);
-          acco[c] = mfma_f32(sv.w, qf[m].w, acco[c]);
-        }
-      // intra-chunk, one key tile at a time: A^T = phi(K_jt) phi(Q_it)^T (masked on the
-      // diagonal tile), then V^T A^T; the key sums 1^T A^T go into this lane's part of the
-      // denominator (its rows 4g..4g+3 of the tile), summed over the lane groups once per row
-      for (int jt = 0; jt <= it; ++jt) {
-        f32x4 accA = zero4();
-#pragma unroll
-        for (int m = 0; m < KM; ++m) {
-          const f32x4 kf = *reinterpret_cast<const f32x4*>(&Kn[(jt * 16 + l16) * LD + m * 16 + g * 4]);
-          accA = mfma_f32(kf.x, qf[m].x, accA);
-          accA = mfma_f32(kf.y, qf[m].y, accA);
-          accA = mfma_f32(kf.z, qf[m].z, accA);
-          accA = mfma_f32(kf.w, qf[m].w, accA);
-        }
-        if (jt == it) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (g * 4 + r > l16) accA[r] = 0.f;
-        }
-        dpart += (accA[0] + accA[1]) + (accA[2] + accA[3]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = jt * 16 + g * 4 + r;
-#pragma unroll
-          for (int c = 0; c < NCO; ++c) acco[c] = mfma_f32(Vn[j * LD + (cb + c) * 16 + l16], accA[r], acco[c]);
-        }
-      }
-      const float den = sum_over_groups(dpart);
-      const int64_t row = c0 + it * 16 + l16;
-      if (row < t1) {
-        // one IEEE division per row, then products (within 1.5 ulp of a division per element);
-        // a denominator too small for its reciprocal to be finite keeps the exact divisions
-        const float inv = 1.0f / den;
-        const bool tiny = !(den >= 0x1p-120f);
-#pragma unroll
-        for (int c = 0; c < NCO; ++c) {
-          f32x4 o = {acco[c][0] * inv, acco[c][1] * inv, acco[c][2] * inv, acco[c][3] * inv};
-          if (tiny) o = f32x4{acco[c][0] / den, acco[c][1] / den, acco[c][2] / den, acco[c][3] / den};
-          *reinterpret_cast<f32x4*>(O + row * D + (cb + c) * 16 + g * 4) = o;
-        }
-      }
+    for (int p = 0; p < RPK; ++p) {
+      *reinterpret_cast<u32x2*>(&KnH[prow(p) * LDK + pcol]) = khi[p];
+      *reinterpret_cast<u32x2*>(&KnL[prow(p) * LDK + pcol]) = klo[p];
+      *reinterpret_cast<u32x2*>(&VnH[vofs(prow(p), pcol)]) = vhi[p];
+      *reinterpret_cast<u32x2*>(&VnL[vofs(prow(p), pcol)]) = vlo[p];
     }
-    __syncthreads();  // S^T, z and the tiles are no longer read for outputs
+  };
 
-    // state update: S[:, own cols] += phi(K)^T V, z[own feature tiles] += phi(K)^T 1
-    float zs[NZW];
+  load_k(t0);
+  load_v(t0);
+  load_q(t0);
+  prep_kv(t0);
+  store_kv();
+  for (int64_t c0 = t0; c0 < t1; c0 += C) {
+    __syncthreads();  // tiles of this chunk, S^T and Zr ready
+    // next chunk's loads in three groups, as in the bf16 kernel
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 qh[KA], ql[KA];
 #pragma unroll
-    for (int i = 0; i < NZW; ++i) zs[i] = 0.f;
-    for (int ks = 0; ks < C / 4; ++ks) {
+    for (int ks = 0; ks < KA; ++ks) {
+      f32x4 x0 = qr[ks][0], x1 = qr[ks][1];
+      x0.x = phi(x0.x);
+      x0.y = phi(x0.y);
+      x0.z = phi(x0.z);
+      x0.w = phi(x0.w);
+      x1.x = phi(x1.x);
+      x1.y = phi(x1.y);
+      x1.z = phi(x1.z);
+      x1.w = phi(x1.w);
+      split8(x0, x1, qh[ks], ql[ks]);
+    }
+
+    // ---- state update in registers: S[own block] += phi(K_c)^T V_c ; z
 #pragma unroll
-      for (int at = 0; at < NA; ++at) {
-        const float ak = Kn[(ks * 4 + g) * LD + at * 16 + l16];
+    for (int ks = 0; ks < KJ; ++ks) {
+      u32x4 bvh[NCW], bvl[NCW];
 #pragma unroll
-        for (int p = 0; p < NCW; ++p)
-          accS[at][p] = mfma_f32(ak, Vn[(ks * 4 + g) * LD + (wave + NW * p) * 16 + l16], accS[at][p]);
+      for (int j = 0; j < NCW; ++j) {
+        bvh[j] = ld_v_operand(VnH, ks * 32, (sc0 + j) * 16);
+        bvl[j] = ld_v_operand(VnL, ks * 32, (sc0 + j) * 16);
       }
 #pragma unroll
-      for (int i = 0; i < NZW; ++i) zs[i] += Kn[(ks * 4 + g) * LD + (wave + NW * i) * 16 + l16];
-    }
+      for (int i = 0; i < NAW; ++i) {
+        const u32x4 akh = ld_rows_operand(KnH, LDK, ks * 32, (sa0 + i) * 16, l16, g);
+        const u32x4 akl = ld_rows_operand(KnL, LDK, ks * 32, (sa0 + i) * 16, l16, g);
+        accz[i] = mfma_bf16(akl, zones, accz[i]);  // zones is zero where z is not kept
+        accz[i] = mfma_bf16(akh, zones, accz[i]);
 #pragma unroll
-    for (int i = 0; i < NZW; ++i) {
-      const float zc = sum_over_groups(zs[i]);
-      if (g == 0) zf[(wave + NW * i) * 16 + l16] += zc;
+        for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_split(akh, akl, bvh[j], bvl[j], accS[i][j]);
+      }
     }
-    write_st();
-    __syncthreads();  // before the next chunk overwrites the tiles
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- this wave's query tile: inter-chunk part S^T phi(Q)^T and [z_hi; z_lo] phi(Q)^T
+    f32x4 acco[OCT];
+    f32x4 accd = zero4();
+#pragma unroll
+    for (int ct = 0; ct < OCT; ++ct) acco[ct] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) {
+#pragma unroll
+      for (int ct = 0; ct < OCT; ++ct) {
+        const int o = pswz<D>((oc0 + ct) * 16 + l16, ks * 32 + g * 8);
+        acco[ct] = mfma_split(ld16(&StH[o]), ld16(&StL[o]), qh[ks], ql[ks], acco[ct]);
+      }
+      const u32x4 zr = ld16(&Zr[l16 * LDK + ks * 32 + g * 8]);
+      accd = mfma_bf16(zr, ql[ks], accd);
+      accd = mfma_bf16(zr, qh[ks], accd);
+    }
+    // intra-chunk: A^T = phi(K) phi(Q)^T masked to key <= query, split, then V^T A^T and
+    // ones A^T; step m covers key tiles 2m and 2m + 1, and the A^T products of step m + 1 go out
+    // before the V products of step m (the bf16 kernel's pipeline)
+    auto a_tiles = [&](int m, f32x4& a0, f32x4& a1) {
+      a0 = zero4();
+      a1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KA; ++ks) {
+        const int o0 = (2 * m * 16 + l16) * LDK + ks * 32 + g * 8, o1 = o0 + 16 * LDK;
+        a0 = mfma_split(ld16(&KnH[o0]), ld16(&KnL[o0]), qh[ks], ql[ks], a0);
+        a1 = mfma_split(ld16(&KnH[o1]), ld16(&KnL[o1]), qh[ks], ql[ks], a1);
+      }
+    };
+    auto split_a = [&](int m, f32x4 a0, f32x4 a1, u32x4& ah, u32x4& al) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (2 * m == it && g * 4 + r > l16) a0[r] = 0.f;
+        if (2 * m + 1 > it || (2 * m + 1 == it && g * 4 + r > l16)) a1[r] = 0.f;
+      }
+      split8(a0, a1, ah, al);
+    };
+    auto av_step = [&](int m, u32x4 ah, u32x4 al) {
+#pragma unroll
+      for (int ct = 0; ct < OCT; ++ct)
+        acco[ct] = mfma_split(ld_v_operand(VnH, m * 32, (oc0 + ct) * 16), ld_v_operand(VnL, m * 32, (oc0 + ct) * 16),
+                         ah, al, acco[ct]);
+      accd = mfma_bf16(ones, al, accd);
+      accd = mfma_bf16(ones, ah, accd);
+    };
+    const int mlast = it >> 1;
+    f32x4 a0, a1;
+    a_tiles(0, a0, a1);
+#pragma unroll
+    for (int m = 0; m < NI / 2 - 1; ++m) {
+      if (m < mlast) {
+        u32x4 ah, al;
+        split_a(m, a0, a1, ah, al);
+        a_tiles(m + 1, a0, a1);
+        av_step(m, ah, al);
+      }
+    }
+    u32x4 ah, al;
+    split_a(mlast, a0, a1, ah, al);
+    av_step(mlast, ah, al);
+
+    const float den = __shfl(accd[0] + accd[1], l16);
+    const int64_t row = c0 + it * 16 + l16;
+    if (row < t1) {
+      // one IEEE division per row, then products (within 1.5 ulp of a division per element);
+      // a denominator too small for its reciprocal to be finite keeps the exact divisions
+      const float inv = 1.0f / den;
+      const bool tiny = !(den >= 0x1p-120f);
+#pragma unroll
+      for (int ct = 0; ct < OCT; ++ct) {
+        f32x4 o = {acco[ct][0] * inv, acco[ct][1] * inv, acco[ct][2] * inv, acco[ct][3] * inv};
+        if (tiny) o = f32x4{acco[ct][0] / den, acco[ct][1] / den, acco[ct][2] / den, acco[ct][3] / den};
+        *reinterpret_cast<f32x4*>(O + row * D + (oc0 + ct) * 16 + g * 4) = o;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(c0 + C);
+    __builtin_amdgcn_sched_barrier(0);
+    prep_kv(c0 + C);  // past the last chunk these are zero tiles that nothing reads
+    __syncthreads();  // every wave is done reading this chunk's tiles, S^T and Zr
+
+    // ---- the next chunk's tiles, the new state
+    store_kv();
+    write_state();
+    if (zown && l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < NAW; ++i) {
+        u32x2 h, l;
+        split4(accz[i], h, l);
+        *reinterpret_cast<u32x2*>(&Zr[(sa0 + i) * 16 + g * 4]) = h;
+        *reinterpret_cast<u32x2*>(&Zr[LDK + (sa0 + i) * 16 + g * 4]) = l;
+      }
+    }
   }
 
   // the state after the last token, from the last segment's workgroup
   if (a.sn && seg == (sp.n - 1) / a.seg_len) {
     float* sn = a.sn + bh * D * D;
 #pragma unroll
-    for (int at = 0; at < NA; ++at)
+    for (int i = 0; i < NAW; ++i)
 #pragma unroll
-      for (int p = 0; p < NCW; ++p)
+      for (int j = 0; j < NCW; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sn[(at * 16 + g * 4 + r) * D + (wave + NW * p) * 16 + l16] = accS[at][p][r];
-    if (tid < D) a.zn[bh * D + tid] = zf[tid];
+        for (int r = 0; r < 4; ++r) sn[((sa0 + i) * 16 + g * 4 + r) * D + (sc0 + j) * 16 + l16] = accS[i][j][r];
+    if (zown && l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < NAW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.zn[bh * D + (sa0 + i) * 16 + g * 4 + r] = accz[i][r];
+    }
   }
 }
 
@@ -700,7 +807,7 @@ static hipError_t launch_causal_tb(const CausalArgs& a, int dtype, hipStream_t s
     hipLaunchKernelGGL((causal_bf16<D, C, TB>), dim3(blocks), dim3(512), 0, s, a, tb);
   } else {
     if constexpr (D * C <= 8192)
-      hipLaunchKernelGGL((causal_f32<D, C, TB>), dim3(blocks), dim3(64 * f32_waves(D)), 0, s, a, tb);
+      hipLaunchKernelGGL((causal_f32<D, C, TB>), dim3(blocks), dim3(512), 0, s, a, tb);
     else
       return hipErrorInvalidValue;
   }

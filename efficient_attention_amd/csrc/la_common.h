@@ -95,6 +95,51 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// fp32 products on the bf16 MFMA from two-term splits (after Henry, Tang and Heinecke,
+// "Leveraging the bfloat16 Artificial Intelligence Datatype For Higher-Precision Computations",
+// ARITH 2019): x = hi + lo + rest with hi the truncation of x to bf16 (|lo| < 2^-7 |x|) and lo
+// the bf16 rounding of x - hi (|rest| <= 2^-16 |x|, either sign).  x y is taken as all four
+// products hi_x hi_y + hi_x lo_y + lo_x hi_y + lo_x lo_y (mfma_split), each exact, accumulated
+// in fp32: what is dropped is the rests, below 2^-15 |x y| and of either sign, so sums do not
+// drift.  (Three terms, without lo_x lo_y, drop up to 2^-14 |x y| always with the sign of x y.)
+// Truncation gives lo the sign of x, which keeps the IEEE class of a product that involves an
+// infinity: lo of +-inf is a finite number of its sign (the residual of the largest finite
+// value), lo of a finite x that bf16 holds exactly is x 2^-100 instead of zero (so inf * lo is
+// inf, not NaN), and lo of zero is zero (so a row whose features are all zero still gives 0/0).
+// A quiet NaN stays NaN in hi.
+__device__ __forceinline__ float split_rest(float x) {
+  const float xc = __builtin_amdgcn_fmed3f(x, -0x1.fffffep127f, 0x1.fffffep127f);
+  const float r = xc - __uint_as_float(__float_as_uint(xc) & 0xffff0000u);
+  return __builtin_fmaf(xc, 0x1p-100f, r);
+}
+// the truncated bf16 pair (a in the low half)
+__device__ __forceinline__ uint32_t trunc_pair(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+__device__ __forceinline__ void split4(const f32x4& x, u32x2& hi, u32x2& lo) {
+  hi.x = trunc_pair(x.x, x.y);
+  hi.y = trunc_pair(x.z, x.w);
+  lo.x = pack_bf16(split_rest(x.x), split_rest(x.y));
+  lo.y = pack_bf16(split_rest(x.z), split_rest(x.w));
+}
+// hi and lo of 8 values (two f32x4) as 16x16x32 operands
+__device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, u32x4& hi, u32x4& lo) {
+  u32x2 h0, l0, h1, l1;
+  split4(x0, h0, l0);
+  split4(x1, h1, l1);
+  hi = u32x4{h0.x, h0.y, h1.x, h1.y};
+  lo = u32x4{l0.x, l0.y, l1.x, l1.y};
+}
+
+// acc + x y for split operands x = (xh, xl), y = (yh, yl) of a 16x16x32 product, smallest
+// terms first
+__device__ __forceinline__ f32x4 mfma_split(u32x4 xh, u32x4 xl, u32x4 yh, u32x4 yl, f32x4 acc) {
+  acc = mfma_bf16(xl, yl, acc);
+  acc = mfma_bf16(xl, yh, acc);
+  acc = mfma_bf16(xh, yl, acc);
+  return mfma_bf16(xh, yh, acc);
+}
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

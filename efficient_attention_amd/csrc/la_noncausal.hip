@@ -354,25 +354,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// fp32 stage 1: tile of 64 tokens kept in natural layout (the fp32 MFMA takes one k value
-// per lane, so no transpose is needed).  The next tile's rows are loaded into registers while
+// fp32 stage 1: the bf16 stage-1 layout (phi(K) and V token-major in LDS, operands of
+// phi(K)^T V through transpose reads) with each tile held as two bf16 planes, hi and lo, and
+// every product taken from the two-term splits on the bf16 MFMA (split4, mfma_split in
+// la_common.h); accumulation is fp32.  z is the column sum of hi + lo.  The next tile's rows are loaded into registers while
 // the current one is multiplied (unconditional loads, rows past the slice end clamped and then
-// zeroed), and the finished [KV | z] reuses the tile area, so that two workgroups fit on a CU
-// at D = 128 and four at D = 64.
+// zeroed).  LDS: 72 KB at D = 128 (two workgroups per CU), 40 KB at D = 64 (four).
 template <int D, class TB>
 __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a, TB tb) {
   constexpr int T = 64;
-  constexpr int LD = D + 4;
-  constexpr int NA = D / 64;
-  constexpr int NC = D / 16;
-  constexpr int PPR = D / 4;            // 16-byte pieces per row
+  constexpr int LDK = D + 16;           // row stride of 8 (mod 64) dwords x odd: conflict-free reads
+  constexpr int PPR = D / 4;            // 16-byte fp32 pieces per row
   constexpr int NP = T * PPR / 256;     // pieces per thread and tensor
-  static_assert(D * D + D <= 2 * T * LD, "the state fits in the tile area");
-  __shared__ __attribute__((aligned(16))) float tiles[2 * T * LD];
-  float* Kn = tiles;
-  float* Vn = tiles + T * LD;
-  float* kv_lds = tiles;  // [KV | z], after the last tile
-  float* z_lds = kv_lds + D * D;
+  constexpr int NA = D / 64;            // feature tiles per wave
+  constexpr int NC = D / 16;            // value-column tiles
+  __shared__ __attribute__((aligned(16))) uint16_t KnH[T * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t KnL[T * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t VnH[T * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t VnL[T * LDK];
 
   const GroupRange gr = group_range(a, tb);
   if (gr.hn == 0) return;
@@ -382,13 +381,11 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a, TB tb) {
   const float* V = reinterpret_cast<const float*>(a.v) + gr.row0 * D;
 
   f32x4 acc[NA][NC];
-  float zacc[NA];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    zacc[i] = 0.f;
+  for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[i][c] = zero4();
-  }
+  f32x4 zp = zero4();  // sums of phi(K) over this thread's rows, columns pcol .. pcol + 3
   auto prow = [&](int p) { return tid / PPR + p * (256 / PPR); };
   const int pcol = (tid % PPR) * 4;
   f32x4 kq[NP], vq[NP];
@@ -403,43 +400,69 @@ __global__ __launch_bounds__(256) void kv_state_f32(KvStateArgs a, TB tb) {
   load(gr.t0);
   for (int64_t t0 = gr.t0; t0 < gr.t1; t0 += T) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {  // phi on K; rows past the end are zero in both tiles
-      const bool ok = t0 + prow(p) < gr.t1;
-      f32x4 kk = kq[p];
+    for (int p = 0; p < NP; ++p) {  // phi on K, both split; rows past the end are zero
+      const uint32_t m = 0u - (uint32_t)(t0 + prow(p) < gr.t1);
+      f32x4 kk = kq[p], vv = vq[p];
       kk.x = phi(kk.x);
       kk.y = phi(kk.y);
       kk.z = phi(kk.z);
       kk.w = phi(kk.w);
-      *reinterpret_cast<u32x4*>(&Kn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, kk), ok);
-      *reinterpret_cast<u32x4*>(&Vn[prow(p) * LD + pcol]) = keep_if(__builtin_bit_cast(u32x4, vq[p]), ok);
+      vv.x = __builtin_canonicalizef(vv.x);  // a signalling NaN stays NaN in hi
+      vv.y = __builtin_canonicalizef(vv.y);
+      vv.z = __builtin_canonicalizef(vv.z);
+      vv.w = __builtin_canonicalizef(vv.w);
+      zp += __builtin_bit_cast(f32x4, keep_if(__builtin_bit_cast(u32x4, kk), m != 0u));
+      u32x2 kh, kl, vh, vl;
+      split4(kk, kh, kl);
+      split4(vv, vh, vl);
+      const int o = prow(p) * LDK + pcol;
+      *reinterpret_cast<u32x2*>(&KnH[o]) = u32x2{kh.x & m, kh.y & m};
+      *reinterpret_cast<u32x2*>(&KnL[o]) = u32x2{kl.x & m, kl.y & m};
+      *reinterpret_cast<u32x2*>(&VnH[o]) = u32x2{vh.x & m, vh.y & m};
+      *reinterpret_cast<u32x2*>(&VnL[o]) = u32x2{vl.x & m, vl.y & m};
     }
     __syncthreads();
     load(t0 + T);  // the next tile arrives while this one is multiplied
-#pragma unroll 4
-    for (int s = 0; s < T / 4; ++s) {
+#pragma unroll
+    for (int s = 0; s < T / 32; ++s) {
+      u32x4 akh[NA], akl[NA];
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int at = wave * NA + i;
-        float ak = Kn[(s * 4 + g) * LD + at * 16 + l16];
-        zacc[i] += ak;
+        akh[i] = ld_rows_operand(KnH, LDK, s * 32, (wave * NA + i) * 16, l16, g);
+        akl[i] = ld_rows_operand(KnL, LDK, s * 32, (wave * NA + i) * 16, l16, g);
+      }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[i][c] = mfma_f32(ak, Vn[(s * 4 + g) * LD + c * 16 + l16], acc[i][c]);
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 bvh = ld_rows_operand(VnH, LDK, s * 32, c * 16, l16, g);
+        const u32x4 bvl = ld_rows_operand(VnL, LDK, s * 32, c * 16, l16, g);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          acc[i][c] = mfma_split(akh[i], akl[i], bvh, bvl, acc[i][c]);
+        }
       }
     }
     __syncthreads();
   }
+  // z: the 256 / PPR partial sums of each column, in thread order (the tile area is free: the
+  // loop ended on a barrier)
+  constexpr int ZR = 256 / PPR;
+  float* zbuf = reinterpret_cast<float*>(KnH);  // [ZR][D]
+  float* zfin = reinterpret_cast<float*>(VnH);  // [D]
+  *reinterpret_cast<f32x4*>(&zbuf[(tid / PPR) * D + pcol]) = zp;
+  __syncthreads();
+  if (tid < D) {
+    float zs = 0.f;
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int at = wave * NA + i;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) kv_lds[(at * 16 + g * 4 + r) * D + c * 16 + l16] = acc[i][c][r];
-    float zs = sum_over_groups(zacc[i]);
-    if (g == 0) z_lds[at * 16 + l16] = zs;
+    for (int r = 0; r < ZR; ++r) zs += zbuf[r * D + tid];
+    zfin[tid] = zs;
   }
   __syncthreads();
-  publish_state<D>(a, gr, kv_lds);
+  float z[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) z[i] = zfin[(wave * NA + i) * 16 + l16];
+  float* dst = a.slices == 1 ? a.state + gr.g * (D * D + D)
+                             : a.partials + (gr.g * a.slices + gr.s) * (D * D + D);
+  store_state_block<D, NA, NC>(dst, wave * NA, acc, z, l16, g);
 }
 
 // ----------------------------------------------------------------------------- stage 2
@@ -645,24 +668,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
   }
 }
 
-// fp32 output: same orientation with the fp32 MFMA (one k value per lane).  A lane loads 16
-// bytes of its query row, a[16m + 4g .. +3]; k-step 4m+e uses a = 16m + 4g + e on both
+// fp32 output: the same orientation with each product of fp32 values taken from two-term bf16
+// splits (split8, mfma_split in la_common.h).  The workgroup holds its head's KV^T in LDS as two bf16 planes, hi
+// and lo (rows = value columns, 16-byte pieces permuted by the row: pswz); a lane loads 32 bytes
+// of its query row per 32-feature step, features 32 ks + 8 g .. + 7, the k slots of both
 // operands.  The normaliser phi(q).z is a plain fp32 dot product.  A wave takes its queries in
 // steps of BB 16-query blocks, which share every KV^T read from LDS, and loads the next step's
 // rows while it computes (unconditional loads; rows past the end read row n - 1 and are not
 // stored).  The KV^T reads are kept inside the loop (an empty asm statement hides that they
-// repeat): hoisted out of it, KV^T would occupy the register file and leave one wave per SIMD.
+// repeat): hoisted out of it, KV^T would occupy the register file.
 template <int D, class TB, int QTV>
 __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
-  constexpr int LD = D + 4;
   constexpr int NC = D / 16;
-  constexpr int KM = D / 16;                 // 16-feature groups of the reduction
+  constexpr int KA = D / 32;                 // 32-feature steps of the reduction
   constexpr int BB = D == 64 ? 2 : 1;        // 16-query blocks per step
   constexpr int64_t QT = QTV;  // queries per workgroup (nc_queries, or less when the heads are few)
   constexpr int QPW = (int)QT / 4;
   constexpr int NB = QPW / (16 * BB);        // steps per wave
   static_assert(NB % 2 == 0, "steps come in pairs");
-  __shared__ __attribute__((aligned(16))) float KVt[D * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t KvH[D * D];
+  __shared__ __attribute__((aligned(16))) uint16_t KvL[D * D];
   __shared__ float zs[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -678,31 +703,35 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
   float zv;
   head_state<D>(a, bh, tid, kv4, zv);
 #pragma unroll
-  for (int i = 0; i < NKV4; ++i) {
+  for (int i = 0; i < NKV4; ++i) {  // KV[ar][c .. c + 3] -> KV^T rows c .. c + 3, column ar
     const int e = (tid + 256 * i) * 4, ar = e / D, c = e % D;
-    KVt[(c + 0) * LD + ar] = kv4[i].x;
-    KVt[(c + 1) * LD + ar] = kv4[i].y;
-    KVt[(c + 2) * LD + ar] = kv4[i].z;
-    KVt[(c + 3) * LD + ar] = kv4[i].w;
+    u32x2 h, l;
+    split4(kv4[i], h, l);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t hw = j < 2 ? h.x : h.y, lw = j < 2 ? l.x : l.y;
+      KvH[pswz<D>(c + j, ar)] = (uint16_t)((j & 1) ? hw >> 16 : hw);
+      KvL[pswz<D>(c + j, ar)] = (uint16_t)((j & 1) ? lw >> 16 : lw);
+    }
   }
   if (tid < D) zs[tid] = zv;
   __syncthreads();
 
   const float* Q = reinterpret_cast<const float*>(a.q) + sp.row0 * D;
   float* O = reinterpret_cast<float*>(a.out) + sp.row0 * D;
-  auto load = [&](int st, f32x4 (&q)[BB][KM]) {
+  auto load = [&](int st, f32x4 (&q)[BB][2 * KA]) {
 #pragma unroll
     for (int bb = 0; bb < BB; ++bb) {
       const int64_t row = q0 + (int64_t)(BB * st + bb) * 16 + l16;
       const int64_t r = row < n ? row : n - 1;
 #pragma unroll
-      for (int m = 0; m < KM; ++m) q[bb][m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Q + r * D + m * 16 + g * 4));
+      for (int m = 0; m < 2 * KA; ++m)
+        q[bb][m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Q + r * D + (m >> 1) * 32 + g * 8 + (m & 1) * 4));
     }
   };
-  auto compute = [&](int st, const f32x4 (&q)[BB][KM]) {
-    int kofs = l16 * LD;
-    asm volatile("" : "+v"(kofs));  // KV^T is re-read every step
-    const float* kvt = KVt + kofs;
+  auto compute = [&](int st, const f32x4 (&q)[BB][2 * KA]) {
+    int l16o = l16;
+    asm volatile("" : "+v"(l16o));  // KV^T is re-read every step
     f32x4 acc[BB][NC];
     float dpart[BB];
 #pragma unroll
@@ -712,26 +741,31 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
       for (int c = 0; c < NC; ++c) acc[bb][c] = zero4();
     }
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      float qf[BB][4];
+    for (int ks = 0; ks < KA; ++ks) {
+      u32x4 qh[BB], ql[BB];
 #pragma unroll
       for (int bb = 0; bb < BB; ++bb) {
-        qf[bb][0] = phi(q[bb][m].x);
-        qf[bb][1] = phi(q[bb][m].y);
-        qf[bb][2] = phi(q[bb][m].z);
-        qf[bb][3] = phi(q[bb][m].w);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dpart[bb] += qf[bb][e] * zs[m * 16 + g * 4 + e];
+        f32x4 x0 = q[bb][2 * ks], x1 = q[bb][2 * ks + 1];
+        x0.x = phi(x0.x);
+        x0.y = phi(x0.y);
+        x0.z = phi(x0.z);
+        x0.w = phi(x0.w);
+        x1.x = phi(x1.x);
+        x1.y = phi(x1.y);
+        x1.z = phi(x1.z);
+        x1.w = phi(x1.w);
+        const float* zp = zs + ks * 32 + g * 8;
+        dpart[bb] += x0.x * zp[0] + x0.y * zp[1] + x0.z * zp[2] + x0.w * zp[3] +
+                     x1.x * zp[4] + x1.y * zp[5] + x1.z * zp[6] + x1.w * zp[7];
+        split8(x0, x1, qh[bb], ql[bb]);
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(kvt + c * 16 * LD + m * 16 + g * 4);
+        const int o = pswz<D>(c * 16 + l16o, ks * 32 + g * 8);
+        const u32x4 kh = ld16(&KvH[o]), kl = ld16(&KvL[o]);
 #pragma unroll
         for (int bb = 0; bb < BB; ++bb) {
-          acc[bb][c] = mfma_f32(kv.x, qf[bb][0], acc[bb][c]);
-          acc[bb][c] = mfma_f32(kv.y, qf[bb][1], acc[bb][c]);
-          acc[bb][c] = mfma_f32(kv.z, qf[bb][2], acc[bb][c]);
-          acc[bb][c] = mfma_f32(kv.w, qf[bb][3], acc[bb][c]);
+          acc[bb][c] = mfma_split(kh, kl, qh[bb], ql[bb], acc[bb][c]);
         }
       }
     }
@@ -753,7 +787,7 @@ __global__ __launch_bounds__(256) void nc_out_f32(NcOutArgs a, TB tb) {
       }
     }
   };
-  f32x4 qa[BB][KM], qb[BB][KM];
+  f32x4 qa[BB][2 * KA], qb[BB][2 * KA];
   load(0, qa);
   for (int st = 0; st < NB; st += 2) {
     load(st + 1, qb);

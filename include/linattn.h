@@ -33,8 +33,17 @@
  *
  * Supported shapes: d in {64, 128}; element types fp32 and bf16 (state and accumulation are
  * always fp32); causal chunk in {64, 128} for bf16, and for fp32 with d * chunk <= 8192 (d = 64:
- * 64 or 128; d = 128: 64 only -- the fp32 kernel keeps two chunk tiles and the transposed state
- * in LDS), else LA_ERR_UNSUPPORTED.
+ * 64 or 128; d = 128: 64 only -- the fp32 kernel keeps the chunk's phi(K) and V and the
+ * transposed state in LDS as two bf16 planes each), else LA_ERR_UNSUPPORTED.
+ *
+ * Precision.  bf16 inputs: products of bf16 values (the running state and the masked weights
+ * rounded to bf16 where they enter a product), fp32 accumulation.  fp32 inputs: every product of
+ * two fp32 values is taken on the bf16 matrix cores from two-term splits, x = hi + lo with hi the
+ * truncation of x to bf16 and lo the bf16 rounding of the rest (x held to 2^-16 of its size):
+ * the four products hi*hi + hi*lo + lo*hi + lo*lo, accumulated in fp32.  A product is within
+ * 2^-15 of its size, with errors of either sign, and results stay well inside a relative error of
+ * 1e-4.  Infinities and NaN give the result classes of fp32 arithmetic.  The decode step and the
+ * normalisers' dot products of the non-causal output compute in fp32 throughout.
  */
 #ifndef LINATTN_H
 #define LINATTN_H

@@ -196,7 +196,7 @@ def test_grid_point_full_size(ea, form, dtype, n, d):
 
     import torch
     B, H = 8, 16
-    chunk = 128 if dtype == "bf16" else 64
+    chunk = 64 if (dtype == "f32" and d == 128) else 128  # as bench.py --grid
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     gen = torch.Generator(device="cuda")
     gen.manual_seed(zlib.crc32(repr((form, dtype, n, d)).encode()))

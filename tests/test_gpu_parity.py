@@ -190,7 +190,10 @@ def test_invariants_on_gpu(ea, form):
     if form == "causal":
         _, _, v2 = random_inputs(10, (1, 2, n, d), "f32", 1.0)
         g2 = run_forward(ea, form, q, k, v2, "f32")
-        np.testing.assert_allclose(g2[:, :, 0], v2[:, :, 0], rtol=1e-5, atol=1e-6)
+        # out_0 = A_00 v_0 / A_00: every other factor cancels, so what remains is how v_0 itself
+        # enters the products.  The fp32 kernels take it as a two-term bf16 split, hi + lo,
+        # which holds v_0 to 2^-16 of its size (plain fp32 arithmetic would give 1e-7)
+        np.testing.assert_allclose(g2[:, :, 0], v2[:, :, 0], rtol=2.0 ** -16 + 1e-6, atol=1e-6)
 
 
 @pytest.mark.parametrize("form", ["noncausal", "causal"])
