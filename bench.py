@@ -235,9 +235,9 @@ def run_grid():
         for form in ("noncausal", "causal"):
             for n in (16384, 65536):
                 for d in (64, 128):
-                    # bf16: chunk 128; fp32: chunk 64 (d*chunk <= 8192 at d = 128; at d = 64 it fits three
-                    # workgroups per compute unit, measured faster than chunk 128)
-                    chunk = 64 if (dtype == "f32" and d == 128) else 128  # the largest the kernel takes
+                    # the largest chunk the kernel takes (fp32 needs d * chunk <= 8192): 128, or 64 for
+                    # fp32 at d = 128; measured fastest where both are taken
+                    chunk = 64 if (dtype == "f32" and d == 128) else 128
                     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
                     gen = torch.Generator(device=dev)
                     gen.manual_seed(zlib.crc32(repr((form, dtype, n, d)).encode()))

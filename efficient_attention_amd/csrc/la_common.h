@@ -8,9 +8,7 @@
 //      v_mfma_f32_16x16x32_bf16: A lane l holds row l%16, k = 8*(l/16)+e (e < 8);
 //                                B lane l holds column l%16, the same k; the 4 results of
 //                                lane l are rows 4*(l/16)+r (r < 4) of column l%16.
-//      v_mfma_f32_16x16x4_f32:   A lane l holds row l%16, k = l/16; B column l%16, k = l/16;
-//                                results as above.
-//    A reduction index may be mapped to the 8 (or 1) k-slots of a lane in any order, as long
+//    A reduction index may be mapped to the 8 k-slots of a lane in any order, as long
 //    as both operands use the same mapping; several kernels use that to feed an MFMA result
 //    straight back in as an operand without moving data between lanes.
 #pragma once
@@ -138,10 +136,6 @@ __device__ __forceinline__ f32x4 mfma_split(u32x4 xh, u32x4 xl, u32x4 yh, u32x4 
   acc = mfma_bf16(xl, yh, acc);
   acc = mfma_bf16(xh, yl, acc);
   return mfma_bf16(xh, yh, acc);
-}
-
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 zero4() {

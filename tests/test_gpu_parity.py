@@ -634,7 +634,8 @@ def test_state_sums_vs_oracle(ea, dtype, d):
     for s in range(nseg):
         S, z = oracle.state_accumulate(K[:, :, s * seg_len:(s + 1) * seg_len], V[:, :, s * seg_len:(s + 1) * seg_len])
         ref = np.concatenate([S.reshape(B, H, d * d), z], axis=-1)
-        # bf16 rounds phi(K) once before the MFMA, fp32 does not
+        # bf16 rounds phi(K) once before the MFMA; fp32 holds every factor to 2^-16 (a two-term
+        # bf16 split, with errors of either sign) and sums z from the fp32 features
         assert normwise_err(g[:, :, s], ref, head_axes_last=1) <= (4e-3 if dtype == "bf16" else 1e-6)
 
 
