@@ -163,3 +163,30 @@ def test_nonfinite_decode(ea, dtype, d):
             assert err.max() <= TOL[dtype], (t, err)
     assert np.array_equal(_classes(S.cpu().numpy().astype(np.float64)), _classes(Sr))
     assert np.array_equal(_classes(z.cpu().numpy().astype(np.float64)), _classes(zr))
+
+
+@pytest.mark.parametrize("form,chunk", [("noncausal", 0), ("causal", 64), ("causal", 128)])
+def test_nonfinite_with_values_bf16_holds_exactly(ea, form, chunk):
+    """fp32 inputs whose features and values bf16 holds exactly, so that the low half of every
+    two-term split is the tiny stand-in, never zero: an infinite value must still give +-inf
+    (inf * lo of an exact factor is inf, not NaN), as fp32 arithmetic and the formula do.
+    q, k in {0, 0.5, 1, 1.5} (phi = x + 1 exact), v in {-2, -1, -0.5, 0.5, 1, 2}; +inf and -inf
+    values at chunk starts of two heads."""
+    rng = np.random.default_rng(324)
+    shape = (1, 3, N, D)
+    q = rng.choice(np.array([0.0, 0.5, 1.0, 1.5], np.float32), shape)
+    k = rng.choice(np.array([0.0, 0.5, 1.0, 1.5], np.float32), shape)
+    v = rng.choice(np.array([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0], np.float32), shape)
+    v[0, 0, 128, 5] = np.inf
+    v[0, 1, 256, 7] = -np.inf
+    say("non-finite with exact bf16 values", form, chunk)
+    tq, tk, tv = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    out = ea.la_forward_noncausal(tq, tk, tv) if form == "noncausal" else ea.la_forward_causal(tq, tk, tv, chunk=chunk)
+    g = from_dev(out, "f32")
+    Q, K, V = (x.astype(np.float64) for x in (q, k, v))
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = oracle.noncausal_linear(Q, K, V) if form == "noncausal" else oracle.causal_recurrent(Q, K, V)
+    cr = _compare(form, g, r, "f32")
+    first = (0, 0) if form == "noncausal" else (128, 256)
+    assert (cr[0, 0][first[0]:, 5] == 1).all() and (cr[0, 1][first[1]:, 7] == 2).all()
+    assert (cr[0, 2] == 0).all()
