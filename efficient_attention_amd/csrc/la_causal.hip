@@ -447,6 +447,7 @@ __global__ __launch_bounds__(512) void causal_f32(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int64_t bh = blockIdx.x / a.segs, seg = blockIdx.x % a.segs;
   const HeadSpan sp = head_span(tb, a.n, bh);
   const int64_t t0 = seg * a.seg_len;
@@ -624,39 +625,48 @@ __global__ __launch_bounds__(512) void causal_f32(
     load_k(c0 + C);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 qh[KA], ql[KA];
+    auto split_q = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < KA; ++ks) {
-      f32x4 x0 = qr[ks][0], x1 = qr[ks][1];
-      x0.x = phi(x0.x);
-      x0.y = phi(x0.y);
-      x0.z = phi(x0.z);
-      x0.w = phi(x0.w);
-      x1.x = phi(x1.x);
-      x1.y = phi(x1.y);
-      x1.z = phi(x1.z);
-      x1.w = phi(x1.w);
-      split8(x0, x1, qh[ks], ql[ks]);
-    }
+      for (int ks = 0; ks < KA; ++ks) {
+        f32x4 x0 = qr[ks][0], x1 = qr[ks][1];
+        x0.x = phi(x0.x);
+        x0.y = phi(x0.y);
+        x0.z = phi(x0.z);
+        x0.w = phi(x0.w);
+        x1.x = phi(x1.x);
+        x1.y = phi(x1.y);
+        x1.z = phi(x1.z);
+        x1.w = phi(x1.w);
+        split8(x0, x1, qh[ks], ql[ks]);
+      }
+    };
 
     // ---- state update in registers: S[own block] += phi(K_c)^T V_c ; z
+    auto update_state = [&]() {
 #pragma unroll
     for (int ks = 0; ks < KJ; ++ks) {
-      u32x4 bvh[NCW], bvl[NCW];
-#pragma unroll
-      for (int j = 0; j < NCW; ++j) {
-        bvh[j] = ld_v_operand(VnH, ks * 32, (sc0 + j) * 16);
-        bvl[j] = ld_v_operand(VnL, ks * 32, (sc0 + j) * 16);
-      }
+      u32x4 akh[NAW], akl[NAW];
 #pragma unroll
       for (int i = 0; i < NAW; ++i) {
-        const u32x4 akh = ld_rows_operand(KnH, LDK, ks * 32, (sa0 + i) * 16, l16, g);
-        const u32x4 akl = ld_rows_operand(KnL, LDK, ks * 32, (sa0 + i) * 16, l16, g);
-        accz[i] = mfma_bf16(akl, zones, accz[i]);  // zones is zero where z is not kept
-        accz[i] = mfma_bf16(akh, zones, accz[i]);
+        akh[i] = ld_rows_operand(KnH, LDK, ks * 32, (sa0 + i) * 16, l16, g);
+        akl[i] = ld_rows_operand(KnL, LDK, ks * 32, (sa0 + i) * 16, l16, g);
+        accz[i] = mfma_bf16(akl[i], zones, accz[i]);  // zones is zero where z is not kept
+        accz[i] = mfma_bf16(akh[i], zones, accz[i]);
+      }
 #pragma unroll
-        for (int j = 0; j < NCW; ++j) accS[i][j] = mfma_split(akh, akl, bvh[j], bvl[j], accS[i][j]);
+      for (int j = 0; j < NCW; ++j) {
+        const u32x4 bvh = ld_v_operand(VnH, ks * 32, (sc0 + j) * 16);
+        const u32x4 bvl = ld_v_operand(VnL, ks * 32, (sc0 + j) * 16);
+#pragma unroll
+        for (int i = 0; i < NAW; ++i) accS[i][j] = mfma_split(akh[i], akl[i], bvh, bvl, accS[i][j]);
       }
     }
+    };
+    // Waves 0..3 update the state here, waves 4..7 (the other wave of each SIMD) after their
+    // outputs, where it runs on the matrix pipe beside the first wave's vector work (output
+    // scaling, the next chunk's feature map and splits)
+    split_q();
+    if (wave_u < 4) update_state();
     __builtin_amdgcn_sched_barrier(0);
     load_v(c0 + C);
     __builtin_amdgcn_sched_barrier(0);
@@ -736,6 +746,7 @@ __global__ __launch_bounds__(512) void causal_f32(
         *reinterpret_cast<f32x4*>(O + row * D + (oc0 + ct) * 16 + g * 4) = o;
       }
     }
+    if (wave_u >= 4) update_state();
     __builtin_amdgcn_sched_barrier(0);
     load_q(c0 + C);
     __builtin_amdgcn_sched_barrier(0);
