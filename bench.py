@@ -260,6 +260,8 @@ def run_grid():
                     ms = float(np.median(times))
                     nbytes = algorithmic_bytes(B, H, n, d, 2 if dtype == "bf16" else 4)
                     points.append({"form": form, "dtype": dtype, "B": B, "H": H, "n": n, "d": d,
+                                   "products": "bf16 MFMA" if dtype == "bf16" else
+                                   "bf16 MFMA, four products of two-term splits of the fp32 values",
                                    "chunk": chunk if form == "causal" else None, "isolated_ms": ms,
                                    "tokens_per_s": B * n / (ms * 1e-3),
                                    "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
